@@ -1,0 +1,315 @@
+/*
+ * oracle.c -- plain CPU oracle of the Kimi-K2-style MoE layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h): loaded by the tests, the smoke
+ * check and the CPU-baseline leg of the benchmark, never by the product.
+ *
+ * Double precision, plain loops, one token at a time.  Tokens are
+ * independent (the MoEGate excerpt flattens [B, T, d] to rows), so the only
+ * parallelism is an OpenMP loop over tokens; the arithmetic of each token
+ * is the same whatever the thread count.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Exact upcast of one stored element to double: fp32 directly, bf16 by
+ * placing its 16 bits in the top half of an fp32 word. */
+static double elem(const void *p, int32_t dtype, size_t i)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)p)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static double sigmoid(double a) { return 1.0 / (1.0 + exp(-a)); }
+
+/* One token of the router [P3 four steps and MoEGate forward].
+ * s_out (length E) receives sigmoid(z); sel (length K) the selected set in
+ * ascending expert id; w (length K) the renormalised, scaled weights. */
+static void route_one(int32_t d, int32_t E, int32_t K, int32_t x_dtype,
+                      const void *x, size_t xrow, const float *W_r,
+                      const float *b, float scale, double *s, double *v,
+                      char *chosen, int32_t *sel, double *w, double *gap)
+{
+    /* step 1: z_e = sum_j x_j W_r[e, j]; step 2: s_e = sigmoid(z_e) */
+    for (int32_t e = 0; e < E; ++e) {
+        double z = 0.0;
+        for (int32_t j = 0; j < d; ++j)
+            z += elem(x, x_dtype, xrow + (size_t)j) * (double)W_r[(size_t)e * d + j];
+        s[e] = sigmoid(z);
+        /* step 3 uses the biased score; the bias only chooses */
+        v[e] = s[e] + (double)b[e];
+        chosen[e] = 0;
+    }
+    /* top-K of v: K rounds of "largest unchosen v"; scanning e upward with a
+     * strict comparison sends ties to the lower expert index. */
+    for (int32_t k = 0; k < K; ++k) {
+        int32_t best = -1;
+        for (int32_t e = 0; e < E; ++e)
+            if (!chosen[e] && (best < 0 || v[e] > v[best]))
+                best = e;
+        chosen[best] = 1;
+        sel[k] = best;
+    }
+    if (gap) {
+        /* the last chosen is the K-th largest; compare with the best left */
+        double vk = v[sel[K - 1]];
+        double next = -INFINITY;
+        for (int32_t e = 0; e < E; ++e)
+            if (!chosen[e] && v[e] > next)
+                next = v[e];
+        *gap = (K == E) ? INFINITY : vk - next;
+    }
+    /* slots in ascending expert id (insertion sort of K values) */
+    for (int32_t i = 1; i < K; ++i) {
+        int32_t key = sel[i], j = i - 1;
+        while (j >= 0 && sel[j] > key) {
+            sel[j + 1] = sel[j];
+            --j;
+        }
+        sel[j + 1] = key;
+    }
+    /* step 4: gather the UNBIASED scores, divide by their sum + 1e-20, then
+     * multiply by the routed scaling factor */
+    double den = 0.0;
+    for (int32_t k = 0; k < K; ++k)
+        den += s[sel[k]];
+    den += 1e-20;
+    for (int32_t k = 0; k < K; ++k)
+        w[k] = (s[sel[k]] / den) * (double)scale;
+}
+
+int oracle_router(int32_t T, int32_t d, int32_t E, int32_t K, int32_t x_dtype,
+                  const void *x, const float *W_r, const float *b, float scale,
+                  int32_t *topk_idx, double *topk_w, double *gap,
+                  double *scores, int32_t nthreads)
+{
+    if (T < 0 || d <= 0 || E <= 0 || K < 1 || K > E)
+        return ORACLE_ERR_SHAPE;
+    if (x_dtype != ORACLE_F32 && x_dtype != ORACLE_BF16)
+        return ORACLE_ERR_SHAPE;
+    if (T > 0 && (!x || !W_r || !b || !topk_idx || !topk_w))
+        return ORACLE_ERR_NULL;
+    int nt = nthreads > 0 ? nthreads : 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int32_t t = 0; t < T; ++t) {
+        double *s = (double *)malloc(sizeof(double) * (size_t)E);
+        double *v = (double *)malloc(sizeof(double) * (size_t)E);
+        char *chosen = (char *)malloc((size_t)E);
+        double g = 0.0;
+        route_one(d, E, K, x_dtype, x, (size_t)t * d, W_r, b, scale, s, v,
+                  chosen, topk_idx + (size_t)t * K, topk_w + (size_t)t * K,
+                  &g);
+        if (gap)
+            gap[t] = g;
+        if (scores)
+            memcpy(scores + (size_t)t * E, s, sizeof(double) * (size_t)E);
+        free(s);
+        free(v);
+        free(chosen);
+    }
+    return ORACLE_OK;
+}
+
+int oracle_dispatch(int32_t T, int32_t E, int32_t K, const int32_t *topk_idx,
+                    int32_t *counts, int32_t *offsets, int32_t *sorted_token,
+                    int32_t *pos)
+{
+    if (T < 0 || E <= 0 || K < 1)
+        return ORACLE_ERR_SHAPE;
+    if (!counts || !offsets || (T > 0 && (!topk_idx || !sorted_token || !pos)))
+        return ORACLE_ERR_NULL;
+    for (int64_t a = 0; a < (int64_t)T * K; ++a)
+        if (topk_idx[a] < 0 || topk_idx[a] >= E)
+            return ORACLE_ERR_SHAPE;
+    /* histogram */
+    for (int32_t e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (int64_t a = 0; a < (int64_t)T * K; ++a)
+        counts[topk_idx[a]] += 1;
+    /* exclusive scan */
+    offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+    /* stable placement: visiting tokens in ascending order fills each
+     * expert's segment in ascending token order */
+    int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    for (int32_t e = 0; e < E; ++e)
+        cursor[e] = offsets[e];
+    for (int32_t t = 0; t < T; ++t)
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t e = topk_idx[(size_t)t * K + k];
+            int32_t p = cursor[e]++;
+            sorted_token[p] = t;
+            pos[(size_t)t * K + k] = p;
+        }
+    free(cursor);
+    return ORACLE_OK;
+}
+
+/* y[o] = sum_f Wd[o*ldd + col0 + f] * h[f],
+ * h[f] = silu(sum_j Wg[(row0+f)*din + j] v[j]) * (sum_j Wu[(row0+f)*din + j] v[j])
+ * The SwiGLU expert of the llm-arch-kb entry (three matrices of
+ * d_model x d_ff each); matrices in [out, in] layout like the router. */
+static void swiglu(int32_t din, int32_t F, int32_t dout, const double *vin,
+                   int32_t wdt, const void *Wg, const void *Wu, size_t row0,
+                   const void *Wd, size_t ldd, size_t col0, double *h,
+                   double *y)
+{
+    for (int32_t f = 0; f < F; ++f) {
+        double g = 0.0, u = 0.0;
+        size_t base = (row0 + (size_t)f) * (size_t)din;
+        for (int32_t j = 0; j < din; ++j) {
+            g += elem(Wg, wdt, base + (size_t)j) * vin[j];
+            u += elem(Wu, wdt, base + (size_t)j) * vin[j];
+        }
+        h[f] = g * sigmoid(g) * u;
+    }
+    for (int32_t o = 0; o < dout; ++o) {
+        double acc = 0.0;
+        for (int32_t f = 0; f < F; ++f)
+            acc += elem(Wd, wdt, (size_t)o * ldd + col0 + (size_t)f) * h[f];
+        y[o] = acc;
+    }
+}
+
+/* out = A v for A [rows, cols] stored row-major. */
+static void matvec(int32_t rows, int32_t cols, const void *A, int32_t dt,
+                   const double *v, double *out)
+{
+    for (int32_t r = 0; r < rows; ++r) {
+        double acc = 0.0;
+        for (int32_t c = 0; c < cols; ++c)
+            acc += elem(A, dt, (size_t)r * cols + c) * v[c];
+        out[r] = acc;
+    }
+}
+
+static int check_layer(const oracle_layer *L)
+{
+    if (!L)
+        return ORACLE_ERR_NULL;
+    if (L->d <= 0 || L->E <= 0 || L->K < 1 || L->K > L->E || L->F <= 0 ||
+        L->n_shared < 0 || L->d_latent < 0 ||
+        (L->n_shared > 0 && L->F_shared <= 0))
+        return ORACLE_ERR_SHAPE;
+    if ((L->act_dtype != ORACLE_F32 && L->act_dtype != ORACLE_BF16) ||
+        (L->w_dtype != ORACLE_F32 && L->w_dtype != ORACLE_BF16))
+        return ORACLE_ERR_SHAPE;
+    if (!L->W_gate || !L->W_up || !L->W_down)
+        return ORACLE_ERR_NULL;
+    if (L->n_shared > 0 && (!L->Ws_gate || !L->Ws_up || !L->Ws_down))
+        return ORACLE_ERR_NULL;
+    if (L->d_latent > 0 && (!L->W_lat_down || !L->W_lat_up))
+        return ORACLE_ERR_NULL;
+    return ORACLE_OK;
+}
+
+int oracle_forward_given_routing(const oracle_layer *L, int32_t T,
+                                 const void *x, const int32_t *topk_idx,
+                                 const double *topk_w, double *out,
+                                 int32_t nthreads)
+{
+    int rc = check_layer(L);
+    if (rc)
+        return rc;
+    if (T < 0)
+        return ORACLE_ERR_SHAPE;
+    if (T == 0)
+        return ORACLE_OK;
+    if (!x || !topk_idx || !topk_w || !out)
+        return ORACLE_ERR_NULL;
+    const int32_t d = L->d, K = L->K, F = L->F;
+    const int32_t din = L->d_latent ? L->d_latent : d;
+    /* every selected expert must be supplied */
+    for (int64_t a = 0; a < (int64_t)T * K; ++a) {
+        int32_t e = topk_idx[a];
+        if (e < 0 || e >= L->E)
+            return ORACLE_ERR_SHAPE;
+        if (!L->W_gate[e] || !L->W_up[e] || !L->W_down[e])
+            return ORACLE_ERR_NULL;
+    }
+    const int32_t Fs_all = L->n_shared * L->F_shared;
+    const int32_t hmax = F > L->F_shared ? F : L->F_shared;
+    int nt = nthreads > 0 ? nthreads : 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int32_t t = 0; t < T; ++t) {
+        double *xd = (double *)malloc(sizeof(double) * (size_t)d);
+        double *xin = (double *)malloc(sizeof(double) * (size_t)din);
+        double *routed_in = (double *)malloc(sizeof(double) * (size_t)din);
+        double *y = (double *)malloc(sizeof(double) * (size_t)(din > d ? din : d));
+        double *h = (double *)malloc(sizeof(double) * (size_t)hmax);
+        double *o = out + (size_t)t * d;
+        for (int32_t j = 0; j < d; ++j)
+            xd[j] = elem(x, L->act_dtype, (size_t)t * d + j);
+        /* routed experts' input: x, or its latent compression [P4] */
+        if (L->d_latent)
+            matvec(din, d, L->W_lat_down, L->w_dtype, xd, xin);
+        else
+            memcpy(xin, xd, sizeof(double) * (size_t)d);
+        /* weighted sum of the selected experts, in slot order [P1 sec. 3] */
+        for (int32_t j = 0; j < din; ++j)
+            routed_in[j] = 0.0;
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t e = topk_idx[(size_t)t * K + k];
+            swiglu(din, F, din, xin, L->w_dtype, L->W_gate[e], L->W_up[e], 0,
+                   L->W_down[e], (size_t)F, 0, h, y);
+            double wk = topk_w[(size_t)t * K + k];
+            for (int32_t j = 0; j < din; ++j)
+                routed_in[j] += wk * y[j];
+        }
+        /* back to the model width [P4]; identity in the K2 form */
+        if (L->d_latent)
+            matvec(d, din, L->W_lat_up, L->w_dtype, routed_in, o);
+        else
+            memcpy(o, routed_in, sizeof(double) * (size_t)d);
+        /* always-on shared experts, unweighted [P1 sec. 3; P4] */
+        for (int32_t sidx = 0; sidx < L->n_shared; ++sidx) {
+            swiglu(d, L->F_shared, d, xd, L->w_dtype, L->Ws_gate, L->Ws_up,
+                   (size_t)sidx * L->F_shared, L->Ws_down, (size_t)Fs_all,
+                   (size_t)sidx * L->F_shared, h, y);
+            for (int32_t j = 0; j < d; ++j)
+                o[j] += y[j];
+        }
+        free(xd);
+        free(xin);
+        free(routed_in);
+        free(y);
+        free(h);
+    }
+    return ORACLE_OK;
+}
+
+int oracle_forward(const oracle_layer *L, int32_t T, const void *x,
+                   double *out, int32_t *topk_idx, double *topk_w,
+                   double *gap, int32_t nthreads)
+{
+    int rc = check_layer(L);
+    if (rc)
+        return rc;
+    if (T < 0)
+        return ORACLE_ERR_SHAPE;
+    if (T == 0)
+        return ORACLE_OK;
+    if (!x || !out || !L->W_r || !L->b)
+        return ORACLE_ERR_NULL;
+    int32_t *idx = topk_idx ? topk_idx
+                            : (int32_t *)malloc(sizeof(int32_t) * (size_t)T * L->K);
+    double *w = topk_w ? topk_w
+                       : (double *)malloc(sizeof(double) * (size_t)T * L->K);
+    rc = oracle_router(T, L->d, L->E, L->K, L->act_dtype, x, L->W_r, L->b,
+                       L->scale, idx, w, gap, NULL, nthreads);
+    if (!rc)
+        rc = oracle_forward_given_routing(L, T, x, idx, w, out, nthreads);
+    if (!topk_idx)
+        free(idx);
+    if (!topk_w)
+        free(w);
+    return rc;
+}

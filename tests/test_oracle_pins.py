@@ -1,0 +1,400 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's own loops: each checks a closed form,
+a brute-force enumeration, a special case that reduces to a library
+routine, an invariant of the definition, or a number printed on a page
+(tests/golden/).  Sources:
+  Kimi K2 router card (OpenModelAtlas "Kimi K2 · Router": four-step
+  formula, in/out shapes, parameter table, MoEGate excerpt);
+  llm-arch-kb "Kimi K2 MoE" sections 2-3 (sigmoid gate, biased top-K for
+  selection only, unbiased renormalised weights, SwiGLU experts, shared
+  expert added unweighted);
+  lilting.ch K3 essay (latent compression 7168->3584, two shared experts).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as Fn
+
+import oracle
+from moe_inputs import Workload, get_workload, make_layer_inputs, make_router_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+SCALE32 = float(np.float32(2.827))  # the boundary takes the scale as fp32
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _small(**kw):
+    base = dict(name="pin", T=16, d=64, E=8, K=2, F=64, n_shared=1,
+                F_shared=64, d_latent=0, scale=2.827, act_dtype="f32",
+                w_dtype="f32", bias_range=0.02, zipf_skew=False,
+                router_only=False)
+    base.update(kw)
+    return Workload(**base)
+
+
+def _f32(a):
+    return torch.tensor(np.asarray(a, dtype=np.float32))
+
+
+# --------------------------------------------------------------------------
+# Router: hand-derived worked example (closed forms, P3 four steps)
+# --------------------------------------------------------------------------
+def test_router_worked_example_closed_form():
+    # x = e_0, so z_e = W_r[e, 0].  sigmoid(ln 3) = 3/4, sigmoid(0) = 1/2,
+    # sigmoid(-ln 3) = 1/4.  With b = (0, .3, 0, -.1):
+    #   s = (.75, .5, .25, .75), v = s + b = (.75, .8, .25, .65)
+    # top-2 of v = {1, 0}; without the bias it would be {0, 3}.
+    # Weights use the UNBIASED s: w = 2.827 * (.75, .5) / 1.25.
+    ln3 = math.log(3.0)
+    x = _f32([[1.0, 0.0]])
+    W_r = _f32([[ln3, 5.0], [0.0, -5.0], [-ln3, 7.0], [ln3, 1.0]])
+    b = _f32([0.0, 0.3, 0.0, -0.1])
+    r = oracle.router(x, W_r, b, 2, 2.827, want_scores=True)
+    assert r["idx"].tolist() == [[0, 1]]
+    np.testing.assert_allclose(r["scores"][0], [0.75, 0.5, 0.25, 0.75], rtol=1e-6)
+    np.testing.assert_allclose(r["w"][0], [SCALE32 * 0.6, SCALE32 * 0.4], rtol=1e-6)
+    np.testing.assert_allclose(r["gap"][0], 0.75 - (0.75 - 0.1), rtol=1e-5)
+
+
+def test_swiglu_worked_example_closed_form():
+    # One expert, d = 2, F = 1, x = e_0, K = 1 (w = scale), no shared expert.
+    # g = ln 3, u = 2, h = silu(g) * u = (3/4 ln 3) * 2 = 1.5 ln 3,
+    # y = W_down h with W_down = (1, -2)^T: y = (1.5 ln 3, -3 ln 3).
+    ln3 = math.log(3.0)
+    lay = oracle.Layer(d=2, E=1, K=1, F=1, scale=2.827, W_r=_f32([[0.0, 0.0]]),
+                       b=_f32([0.0]), W_gate=[_f32([[ln3, 9.0]])],
+                       W_up=[_f32([[2.0, -4.0]])], W_down=[_f32([[1.0], [-2.0]])])
+    out = oracle.forward(lay, _f32([[1.0, 0.0]]))["out"][0]
+    np.testing.assert_allclose(out, [SCALE32 * 1.5 * ln3, SCALE32 * -3.0 * ln3], rtol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# Selection: brute force over every K-subset (tiny workload)
+# --------------------------------------------------------------------------
+def test_selection_matches_bruteforce_over_all_subsets():
+    wl = get_workload("tiny_fp32_t128")
+    inp = make_router_inputs(wl, "cpu", seed=7)
+    r = oracle.router(inp["x"], inp["W_r"], inp["b"], wl.K, wl.scale, want_scores=True)
+    v = r["scores"] + inp["b"].double().numpy()[None, :]
+    subsets = np.array(list(itertools.combinations(range(wl.E), wl.K)))
+    assert len(subsets) == math.comb(32, 4) == 35960
+    M = np.zeros((len(subsets), wl.E))
+    M[np.arange(len(subsets))[:, None], subsets] = 1.0
+    sums = v @ M.T                                    # [T, C(E,K)]
+    best = np.argmax(sums, axis=1)
+    top2 = np.sort(sums, axis=1)[:, -2:]
+    assert np.all(top2[:, 1] - top2[:, 0] > 1e-12)   # unique maximiser
+    np.testing.assert_array_equal(r["idx"], subsets[best])
+
+
+# --------------------------------------------------------------------------
+# Weights: closed forms from the formula (P3) and the explanation (P3)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_fp32_t128", "mid_bf16_t300"])
+def test_weights_sum_to_scale_and_G_is_zero_off_the_set(name):
+    wl = get_workload(name)
+    inp = make_router_inputs(wl, "cpu", seed=3)
+    r = oracle.router(inp["x"], inp["W_r"], inp["b"], wl.K, wl.scale)
+    idx, w = r["idx"], r["w"]
+    np.testing.assert_allclose(w.sum(1), float(np.float32(wl.scale)), rtol=1e-12)
+    assert np.all(np.diff(idx, axis=1) > 0)          # K distinct, ascending
+    assert np.all((idx >= 0) & (idx < wl.E))
+    G = np.zeros((wl.T, wl.E))
+    np.put_along_axis(G, idx, w, axis=1)
+    assert np.all((G > 0).sum(1) == wl.K)
+    assert np.all((G == 0).sum(1) == wl.E - wl.K)
+
+
+def test_k2_card_shapes_and_376_zeros():
+    card = _golden("k2_router_card.json")
+    wl = get_workload("k2_router_t4096")
+    assert (wl.d, wl.E, wl.K, wl.scale) == (card["hidden_size"], card["n_routed_experts"],
+                                            card["top_k"], card["routed_scaling_factor"])
+    inp = make_router_inputs(wl, "cpu", seed=11, T=4)
+    # parameter table: W_r [E, d] plus b [E]
+    assert inp["W_r"].numel() == card["params_expert_scores"]
+    assert inp["b"].numel() == card["params_select_bias"]
+    assert inp["W_r"].numel() + inp["b"].numel() == card["params_per_instance"]
+    assert card["params_per_instance"] * card["moe_blocks"] == card["params_all_moe_blocks"]
+    r = oracle.router(inp["x"], inp["W_r"], inp["b"], wl.K, wl.scale)
+    G = np.zeros((4, wl.E))
+    np.put_along_axis(G, r["idx"], r["w"], axis=1)
+    assert np.all((G == 0).sum(1) == card["zeros_per_token_in_G"])
+    np.testing.assert_allclose(G.sum(1), float(np.float32(card["routed_scaling_factor"])),
+                               rtol=1e-12)
+
+
+def test_k3_workload_matches_k3_table():
+    tab = _golden("k3_dimensions.json")
+    wl = get_workload("k3_latent_t4096")
+    assert (wl.d, wl.E, wl.K, wl.n_shared, wl.d_latent, wl.F, wl.F_shared) == (
+        tab["hidden_size"], tab["n_routed_experts"], tab["top_k"],
+        tab["n_shared_experts"], tab["latent_dim"], tab["intermediate_dim"],
+        tab["intermediate_dim"])
+
+
+def test_k2_expert_width_consistent_with_parameter_accounting():
+    acc = _golden("k2_kb_accounting.json")
+    wl = get_workload("k2_decode_t256")
+    card = _golden("k2_router_card.json")
+    per_expert = 3 * wl.d * wl.F
+    routed_all = acc["n_routed_experts"] * per_expert * card["moe_blocks"]
+    active_moe = (acc["top_k"] + acc["n_shared_experts"]) * per_expert * card["moe_blocks"]
+    # routed experts are most, but not more, of the ~1.04T total; the active
+    # MoE part is most, but not more, of the ~32B active
+    assert 0.9 * acc["total_params_approx"] < routed_all < acc["total_params_approx"]
+    assert 0.6 * acc["active_params_approx"] < active_moe < acc["active_params_approx"]
+
+
+def test_bias_selects_but_does_not_weight():
+    # W_r = 0: every s = 1/2, so the selection is the top-K of b alone and
+    # every weight is scale / K whatever b is (bias used only for choice).
+    wl = _small(E=12, K=3, T=5)
+    rng = np.random.default_rng(0)
+    b = rng.permutation(np.linspace(-0.05, 0.05, 12)).astype(np.float32)
+    x = _f32(rng.standard_normal((5, wl.d)))
+    r = oracle.router(x, _f32(np.zeros((12, wl.d))), _f32(b), 3, 2.827, want_scores=True)
+    np.testing.assert_array_equal(r["scores"], 0.5)
+    expect = np.sort(np.argsort(-b)[:3])
+    assert all(row.tolist() == expect.tolist() for row in r["idx"])
+    np.testing.assert_allclose(r["w"], SCALE32 / 3, rtol=1e-15)
+
+
+def test_ties_go_to_the_lower_expert_index():
+    # W_r = 0 and b = 0: all biased scores tie, the first K experts win.
+    x = _f32(np.ones((3, 16)))
+    r = oracle.router(x, _f32(np.zeros((10, 16))), _f32(np.zeros(10)), 4, 2.827)
+    assert r["idx"].tolist() == [[0, 1, 2, 3]] * 3
+    assert np.all(r["gap"] == 0.0)
+
+
+def test_sigmoid_one_hot_and_K_equals_E():
+    # x = e_j makes z_e = W_r[e, j] exactly; with K = E every expert is
+    # selected and w_e = scale * sigmoid(W_r[e,j]) / sum_e' sigmoid(W_r[e',j]).
+    rng = np.random.default_rng(1)
+    E, d, j = 9, 32, 5
+    W_r = rng.standard_normal((E, d)).astype(np.float32)
+    x = np.zeros((1, d), np.float32)
+    x[0, j] = 1.0
+    r = oracle.router(_f32(x), _f32(W_r), _f32(np.zeros(E)), E, 2.827, want_scores=True)
+    s = scipy.special.expit(W_r[:, j].astype(np.float64))
+    np.testing.assert_allclose(r["scores"][0], s, rtol=1e-14)
+    assert r["idx"][0].tolist() == list(range(E))
+    np.testing.assert_allclose(r["w"][0], SCALE32 * s / s.sum(), rtol=1e-13)
+    assert math.isinf(r["gap"][0])
+
+
+def test_K_equals_one_gives_the_scale_exactly():
+    wl = _small(K=1, T=20)
+    inp = make_router_inputs(wl, "cpu", seed=5)
+    r = oracle.router(inp["x"], inp["W_r"], inp["b"], 1, 2.827)
+    assert np.all(r["w"] == SCALE32)
+
+
+# --------------------------------------------------------------------------
+# Experts and combine: special cases reducing to library routines
+# --------------------------------------------------------------------------
+def _torch_swiglu(x, Wg, Wu, Wd):
+    """SwiGLU with torch's silu and matmul in float64 (library routines)."""
+    return (Fn.silu(x @ Wg.T) * (x @ Wu.T)) @ Wd.T
+
+
+def test_single_expert_layer_reduces_to_library_swiglu():
+    wl = _small(E=1, K=1, T=9, d=96, F=64, F_shared=128)
+    inp = make_layer_inputs(wl, "cpu", seed=9)
+    lay = oracle.layer_from_inputs(wl, inp)
+    out = oracle.forward(lay, inp["x"])["out"]
+    x = inp["x"].double()
+    routed = _torch_swiglu(x, inp["W_gate"][0].double(), inp["W_up"][0].double(),
+                           inp["W_down"][0].double())
+    shared = _torch_swiglu(x, inp["Ws_gate"].double(), inp["Ws_up"].double(),
+                           inp["Ws_down"].double())
+    expect = shared + SCALE32 * routed
+    np.testing.assert_allclose(out, expect.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_identical_experts_give_shared_plus_scale_times_expert():
+    wl = _small(E=6, K=3, T=11)
+    inp = make_layer_inputs(wl, "cpu", seed=4)
+    for k in ("W_gate", "W_up", "W_down"):
+        inp[k] = inp[k][:1].repeat(wl.E, 1, 1).contiguous()
+    out = oracle.forward(oracle.layer_from_inputs(wl, inp), inp["x"])["out"]
+    x = inp["x"].double()
+    routed = _torch_swiglu(x, inp["W_gate"][0].double(), inp["W_up"][0].double(),
+                           inp["W_down"][0].double())
+    shared = _torch_swiglu(x, inp["Ws_gate"].double(), inp["Ws_up"].double(),
+                           inp["Ws_down"].double())
+    np.testing.assert_allclose(out, (shared + SCALE32 * routed).numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_zero_down_projection_leaves_the_shared_expert_and_is_linear():
+    wl = _small(E=7, K=2, T=13)
+    inp = make_layer_inputs(wl, "cpu", seed=12)
+    x = inp["x"]
+    base = oracle.forward(oracle.layer_from_inputs(wl, inp), x)["out"]
+    shared = _torch_swiglu(x.double(), inp["Ws_gate"].double(), inp["Ws_up"].double(),
+                           inp["Ws_down"].double()).numpy()
+    zero = dict(inp, W_down=torch.zeros_like(inp["W_down"]))
+    np.testing.assert_allclose(oracle.forward(oracle.layer_from_inputs(wl, zero), x)["out"],
+                               shared, rtol=1e-12, atol=1e-13)
+    dbl = dict(inp, W_down=(inp["W_down"] * 2).contiguous())   # exact in fp32
+    out2 = oracle.forward(oracle.layer_from_inputs(wl, dbl), x)["out"]
+    np.testing.assert_allclose(out2 - shared, 2 * (base - shared), rtol=1e-10, atol=1e-12)
+
+
+def test_no_shared_expert_and_only_shared_expert():
+    wl = _small(E=5, K=2, T=6, n_shared=0, F_shared=0)
+    inp = make_layer_inputs(wl, "cpu", seed=21)
+    lay = oracle.layer_from_inputs(wl, inp)
+    r = oracle.forward(lay, inp["x"])
+    # without a shared expert the output is exactly the weighted routed sum
+    x = inp["x"].double()
+    expect = torch.zeros(wl.T, wl.d, dtype=torch.float64)
+    for t in range(wl.T):
+        for k in range(wl.K):
+            e = int(r["idx"][t, k])
+            expect[t] += r["w"][t, k] * _torch_swiglu(
+                x[t:t + 1], inp["W_gate"][e].double(), inp["W_up"][e].double(),
+                inp["W_down"][e].double())[0]
+    np.testing.assert_allclose(r["out"], expect.numpy(), rtol=1e-11, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Dispatch: invariants and brute-force counts
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_fp32_t128", "mid_bf16_t300"])
+def test_dispatch_invariants(name):
+    wl = get_workload(name)
+    inp = make_router_inputs(wl, "cpu", seed=2)
+    idx = oracle.router(inp["x"], inp["W_r"], inp["b"], wl.K, wl.scale)["idx"]
+    dsp = oracle.dispatch(idx, wl.E)
+    counts, offsets, st, pos = dsp["counts"], dsp["offsets"], dsp["sorted_token"], dsp["pos"]
+    assert counts.sum() == wl.T * wl.K
+    np.testing.assert_array_equal(counts, np.bincount(idx.ravel(), minlength=wl.E))
+    assert offsets[0] == 0 and offsets[-1] == wl.T * wl.K
+    np.testing.assert_array_equal(np.diff(offsets), counts)
+    pairs = set()
+    for e in range(wl.E):
+        seg = st[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(seg) > 0)               # strictly ascending tokens
+        expect = np.nonzero((idx == e).any(1))[0]     # brute force membership
+        np.testing.assert_array_equal(seg, expect)
+        pairs.update((int(t), e) for t in seg)
+    assert len(pairs) == wl.T * wl.K
+    # pos is the inverse map of the permutation
+    for t in range(wl.T):
+        for k in range(wl.K):
+            p = pos[t, k]
+            assert st[p] == t and offsets[idx[t, k]] <= p < offsets[idx[t, k] + 1]
+
+
+def test_dispatch_with_empty_experts():
+    idx = np.array([[0, 3], [3, 5], [0, 5]], np.int32)
+    dsp = oracle.dispatch(idx, 7)
+    assert dsp["counts"].tolist() == [2, 0, 0, 2, 0, 2, 0]
+    assert dsp["offsets"].tolist() == [0, 2, 2, 2, 4, 4, 6, 6]
+    assert dsp["sorted_token"].tolist() == [0, 2, 0, 1, 1, 2]
+    assert dsp["pos"].tolist() == [[0, 2], [3, 4], [1, 5]]
+
+
+# --------------------------------------------------------------------------
+# Layer invariants
+# --------------------------------------------------------------------------
+def test_tokens_are_independent():
+    wl = get_workload("mid_fp32_t77")
+    inp = make_layer_inputs(wl, "cpu", seed=8)
+    lay = oracle.layer_from_inputs(wl, inp)
+    whole = oracle.forward(lay, inp["x"])
+    parts = [oracle.forward(lay, inp["x"][a:a + 20]) for a in range(0, wl.T, 20)]
+    np.testing.assert_array_equal(whole["idx"], np.concatenate([p["idx"] for p in parts]))
+    np.testing.assert_array_equal(whole["out"], np.concatenate([p["out"] for p in parts]))
+
+
+def test_expert_relabelling_is_equivariant():
+    wl = _small(E=10, K=3, T=15)
+    inp = make_layer_inputs(wl, "cpu", seed=13)
+    lay = oracle.layer_from_inputs(wl, inp)
+    ref = oracle.forward(lay, inp["x"])
+    perm = np.random.default_rng(5).permutation(wl.E)       # new label i -> old perm[i]
+    p = torch.from_numpy(perm)
+    inp2 = dict(inp, W_r=inp["W_r"][p].contiguous(), b=inp["b"][p].contiguous(),
+                W_gate=inp["W_gate"][p].contiguous(), W_up=inp["W_up"][p].contiguous(),
+                W_down=inp["W_down"][p].contiguous())
+    got = oracle.forward(oracle.layer_from_inputs(wl, inp2), inp["x"])
+    inv = np.argsort(perm)
+    for t in range(wl.T):
+        assert sorted(perm[got["idx"][t]].tolist()) == ref["idx"][t].tolist()
+        wmap = dict(zip(perm[got["idx"][t]].tolist(), got["w"][t].tolist()))
+        np.testing.assert_allclose([wmap[e] for e in ref["idx"][t]], ref["w"][t], rtol=1e-12)
+    assert inv is not None
+    np.testing.assert_allclose(got["out"], ref["out"], rtol=1e-11, atol=1e-12)
+
+
+def test_latent_form_with_identity_maps_equals_plain_form():
+    wl = _small(E=6, K=2, T=10, d=64)
+    inp = make_layer_inputs(wl, "cpu", seed=14)
+    ref = oracle.forward(oracle.layer_from_inputs(wl, inp), inp["x"])["out"]
+    wl_lat = _small(E=6, K=2, T=10, d=64, d_latent=64)
+    eye = torch.eye(64, dtype=torch.float32)
+    inp_lat = dict(inp, W_lat_down=eye, W_lat_up=eye)
+    got = oracle.forward(oracle.layer_from_inputs(wl_lat, inp_lat), inp["x"])["out"]
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-14)
+
+
+def test_latent_form_matches_library_composition():
+    wl = _small(E=1, K=1, T=7, d=96, d_latent=32, F=48, n_shared=2, F_shared=40)
+    inp = make_layer_inputs(wl, "cpu", seed=15)
+    out = oracle.forward(oracle.layer_from_inputs(wl, inp), inp["x"])["out"]
+    x = inp["x"].double()
+    xl = x @ inp["W_lat_down"].double().T
+    routed = _torch_swiglu(xl, inp["W_gate"][0].double(), inp["W_up"][0].double(),
+                           inp["W_down"][0].double()) @ inp["W_lat_up"].double().T
+    Wg, Wu, Wd = (inp[k].double() for k in ("Ws_gate", "Ws_up", "Ws_down"))
+    shared = (_torch_swiglu(x, Wg[:40], Wu[:40], Wd[:, :40]) +
+              _torch_swiglu(x, Wg[40:], Wu[40:], Wd[:, 40:]))
+    np.testing.assert_allclose(out, (shared + SCALE32 * routed).numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_two_shared_experts_equal_one_of_double_width():
+    wl2 = _small(E=4, K=2, T=8, n_shared=2, F_shared=32)
+    inp = make_layer_inputs(wl2, "cpu", seed=16)
+    two = oracle.forward(oracle.layer_from_inputs(wl2, inp), inp["x"])["out"]
+    wl1 = _small(E=4, K=2, T=8, n_shared=1, F_shared=64)
+    one = oracle.forward(oracle.layer_from_inputs(wl1, inp), inp["x"])["out"]
+    np.testing.assert_allclose(two, one, rtol=1e-12, atol=1e-13)
+
+
+def test_bf16_inputs_are_upcast_exactly():
+    # the same values given as bf16 or as fp32 give bit-identical results
+    wl = get_workload("mid_bf16_t300").with_tokens(12)
+    inp = make_layer_inputs(wl, "cpu", seed=17)
+    lay = oracle.layer_from_inputs(wl, inp)
+    a = oracle.forward(lay, inp["x"])
+    inp32 = {k: (v.float() if isinstance(v, torch.Tensor) and v.dtype == torch.bfloat16 else v)
+             for k, v in inp.items()}
+    b = oracle.forward(oracle.layer_from_inputs(wl, inp32), inp32["x"])
+    np.testing.assert_array_equal(a["out"], b["out"])
+    np.testing.assert_array_equal(a["idx"], b["idx"])
+
+
+def test_missing_expert_is_an_error():
+    wl = _small(E=6, K=2, T=4)
+    inp = make_layer_inputs(wl, "cpu", seed=18)
+    r = oracle.router(inp["x"], inp["W_r"], inp["b"], wl.K, wl.scale)
+    used = set(np.unique(r["idx"]).tolist())
+    lay = oracle.layer_from_inputs(wl, inp, experts=used)
+    oracle.forward_given_routing(lay, inp["x"], r["idx"], r["w"])   # enough
+    lay2 = oracle.layer_from_inputs(wl, inp, experts=used - {min(used)})
+    with pytest.raises(oracle.OracleError):
+        oracle.forward_given_routing(lay2, inp["x"], r["idx"], r["w"])
