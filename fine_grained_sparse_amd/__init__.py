@@ -1,0 +1,237 @@
+"""MI355X (gfx950) forward pass of a Kimi-K2-style fine-grained MoE layer.
+
+Thin Python binding of libmoe.so, the C-ABI library declared in
+include/moe.h.  This module only marshals arguments: it checks tensor
+shapes and dtypes, allocates outputs and the workspace with torch (device
+memory and streams are the only things torch is used for) and calls
+moe_router / moe_forward.  Every step of the layer runs in the library's
+HIP kernels; there is no fallback, and importing this module without the
+built library raises.
+
+Layer (OpenModelAtlas "Kimi K2 · Router" four steps; llm-arch-kb "Kimi K2
+MoE" sections 2-3; lilting.ch K3 essay for the latent form):
+    s = sigmoid(x W_r^T);  S = top_K(s + b);  w_i = scale * s_i / (sum_S s + 1e-20)
+    out = sum_shared f_s(x) + U(sum_{i in S} w_i f_i(L(x)))
+with SwiGLU experts f(v) = W_down (silu(W_gate v) * (W_up v)).
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+_STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
+           4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_UNSUPPORTED", 6: "MOE_ERR_HIP"}
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+EXPORTS = ("moe_workspace_size", "moe_router", "moe_forward", "moe_status_str")
+STAGES = ("start", "router", "dispatch", "latent", "up", "down", "end")
+NUM_STAGE_EVENTS = len(STAGES)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = lib().moe_status_str(status).decode()
+        super().__init__(f"{fn}: {_STATUS.get(status, status)} ({msg})")
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("F", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("F_shared", ctypes.c_int32), ("d_latent", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("act_dtype", ctypes.c_int32),
+                ("w_dtype", ctypes.c_int32)]
+
+
+class ExpertWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("W_gate", "W_up", "W_down", "Ws_gate", "Ws_up", "Ws_down",
+                 "W_lat_down", "W_lat_up")]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "fine_grained_sparse_amd/build.py (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        L.moe_workspace_size.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_int]
+        L.moe_workspace_size.restype = ctypes.c_size_t
+        L.moe_router.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, vp, vp, vp, vp, vp,
+                                 ctypes.c_size_t, vp]
+        L.moe_router.restype = ctypes.c_int
+        L.moe_forward.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, vp,
+                                  ctypes.POINTER(ExpertWeights), vp, vp, vp, vp, vp, vp,
+                                  vp, ctypes.c_size_t, vp, vp]
+        L.moe_forward.restype = ctypes.c_int
+        L.moe_status_str.argtypes = [ctypes.c_int]
+        L.moe_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def desc(*, T, d, E, K, F=0, n_shared=0, F_shared=0, d_latent=0, scale=2.827,
+         act_dtype=MOE_BF16, w_dtype=None):
+    return LayerDesc(T, d, E, K, F, n_shared, F_shared, d_latent, scale, act_dtype,
+                     act_dtype if w_dtype is None else w_dtype)
+
+
+def workspace_size(layer_desc: LayerDesc, forward: bool) -> int:
+    return int(lib().moe_workspace_size(ctypes.byref(layer_desc), 1 if forward else 0))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+class Workspace:
+    """A growable device byte buffer (allocated by torch, owned here)."""
+
+    def __init__(self):
+        self._buf = {}
+
+    def get(self, device, nbytes):
+        buf = self._buf.get(device)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self._buf[device] = buf
+        return buf
+
+
+_default_ws = Workspace()
+
+
+def router(x, W_r, b, K, scale=2.827, *, counts=True, workspace=None, stream=None):
+    """moe_router: returns (topk_idx int32 [T,K], topk_w fp32 [T,K],
+    expert_counts int32 [E] or None).  Slots are in ascending expert id."""
+    _need(x, "x")
+    if x.dim() != 2 or x.dtype not in _DT:
+        raise ValueError("x must be [T, d] fp32 or bf16")
+    T, d = x.shape
+    dev = x.device
+    _need(W_r, "W_r", torch.float32, device=dev)
+    E = W_r.shape[0]
+    _need(W_r, "W_r", torch.float32, (E, d))
+    _need(b, "b", torch.float32, (E,), dev)
+    D = desc(T=T, d=d, E=E, K=K, scale=scale, act_dtype=_DT[x.dtype])
+    nbytes = workspace_size(D, False)
+    if nbytes == 0:
+        raise MoeError("moe_workspace_size", 2)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    cnt = torch.empty((E,), dtype=torch.int32, device=dev) if counts else None
+    ws = (workspace or _default_ws).get(dev, nbytes)
+    rc = lib().moe_router(ctypes.byref(D), _ptr(x), _ptr(W_r), _ptr(b), _ptr(idx), _ptr(w),
+                          _ptr(cnt), _ptr(ws), nbytes, _stream(stream))
+    if rc:
+        raise MoeError("moe_router", rc)
+    return idx, w, cnt
+
+
+def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
+            return_routing=False, workspace=None, stream=None, stage_events=None):
+    """moe_forward: the whole layer.  `weights` holds W_gate [E,F,d_in],
+    W_up [E,F,d_in], W_down [E,d_in,F] and optionally Ws_gate/Ws_up
+    [n_shared*F_shared, d], Ws_down [d, n_shared*F_shared], W_lat_down
+    [d_latent, d], W_lat_up [d, d_latent].  Returns out [T, d], or
+    (out, routing dict) with return_routing=True.  `stage_events` (optional)
+    is a sequence of NUM_STAGE_EVENTS already-created torch.cuda.Event
+    objects recorded at the stage boundaries listed in include/moe.h."""
+    _need(x, "x")
+    if x.dim() != 2 or x.dtype not in _DT:
+        raise ValueError("x must be [T, d] fp32 or bf16")
+    T, d = x.shape
+    dev, dt = x.device, x.dtype
+    E = W_r.shape[0]
+    _need(W_r, "W_r", torch.float32, (E, d), dev)
+    _need(b, "b", torch.float32, (E,), dev)
+    Wg, Wu, Wd = weights["W_gate"], weights["W_up"], weights["W_down"]
+    _need(Wg, "W_gate", dt, device=dev)
+    if Wg.dim() != 3 or Wg.shape[0] != E:
+        raise ValueError("W_gate must be [E, F, d_in]")
+    F, din = Wg.shape[1], Wg.shape[2]
+    _need(Wu, "W_up", dt, (E, F, din), dev)
+    _need(Wd, "W_down", dt, (E, din, F), dev)
+    Wl_d, Wl_u = weights.get("W_lat_down"), weights.get("W_lat_up")
+    d_lat = 0
+    if Wl_d is not None or Wl_u is not None:
+        d_lat = din
+        _need(Wl_d, "W_lat_down", dt, (d_lat, d), dev)
+        _need(Wl_u, "W_lat_up", dt, (d, d_lat), dev)
+    elif din != d:
+        raise ValueError("experts act on d_in != d but no latent maps were given")
+    Wsg, Wsu, Wsd = weights.get("Ws_gate"), weights.get("Ws_up"), weights.get("Ws_down")
+    ns = 0 if Wsg is None else (1 if n_shared is None else n_shared)
+    Fs = 0
+    if ns:
+        if Wsg.shape[0] % ns:
+            raise ValueError("Ws_gate rows must be n_shared * F_shared")
+        Fs = Wsg.shape[0] // ns
+        _need(Wsg, "Ws_gate", dt, (ns * Fs, d), dev)
+        _need(Wsu, "Ws_up", dt, (ns * Fs, d), dev)
+        _need(Wsd, "Ws_down", dt, (d, ns * Fs), dev)
+    D = desc(T=T, d=d, E=E, K=K, F=F, n_shared=ns, F_shared=Fs, d_latent=d_lat,
+             scale=scale, act_dtype=_DT[dt])
+    nbytes = workspace_size(D, True)
+    if nbytes == 0:
+        raise MoeError("moe_workspace_size", 2)
+    if out is None:
+        out = torch.empty((T, d), dtype=dt, device=dev)
+    else:
+        _need(out, "out", dt, (T, d), dev)
+    W = ExpertWeights(*[None if t is None else t.data_ptr() for t in
+                        (Wg, Wu, Wd, Wsg, Wsu, Wsd, Wl_d, Wl_u)])
+    routing = None
+    if return_routing:
+        routing = dict(idx=torch.empty((T, K), dtype=torch.int32, device=dev),
+                       w=torch.empty((T, K), dtype=torch.float32, device=dev),
+                       counts=torch.empty((E,), dtype=torch.int32, device=dev),
+                       offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+                       sorted_token=torch.empty((max(T * K, 1),), dtype=torch.int32, device=dev))
+    r = routing or {}
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != NUM_STAGE_EVENTS:
+            raise ValueError(f"stage_events needs {NUM_STAGE_EVENTS} events")
+        ev = (ctypes.c_void_p * NUM_STAGE_EVENTS)(*[e.cuda_event or None for e in stage_events])
+    ws = (workspace or _default_ws).get(dev, nbytes)
+    rc = lib().moe_forward(ctypes.byref(D), _ptr(x), _ptr(W_r), _ptr(b), ctypes.byref(W),
+                           _ptr(out), _ptr(r.get("idx")), _ptr(r.get("w")), _ptr(r.get("counts")),
+                           _ptr(r.get("offsets")), _ptr(r.get("sorted_token")), _ptr(ws), nbytes,
+                           _stream(stream), ev)
+    if rc:
+        raise MoeError("moe_forward", rc)
+    return (out, routing) if return_routing else out
+
+
+__all__ = ["router", "forward", "workspace_size", "desc", "lib", "MoeError",
+           "LayerDesc", "ExpertWeights", "Workspace", "MOE_F32", "MOE_BF16", "EXPORTS"]

@@ -1,0 +1,285 @@
+// Grouped GEMM on gfx950 MFMA for the MoE layer.
+//
+// One kernel template computes C = epi(A * B^T) over a list of tiles:
+//   - routed experts: each tile is up to BM consecutive rows of the
+//     expert-sorted assignment space; A rows are gathered through a row map
+//     (sorted position -> token) while they are loaded, B is that expert's
+//     [N, K] weight matrix;
+//   - dense groups (shared experts, latent maps, router): plain row tiles.
+// The SwiGLU epilogue computes H = silu(A Wg^T) * (A Wu^T) with the gate and
+// up tiles held by the same lanes (the expert form of the llm-arch-kb
+// "Kimi K2 MoE" entry, section 2: three matrices per expert).
+//
+// Data flow per workgroup (256 threads = 4 waves of 64):
+//   global --(16 B per lane, coalesced rows)--> registers --> LDS (two
+//   stages, 144-byte padded rows) --> MFMA fragments --> fp32 accumulators
+//   --> LDS epilogue tile --> 16-byte coalesced stores.
+// A K stage is 128 bytes of each row (64 bf16 or 32 fp32); each 64-byte
+// slab of a stage feeds one v_mfma_f32_16x16x32_bf16 (or four
+// v_mfma_f32_16x16x4_f32) per 16x16 block.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+int tile_bm(TileCfg cfg) { return cfg == TILE_SMALL ? 16 : 128; }
+int tile_bn_out(TileCfg cfg, Epi epi) {
+    int bn = cfg == TILE_SMALL ? 256 : 128;
+    return epi == EPI_SWIGLU ? bn / 2 : bn;
+}
+
+namespace {
+
+constexpr int kStageRowBytes = 128;
+constexpr int kLdsRowBytes = 144;  // 16 bytes of padding against bank conflicts
+
+__device__ __forceinline__ const GemmSeg& seg_of(const GemmGroup& G, int s) {
+    return s == 0 ? G.seg[0] : (s == 1 ? G.seg[1] : G.seg[2]);
+}
+
+template <typename T, typename TC, int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
+    constexpr int ES = sizeof(T);
+    constexpr int BKE = kStageRowBytes / ES;  // K elements per stage
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int MB = TM / 16, NB = TN / 16;
+    constexpr int BNO = EPI == EPI_SWIGLU ? BN / 2 : BN;
+    constexpr int A_CH = BM * 8, B_CH = BN * 8;  // 16-byte chunks per stage
+    constexpr int LA = (A_CH + 255) / 256, LB = B_CH / 256;
+    constexpr int STAGE = (BM + BN) * kLdsRowBytes;
+    constexpr int EP_STRIDE = BNO + 4;
+    constexpr int LDS_BYTES = (2 * STAGE > BM * EP_STRIDE * 4) ? 2 * STAGE : BM * EP_STRIDE * 4;
+    static_assert(WM * WN == 4, "four waves");
+    static_assert(B_CH % 256 == 0, "B tile chunks");
+    static_assert(EPI != EPI_SWIGLU || NB % 2 == 0, "gate/up pairs per wave");
+    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm = wid / WN, wn = wid % WN;
+
+    // ---- which tile: linear block id -> (M tile, N tile), N fastest, so
+    // the workgroups that share an A tile are launched together and the
+    // M tiles of one expert read each weight tile on the same XCD when the
+    // N-tile count is a multiple of the eight XCDs.
+    int gi = 0, expert = 0, row0, rows;
+    const int mt = static_cast<int>(blockIdx.x) / a.ntn;
+    const int nt_n = static_cast<int>(blockIdx.x) % a.ntn;
+    if (a.tiles) {
+        if (mt >= *a.ntiles) return;
+        const TileInfo ti = a.tiles[mt];
+        gi = ti.group;
+        expert = ti.expert;
+        row0 = ti.row0;
+        rows = ti.rows;
+    } else {
+        row0 = mt * BM;
+        rows = min(BM, a.M - row0);
+        if (rows <= 0) return;
+    }
+    const GemmGroup& G = gi ? a.g[1] : a.g[0];
+    const int N = G.N;
+    const int n0 = nt_n * BNO;
+    if (n0 >= N) return;
+
+    // ---- split-K range over the concatenated segments
+    int nk = 0;
+    for (int s = 0; s < G.nseg; ++s) nk += seg_of(G, s).K / BKE;
+    const int chunk = (nk + a.nsplit - 1) / a.nsplit;
+    const int kt0 = min(nk, static_cast<int>(blockIdx.z) * chunk);
+    const int kt1 = min(nk, kt0 + chunk);
+
+    // ---- per-thread source rows
+    int arow[LA];
+    int achunk[LA];
+    bool aval[LA];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int c = tid + i * 256;
+        aval[i] = c < A_CH;
+        const int r = aval[i] ? (c >> 3) : 0;
+        const int p = row0 + (r < rows ? r : 0);
+        arow[i] = G.rowmap ? G.rowmap[p] : p;
+        achunk[i] = c & 7;
+    }
+    int bn_[LB];
+    bool bup[LB];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int c = tid + i * 256;
+        const int q = c >> 3;
+        int n;
+        if (EPI == EPI_SWIGLU) {
+            const int blk = q / TN, rq = q % TN, half = TN / 2;
+            n = n0 + blk * half + (rq % half);
+            bup[i] = rq >= half;
+        } else {
+            n = n0 + q;
+            bup[i] = false;
+        }
+        bn_[i] = n < N ? n : N - 1;
+    }
+
+    // ---- global load cursor (segment s, step kk within it)
+    int cs = 0, ck = kt0;
+    while (cs + 1 < G.nseg && ck >= seg_of(G, cs).K / BKE) {
+        ck -= seg_of(G, cs).K / BKE;
+        ++cs;
+    }
+    const char* ap[LA];
+    const char* bp[LB];
+    auto set_ptrs = [&](int s) {
+        const GemmSeg& S = seg_of(G, s);
+        const int64_t eoff = s == 0 ? static_cast<int64_t>(expert) * G.b_estride : 0;
+#pragma unroll
+        for (int i = 0; i < LA; ++i)
+            ap[i] = static_cast<const char*>(S.A) + (static_cast<int64_t>(arow[i]) * S.lda) * ES + achunk[i] * 16;
+#pragma unroll
+        for (int i = 0; i < LB; ++i) {
+            const void* base = bup[i] ? S.Bu : S.B;
+            bp[i] = static_cast<const char*>(base) + (eoff + static_cast<int64_t>(bn_[i]) * S.ldb) * ES + ((tid + i * 256) & 7) * 16;
+        }
+    };
+    set_ptrs(cs);
+
+    uint4 ra[LA], rb[LB];
+    auto gload = [&]() {
+        const int64_t off = static_cast<int64_t>(ck) * kStageRowBytes;
+#pragma unroll
+        for (int i = 0; i < LA; ++i)
+            if (aval[i]) ra[i] = ldg16(ap[i] + off);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) rb[i] = ldg16(bp[i] + off);
+        ++ck;
+        if (cs + 1 < G.nseg && ck == seg_of(G, cs).K / BKE) {
+            ++cs;
+            ck = 0;
+            set_ptrs(cs);
+        }
+    };
+    auto lstore = [&](int stage) {
+        char* As = lds + stage * STAGE;
+        char* Bs = As + BM * kLdsRowBytes;
+#pragma unroll
+        for (int i = 0; i < LA; ++i)
+            if (aval[i]) {
+                const int c = tid + i * 256;
+                *reinterpret_cast<uint4*>(As + (c >> 3) * kLdsRowBytes + (c & 7) * 16) = ra[i];
+            }
+#pragma unroll
+        for (int i = 0; i < LB; ++i) {
+            const int c = tid + i * 256;
+            *reinterpret_cast<uint4*>(Bs + (c >> 3) * kLdsRowBytes + (c & 7) * 16) = rb[i];
+        }
+    };
+
+    f32x4 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int frow = lane & 15;
+    const int fcol = (lane >> 4) * 16;
+    if (kt0 < kt1) {
+        gload();
+        lstore(0);
+        __syncthreads();
+        for (int kt = kt0; kt < kt1; ++kt) {
+            const int cur = (kt - kt0) & 1;
+            const bool more = kt + 1 < kt1;
+            if (more) gload();
+            const char* As = lds + cur * STAGE;
+            const char* Bs = As + BM * kLdsRowBytes;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                uint4 fa[MB], fb[NB];
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    fa[i] = *reinterpret_cast<const uint4*>(As + (wm * TM + i * 16 + frow) * kLdsRowBytes + s * 64 + fcol);
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    fb[j] = *reinterpret_cast<const uint4*>(Bs + (wn * TN + j * 16 + frow) * kLdsRowBytes + s * 64 + fcol);
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) acc[i][j] = Mfma<T>::run(fa[i], fb[j], acc[i][j]);
+            }
+            if (more) lstore(cur ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: accumulators -> LDS tile (fp32) -> coalesced stores.
+    // MFMA 16x16 output layout: lane l holds rows 4*(l/16)+r, column l%16.
+    float* ep = reinterpret_cast<float*>(lds);
+    if (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB / 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = wm * TM + i * 16 + (lane >> 4) * 4 + r;
+                    const int col = wn * (TN / 2) + j * 16 + (lane & 15);
+                    const float g = acc[i][j][r], u = acc[i][j + NB / 2][r];
+                    ep[row * EP_STRIDE + col] = g / (1.0f + expf(-g)) * u;
+                }
+    } else {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = wm * TM + i * 16 + (lane >> 4) * 4 + r;
+                    const int col = wn * TN + j * 16 + (lane & 15);
+                    ep[row * EP_STRIDE + col] = acc[i][j][r];
+                }
+    }
+    __syncthreads();
+    constexpr int CPR = BNO / 8;
+    TC* C = static_cast<TC*>(G.C) + static_cast<int64_t>(blockIdx.z) * a.split_stride;
+    for (int c = tid; c < BM * CPR; c += 256) {
+        const int r = c / CPR, cc = c % CPR;
+        const int col = n0 + cc * 8;
+        if (r >= rows || col >= N) continue;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = ep[r * EP_STRIDE + cc * 8 + e];
+        TC* dst = C + static_cast<int64_t>(row0 + r) * G.ldc + col;
+        if (col + 8 <= N) {
+            pack8(dst, v);
+        } else {
+            for (int e = 0; e < N - col; ++e) dst[e] = Elem<TC>::from_f32(v[e]);
+        }
+    }
+}
+
+template <typename T, typename TC, int EPI>
+hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n, hipStream_t stream) {
+    const int bno = tile_bn_out(cfg, static_cast<Epi>(EPI));
+    GemmArgs a = args;
+    a.ntn = (max_n + bno - 1) / bno;
+    dim3 grid(static_cast<unsigned>(max_tiles) * a.ntn, 1, a.nsplit);
+    if (cfg == TILE_SMALL)
+        hipLaunchKernelGGL((k_gemm<T, TC, 16, 256, 1, 4, EPI>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_gemm<T, TC, 128, 128, 2, 2, EPI>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& args, DType dt, bool out_f32, Epi epi, TileCfg cfg, int max_tiles,
+                       int max_n, hipStream_t stream) {
+    if (max_tiles <= 0 || max_n <= 0) return hipSuccess;
+    if (dt == DT_F32) {
+        if (epi == EPI_SWIGLU) return launch_t<float, float, EPI_SWIGLU>(args, cfg, max_tiles, max_n, stream);
+        return launch_t<float, float, EPI_STORE>(args, cfg, max_tiles, max_n, stream);
+    }
+    if (out_f32) return launch_t<bf16_t, float, EPI_STORE>(args, cfg, max_tiles, max_n, stream);
+    if (epi == EPI_SWIGLU) return launch_t<bf16_t, bf16_t, EPI_SWIGLU>(args, cfg, max_tiles, max_n, stream);
+    return launch_t<bf16_t, bf16_t, EPI_STORE>(args, cfg, max_tiles, max_n, stream);
+}
+
+}  // namespace moe

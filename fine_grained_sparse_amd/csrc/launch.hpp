@@ -1,0 +1,96 @@
+// Internal launchers of the MoE layer kernels (host side).  Not part of the
+// C ABI: api.cpp sequences these on the caller's stream.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1 };
+enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1 };
+// Tile shapes of the grouped GEMM: SMALL streams weights for a few rows
+// per expert (decode-sized batches), LARGE is the MFMA-bound prefill tile.
+enum TileCfg { TILE_SMALL = 0, TILE_LARGE = 1 };
+
+int tile_bm(TileCfg cfg);         // rows per M tile
+int tile_bn_out(TileCfg cfg, Epi epi);  // output columns per N tile
+
+// One K segment: C += A[:, 0:K] * B[:, 0:K]^T.  A rows have stride lda,
+// B (weights, [N, K] row-major) rows have stride ldb; Bu is the up
+// projection paired with B for the SwiGLU epilogue.  Strides in elements.
+struct GemmSeg {
+    const void* A;
+    const void* B;
+    const void* Bu;
+    int64_t lda, ldb;
+    int32_t K;
+    int32_t pad_;
+};
+
+// A family of tiles sharing operands: the routed experts (B offset by
+// expert * b_estride) or one dense matrix (the shared experts, a latent
+// map, the router).  Row p of the group reads A row rowmap ? rowmap[p] : p
+// and writes C row p.
+struct GemmGroup {
+    GemmSeg seg[3];
+    int32_t nseg;
+    int32_t N;
+    int64_t b_estride;
+    const int32_t* rowmap;
+    void* C;
+    int64_t ldc;
+};
+
+struct TileInfo {
+    int32_t group, expert, row0, rows;
+};
+
+struct GemmArgs {
+    GemmGroup g[2];
+    const TileInfo* tiles;   // device tile table (grouped) or NULL (dense)
+    const int32_t* ntiles;   // device count of valid tiles (grouped)
+    int32_t M;               // dense: rows of group 0
+    int32_t nsplit;          // split-K ways; output split s at C + s*split_stride
+    int64_t split_stride;
+    int32_t ntn;             // N tiles per M tile (set by launch_gemm)
+};
+
+// Launch C = epi(A * B^T) for element type `dt`; `out_f32` selects an fp32
+// output (the router logits) instead of the element type.  `max_tiles` is
+// the grid's M extent (upper bound of the device tile count when grouped).
+hipError_t launch_gemm(const GemmArgs& args, DType dt, bool out_f32, Epi epi,
+                       TileCfg cfg, int max_tiles, int max_n,
+                       hipStream_t stream);
+
+// W_r (fp32) -> three bf16 planes with hi + mid + lo == W_r exactly.
+hipError_t launch_split3(const float* W, int64_t n, uint16_t* hi,
+                         uint16_t* mid, uint16_t* lo, hipStream_t stream);
+
+// Sigmoid, biased top-K, renormalise and scale; z holds nsplit partial
+// logit planes of [T, ldz].  counts (nullable) gets +1 per selection.
+hipError_t launch_topk_gate(const float* z, int nsplit, int64_t split_stride,
+                            int ldz, const float* b, int T, int E, int K,
+                            float scale, int32_t* idx, float* w,
+                            int32_t* counts, hipStream_t stream);
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n,
+                           hipStream_t stream);
+
+// Histogram, scan and stable permutation; also the tile table for the
+// grouped GEMMs (routed tiles of bm rows, then shared tiles if
+// shared_rows > 0).
+hipError_t launch_dispatch(const int32_t* idx, int T, int E, int K, int bm,
+                           int shared_rows, uint64_t* masks,
+                           int32_t* chunk_base, int32_t* counts,
+                           int32_t* offsets, int32_t* sorted_token,
+                           int32_t* pos, TileInfo* tiles, int32_t* ntiles,
+                           hipStream_t stream);
+
+// out[t] = (Yshared ? Yshared[t] : 0) + sum_k w[t,k] * Y[pos[t,k]]
+hipError_t launch_combine(DType dt, const void* Y, int64_t ldy,
+                          const void* Yshared, const int32_t* pos,
+                          const float* w, int T, int K, int N, void* out,
+                          int64_t ldo, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,153 @@
+// Router kernels of the MoE layer (OpenModelAtlas "Kimi K2 · Router": the
+// four steps z = x W_r, s = sigmoid(z), top-K of s + b, renormalised and
+// scaled weights; the MoEGate excerpt computes the logits in fp32).
+//
+// The logits themselves come from the grouped GEMM (gemm.hip).  For bf16
+// activations the fp32 router weight is split exactly into three bf16
+// planes, W_r = hi + mid + lo (Henry, Tang & Heinecke 2019, "Leveraging the
+// bfloat16 Artificial Intelligence Datatype for Higher-Precision
+// Computations"): every bf16 x bf16 product is exact in the fp32 MFMA
+// accumulator, so three bf16 MFMA passes give an fp32-accumulated product
+// of the exact inputs at 16/3 times the fp32 MFMA rate.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+// hi = rne(w); mid = rne(w - hi); lo = rne(w - hi - mid).  Each difference
+// is exact in fp32 (its operands agree to within a factor of two), and
+// after two 8-bit captures at most 8 significant bits remain, so lo holds
+// the rest exactly: hi + mid + lo == w for finite normal w.
+__global__ __launch_bounds__(256) void k_split3(const float* __restrict__ W, int64_t n, bf16_t* __restrict__ hi,
+                                                bf16_t* __restrict__ mid, bf16_t* __restrict__ lo) {
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
+        const float w = W[i];
+        const bf16_t h = f32_to_bf16(w);
+        const float r1 = w - bf16_to_f32(h);
+        const bf16_t m = f32_to_bf16(r1);
+        const float r2 = r1 - bf16_to_f32(m);
+        hi[i] = h;
+        mid[i] = m;
+        lo[i] = f32_to_bf16(r2);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t* p, int32_t v, int64_t n) {
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) p[i] = v;
+}
+
+// (value, index) order of the selection: larger biased score first, the
+// lower expert index on equal scores.
+__device__ __forceinline__ bool better(float v, int e, float bv, int be) {
+    return v > bv || (v == bv && e < be);
+}
+
+// One wave per token.  Lane l holds experts l, l+64, l+128, ... (J of
+// them), so inside a lane the expert index rises with j.  K rounds of a
+// wave-wide (value, index) arg-max pick the set; slot order is then the
+// ascending expert id (rank of each pick among the picks).
+template <int J>
+__global__ __launch_bounds__(256) void k_topk_gate(const float* __restrict__ z, int nsplit, int64_t split_stride,
+                                                   int ldz, const float* __restrict__ b, int T, int E, int K,
+                                                   float scale, int32_t* __restrict__ idx, float* __restrict__ w,
+                                                   int32_t* __restrict__ counts) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    float v[J], s[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int e = j * 64 + lane;
+        if (e < E) {
+            float zz = 0.f;
+            for (int p = 0; p < nsplit; ++p) zz += z[p * split_stride + static_cast<int64_t>(t) * ldz + e];
+            s[j] = 1.0f / (1.0f + expf(-zz));  // step 2: per-expert sigmoid
+            v[j] = s[j] + b[e];                // step 3: the bias only chooses
+        } else {
+            s[j] = 0.f;
+            v[j] = -INFINITY;
+        }
+    }
+    uint32_t taken = 0;
+    int my_e = 0;
+    float my_s = 0.f, den = 0.f;
+    for (int k = 0; k < K; ++k) {
+        float bv = -INFINITY, bs = 0.f;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int e = j * 64 + lane;
+            if (!((taken >> j) & 1u) && e < E && better(v[j], e, bv, be)) {
+                bv = v[j];
+                be = e;
+                bs = s[j];
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oe = __shfl_xor(be, off);
+            const float os = __shfl_xor(bs, off);
+            if (better(ov, oe, bv, be)) {
+                bv = ov;
+                be = oe;
+                bs = os;
+            }
+        }
+        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+        if (lane == k) {
+            my_e = be;
+            my_s = bs;
+        }
+        den += bs;  // sum of the unbiased scores of the set, in pick order
+    }
+    // step 4: renormalise over the set (+1e-20 as in the MoEGate excerpt)
+    // and apply the routed scaling factor
+    den += 1e-20f;
+    int rank = 0;
+    for (int j = 0; j < K; ++j) rank += __shfl(my_e, j) < my_e ? 1 : 0;
+    if (lane < K) {
+        idx[static_cast<int64_t>(t) * K + rank] = my_e;
+        w[static_cast<int64_t>(t) * K + rank] = (my_s / den) * scale;
+        if (counts) atomicAdd(counts + my_e, 1);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_split3(const float* W, int64_t n, uint16_t* hi, uint16_t* mid, uint16_t* lo, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(k_split3, dim3(static_cast<unsigned>(blocks < 8192 ? blocks : 8192)), dim3(256), 0, stream, W,
+                       n, hi, mid, lo);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(k_fill_i32, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream, p,
+                       v, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_gate(const float* z, int nsplit, int64_t split_stride, int ldz, const float* b, int T, int E,
+                            int K, float scale, int32_t* idx, float* w, int32_t* counts, hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    const dim3 grid((T + 3) / 4), block(256);
+    const int J = (E + 63) / 64;
+    if (J <= 1)
+        hipLaunchKernelGGL(k_topk_gate<1>, grid, block, 0, stream, z, nsplit, split_stride, ldz, b, T, E, K, scale, idx, w, counts);
+    else if (J <= 2)
+        hipLaunchKernelGGL(k_topk_gate<2>, grid, block, 0, stream, z, nsplit, split_stride, ldz, b, T, E, K, scale, idx, w, counts);
+    else if (J <= 4)
+        hipLaunchKernelGGL(k_topk_gate<4>, grid, block, 0, stream, z, nsplit, split_stride, ldz, b, T, E, K, scale, idx, w, counts);
+    else if (J <= 8)
+        hipLaunchKernelGGL(k_topk_gate<8>, grid, block, 0, stream, z, nsplit, split_stride, ldz, b, T, E, K, scale, idx, w, counts);
+    else
+        hipLaunchKernelGGL(k_topk_gate<16>, grid, block, 0, stream, z, nsplit, split_stride, ldz, b, T, E, K, scale, idx, w, counts);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,150 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) Kimi-K2-style MoE layer forward.
+ *
+ * The layer (sources by page title and section):
+ *   Router -- OpenModelAtlas "Kimi K2 · Router", the four steps and the
+ *   MoEGate excerpt:  z = x W_r^T (fp32),  s = sigmoid(z),
+ *   S = top_K(s + b) (the bias only chooses),  w_i = scale * s_i /
+ *   (sum_{j in S} s_j + 1e-20) for i in S.
+ *   Experts -- llm-arch-kb "Kimi K2 MoE" sections 2 and 3: SwiGLU experts
+ *   f(v) = W_down (silu(W_gate v) * (W_up v)); the layer returns the
+ *   always-on shared expert(s) plus sum_{i in S} w_i f_i(x).
+ *   Latent form -- lilting.ch "Kimi K3's router picks 16 of 896 experts",
+ *   the K3 table and the Stable LatentMoE paragraph: routed experts act on
+ *   x_lat = W_lat_down x, their weighted sum is mapped back by W_lat_up,
+ *   the shared experts act on x.
+ * Readings where the pages leave a choice open:
+ *   - ties in s + b go to the lower expert index;
+ *   - the K slots of a token are written in ascending expert id;
+ *   - dispatch is dropless (every token reaches exactly K experts);
+ *   - several shared experts are stacked along their intermediate axis
+ *     (their outputs are summed, unweighted);
+ *   - intermediate activations (H = silu(g)*u, expert outputs, x_lat and
+ *     the latent weighted sum) are rounded to the activation dtype; all
+ *     products accumulate in fp32; the output is rounded once (RNE).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, row-major,
+ *     16-byte aligned.  The library never allocates, frees or retains memory;
+ *     scratch lives in the caller's workspace (see moe_workspace_size).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work on it and return without synchronising; results are
+ *     ready when the stream reaches them.  Concurrent calls need distinct
+ *     workspaces.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     an error nothing is enqueued and no output is touched.  A failed
+ *     kernel launch returns MOE_ERR_HIP; faults inside kernels surface at
+ *     the caller's next synchronisation.
+ *   - Limits: 1 <= K <= min(E, 16); E <= 1024; d, F, F_shared and d_latent
+ *     are positive multiples of 64; 0 <= n_shared <= 8; T*K < 2^31.
+ *   - T == 0 is a no-op: the data pointers may then be NULL (empty tensors);
+ *     non-NULL expert_counts / expert_offsets are zero-filled.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    MOE_ERR_SHAPE = 2,       /* a size is out of range                        */
+    MOE_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned              */
+    MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_size()   */
+    MOE_ERR_UNSUPPORTED = 5, /* a dtype combination the library does not run  */
+    MOE_ERR_HIP = 6          /* a HIP launch failed                           */
+} moe_status;
+
+typedef struct {
+    int32_t T;         /* tokens: batch x positions flattened                 */
+    int32_t d;         /* model dimension (7168 for K2 and K3)                */
+    int32_t E;         /* routed experts (384 for K2, 896 for K3)             */
+    int32_t K;         /* experts per token (8 for K2, 16 for K3)             */
+    int32_t F;         /* routed-expert intermediate size                     */
+    int32_t n_shared;  /* always-on shared experts (1 for K2, 2 for K3)       */
+    int32_t F_shared;  /* intermediate size of EACH shared expert             */
+    int32_t d_latent;  /* 0 = experts act on x; else the latent width (3584)  */
+    float scale;       /* routed scaling factor (2.827 for K2)                */
+    int32_t act_dtype; /* moe_dtype of x, out and the intermediates           */
+    int32_t w_dtype;   /* moe_dtype of expert, shared and latent weights;     */
+                       /* must equal act_dtype (W_r and b are always fp32)    */
+} moe_layer_desc;
+
+/* Expert weights, nn.Linear layout [out, in]; d_in = d_latent ? d_latent : d.
+ *   W_gate, W_up [E, F, d_in];  W_down [E, d_in, F]
+ *   Ws_gate, Ws_up [n_shared*F_shared, d];  Ws_down [d, n_shared*F_shared]
+ *     (shared expert s owns rows/columns [s*F_shared, (s+1)*F_shared))
+ *   W_lat_down [d_latent, d];  W_lat_up [d, d_latent]  (NULL if d_latent == 0)
+ * Shared pointers may be NULL when n_shared == 0.                            */
+typedef struct {
+    const void *W_gate, *W_up, *W_down;
+    const void *Ws_gate, *Ws_up, *Ws_down;
+    const void *W_lat_down, *W_lat_up;
+} moe_expert_weights;
+
+/* Bytes of device workspace moe_router (for_forward = 0) or moe_forward
+ * (for_forward != 0) needs for this descriptor; 0 if the descriptor is
+ * invalid.  Host-only; touches no device.                                    */
+size_t moe_workspace_size(const moe_layer_desc *desc, int for_forward);
+
+/* Router [router card, four steps and MoEGate excerpt].
+ *   x [T, d] (act_dtype), W_r [E, d] fp32, b [E] fp32
+ *   -> topk_idx [T, K] int32 (ascending expert id within each token),
+ *      topk_w [T, K] fp32, expert_counts [E] int32 (nullable: tokens per
+ *      expert).                                                              */
+moe_status moe_router(const moe_layer_desc *desc, const void *x,
+                      const float *W_r, const float *b, int32_t *topk_idx,
+                      float *topk_w, int32_t *expert_counts, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* Stage boundaries of moe_forward, for timing: when `stage_events` is not
+ * NULL it points to MOE_NUM_STAGE_EVENTS hipEvent_t handles (created by the
+ * caller; a NULL entry is skipped) that are recorded on `stream`:
+ *   [MOE_EV_START]    before the first kernel
+ *   [MOE_EV_ROUTER]   after the router (logits, top-K gate)
+ *   [MOE_EV_DISPATCH] after histogram, scan and permutation
+ *   [MOE_EV_LATENT]   after x_lat = x W_lat_down^T (same point as the
+ *                     previous event in the K2 form)
+ *   [MOE_EV_UP]       after the gate/up projection with SwiGLU (one kernel)
+ *   [MOE_EV_DOWN]     after the down projection (one kernel)
+ *   [MOE_EV_END]      after the combine (and latent up-projection)          */
+enum {
+    MOE_EV_START = 0,
+    MOE_EV_ROUTER = 1,
+    MOE_EV_DISPATCH = 2,
+    MOE_EV_LATENT = 3,
+    MOE_EV_UP = 4,
+    MOE_EV_DOWN = 5,
+    MOE_EV_END = 6,
+    MOE_NUM_STAGE_EVENTS = 7
+};
+
+/* Whole layer [router card; llm-arch-kb K2 MoE sections 2-3; K3 essay].
+ *   x [T, d], W_r [E, d], b [E], weights as above -> out [T, d] (act_dtype).
+ * Optional outputs (each nullable), for inspection and parity checks:
+ *   topk_idx [T, K], topk_w [T, K], expert_counts [E],
+ *   expert_offsets [E + 1] (exclusive scan of the counts),
+ *   sorted_token [T*K]: for e ascending, the tokens routed to e, ascending.  */
+moe_status moe_forward(const moe_layer_desc *desc, const void *x,
+                       const float *W_r, const float *b,
+                       const moe_expert_weights *weights, void *out,
+                       int32_t *topk_idx, float *topk_w,
+                       int32_t *expert_counts, int32_t *expert_offsets,
+                       int32_t *sorted_token, void *workspace,
+                       size_t workspace_bytes, void *stream,
+                       void *const *stage_events);
+
+/* Static text for a status code.                                            */
+const char *moe_status_str(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

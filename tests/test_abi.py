@@ -1,0 +1,133 @@
+"""C-ABI contract checks that need no GPU.
+
+The library loads, exports every function include/moe.h declares, sizes
+workspaces on the host, and rejects bad arguments with the documented status
+codes before anything is enqueued.  The pointers handed over here are fake
+but aligned addresses; every call is built to fail validation, so no kernel
+is ever launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fine_grained_sparse_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, NULL, SHAPE, ALIGN, WS, UNSUP = 0, 1, 2, 3, 4, 5
+FAKE = 1 << 20          # 16-byte aligned, never dereferenced
+FAKE_ODD = FAKE + 8     # 8-byte aligned only
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(["moe_forward", "moe_router", "moe_status_str",
+                                  "moe_workspace_size"])
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    assert set(_declared()) <= exported
+    # nothing else of the library's own leaks as a C symbol
+    assert {s for s in exported if s.startswith("moe_")} == set(_declared())
+
+
+def test_status_strings():
+    L = moe.lib()
+    for code in range(7):
+        assert L.moe_status_str(code)
+    assert L.moe_status_str(99) == b"unknown status"
+
+
+def _k2(**kw):
+    base = dict(T=256, d=7168, E=384, K=8, F=2048, n_shared=1, F_shared=2048,
+                d_latent=0, scale=2.827, act_dtype=moe.MOE_BF16)
+    base.update(kw)
+    return moe.desc(**base)
+
+
+def test_workspace_size_valid_and_invalid():
+    assert moe.workspace_size(_k2(), True) > moe.workspace_size(_k2(), False) > 0
+    assert moe.workspace_size(_k2(T=16384), True) > moe.workspace_size(_k2(T=256), True)
+    assert moe.workspace_size(_k2(T=0), True) > 0
+    for bad in (dict(K=0), dict(K=17), dict(E=1025), dict(K=9, E=8), dict(d=100),
+                dict(F=100), dict(F_shared=65), dict(d_latent=100), dict(n_shared=-1),
+                dict(T=-1), dict(n_shared=9)):
+        assert moe.workspace_size(_k2(**bad), True) == 0, bad
+    # router-only sizing ignores the expert fields
+    assert moe.workspace_size(_k2(F=100), False) > 0
+    assert moe.workspace_size(_k2(act_dtype=7), False) == 0
+
+
+def _router(D, x=FAKE, W_r=FAKE, b=FAKE, idx=FAKE, w=FAKE, counts=None, ws=FAKE, nbytes=None):
+    if nbytes is None:
+        nbytes = moe.workspace_size(D, False)
+    vp = ctypes.c_void_p
+    return moe.lib().moe_router(ctypes.byref(D), vp(x), vp(W_r), vp(b), vp(idx), vp(w),
+                                vp(counts), vp(ws), nbytes, None)
+
+
+def test_router_rejects_bad_arguments():
+    D = _k2()
+    assert _router(D, x=None) == NULL
+    assert _router(D, idx=None) == NULL
+    assert _router(D, ws=None) == NULL
+    assert _router(D, x=FAKE_ODD) == ALIGN
+    assert _router(D, counts=FAKE_ODD) == ALIGN
+    assert _router(D, nbytes=moe.workspace_size(D, False) - 1) == WS
+    assert _router(_k2(K=17)) == SHAPE
+    assert _router(_k2(E=2000)) == SHAPE
+    assert _router(_k2(d=7000)) == SHAPE
+    assert _router(_k2(act_dtype=3)) == UNSUP
+    assert moe.lib().moe_router(None, None, None, None, None, None, None, None, 0, None) == NULL
+
+
+def _forward(D, W=None, nbytes=None, **ptr):
+    p = dict(x=FAKE, W_r=FAKE, b=FAKE, out=FAKE, ws=FAKE)
+    p.update(ptr)
+    if W is None:
+        W = moe.ExpertWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    if nbytes is None:
+        nbytes = moe.workspace_size(D, True)
+    vp = ctypes.c_void_p
+    return moe.lib().moe_forward(ctypes.byref(D), vp(p["x"]), vp(p["W_r"]), vp(p["b"]),
+                                 ctypes.byref(W), vp(p["out"]), vp(p.get("idx")),
+                                 vp(p.get("w")), vp(p.get("counts")), vp(p.get("offsets")),
+                                 vp(p.get("sorted")), vp(p["ws"]), nbytes, None, None)
+
+
+def test_forward_rejects_bad_arguments():
+    D = _k2()
+    assert _forward(D, out=None) == NULL
+    assert _forward(D, W=moe.ExpertWeights(FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None)) == NULL
+    # shared weights required when n_shared > 0, latent maps when d_latent > 0
+    assert _forward(D, W=moe.ExpertWeights(FAKE, FAKE, FAKE, None, None, None, None, None)) == NULL
+    assert _forward(_k2(d_latent=3584)) == NULL
+    assert _forward(D, W=moe.ExpertWeights(FAKE, FAKE, FAKE_ODD, FAKE, FAKE, FAKE, None, None)) == ALIGN
+    assert _forward(D, sorted=FAKE_ODD) == ALIGN
+    assert _forward(D, nbytes=moe.workspace_size(D, True) - 256) == WS
+    assert _forward(_k2(w_dtype=moe.MOE_F32)) == UNSUP
+    assert _forward(_k2(F=2000)) == SHAPE
+    assert _forward(_k2(n_shared=1, F_shared=0)) == SHAPE
+
+
+def test_zero_tokens_accepts_null_data_pointers():
+    # nothing to read or write: no kernel is launched without count outputs
+    D = _k2(T=0)
+    assert _router(D, x=None, W_r=None, b=None, idx=None, w=None, ws=None) == OK
+    assert _forward(D, x=None, W_r=None, b=None, out=None, ws=None) == OK
+    assert _forward(D, x=None, out=None, counts=FAKE_ODD) == ALIGN

@@ -1,0 +1,205 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every case prints its name before it touches the GPU.  Tolerances are
+documented in tests/parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_sparse_amd as moe
+import oracle
+from moe_inputs import Workload, get_workload, make_layer_inputs, make_router_inputs
+from parity import (TIE, check_dispatch, effective_routing, expert_weights, host, log,
+                    rel_l2, weights_to_device)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def out_tol(wl):
+    return 1e-4 if wl.act_dtype == "f32" else 2e-2
+
+
+def _custom(**kw):
+    base = dict(name="custom", T=64, d=256, E=16, K=4, F=128, n_shared=1, F_shared=128,
+                d_latent=0, scale=2.827, act_dtype="bf16", w_dtype="bf16", bias_range=0.02,
+                zipf_skew=False, router_only=False)
+    base.update(kw)
+    return Workload(**base)
+
+
+def _run_forward(wl, dev, **kw):
+    out, r = moe.forward(dev["x"], dev["W_r"], dev["b"], expert_weights(dev), wl.K, wl.scale,
+                         n_shared=wl.n_shared, return_routing=True, **kw)
+    torch.cuda.synchronize()
+    return out, r
+
+
+def _full_parity(wl, inp, seed_note=""):
+    """Run the layer on the GPU and compare every token with the oracle."""
+    log(f"[gpu] forward {wl.name} T={wl.T} d={wl.d} E={wl.E} K={wl.K} {seed_note}")
+    dev = weights_to_device(inp, DEV)
+    out, r = _run_forward(wl, dev)
+    ref = oracle.router(inp["x"], inp["W_r"], inp["b"], wl.K, wl.scale, want_scores=True)
+    idx_eff, w_eff, st = effective_routing(ref, r["idx"].cpu().numpy(), r["w"].cpu().numpy(),
+                                           inp["b"].numpy(), wl.K, wl.scale)
+    check_dispatch(r, wl.E)
+    out_ref = oracle.forward_given_routing(oracle.layer_from_inputs(wl, inp), inp["x"],
+                                           idx_eff, w_eff)
+    err = rel_l2(out.float().cpu().numpy(), out_ref)
+    log(f"  rel_l2={err:.3e} near_tie={st['near_tie']} differ={st['differ']} "
+        f"w_max_rel={st['w_max_rel']:.2e}")
+    assert err <= out_tol(wl), f"rel L2 {err:.3e} > {out_tol(wl)}"
+    return out, r, err
+
+
+# ---------------------------------------------------------------- router
+@pytest.mark.parametrize("name,T", [("tiny_fp32_t128", None), ("mid_bf16_t300", None),
+                                    ("k2_router_t4096", None), ("k3_latent_t4096", 1024)])
+def test_router_parity(name, T):
+    wl = get_workload(name)
+    log(f"[gpu] router {name} T={T or wl.T}")
+    inp = make_router_inputs(wl, "cpu", seed=42, T=T)
+    dev = weights_to_device(inp, DEV)
+    idx, w, counts = moe.router(dev["x"], dev["W_r"], dev["b"], wl.K, wl.scale)
+    torch.cuda.synchronize()
+    ref = oracle.router(inp["x"], inp["W_r"], inp["b"], wl.K, wl.scale, want_scores=True)
+    gi = idx.cpu().numpy()
+    _, _, st = effective_routing(ref, gi, w.cpu().numpy(), inp["b"].numpy(), wl.K, wl.scale)
+    np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(gi.ravel(), minlength=wl.E))
+    np.testing.assert_allclose(w.double().sum(1).cpu().numpy(), float(np.float32(wl.scale)), rtol=1e-6)
+    log(f"  near_tie={st['near_tie']} differ={st['differ']} w_max_rel={st['w_max_rel']:.2e}")
+
+
+def test_router_1024_experts_top16():
+    wl = _custom(E=1024, K=16, d=320 - 64, T=70)
+    log("[gpu] router E=1024 K=16")
+    inp = make_router_inputs(wl, "cpu", seed=3)
+    dev = weights_to_device(inp, DEV)
+    idx, w, counts = moe.router(dev["x"], dev["W_r"], dev["b"], wl.K, wl.scale)
+    torch.cuda.synchronize()
+    ref = oracle.router(inp["x"], inp["W_r"], inp["b"], wl.K, wl.scale, want_scores=True)
+    effective_routing(ref, idx.cpu().numpy(), w.cpu().numpy(), inp["b"].numpy(), wl.K, wl.scale)
+
+
+def test_router_all_tied_and_K1():
+    log("[gpu] router ties / K=1")
+    T, d, E = 40, 128, 24
+    x = torch.randn(T, d).to(torch.bfloat16).to(DEV)
+    idx, w, _ = moe.router(x, torch.zeros(E, d, device=DEV), torch.zeros(E, device=DEV), 5)
+    assert (idx.cpu() == torch.arange(5, dtype=torch.int32)).all()
+    assert torch.allclose(w.cpu(), torch.full((T, 5), float(np.float32(2.827)) / 5), rtol=1e-6)
+    inp = make_router_inputs(_custom(E=E, d=d, T=T), "cpu", seed=9)
+    dev = weights_to_device(inp, DEV)
+    idx1, w1, _ = moe.router(dev["x"], dev["W_r"], dev["b"], 1)
+    assert torch.all(w1.cpu() == torch.tensor(np.float32(2.827)))
+
+
+# ---------------------------------------------------------------- whole layer, every token
+@pytest.mark.parametrize("name", ["tiny_fp32_t128", "mid_fp32_t77", "mid_bf16_t300",
+                                  "mid_latent_t200"])
+def test_forward_parity_every_token(name):
+    wl = get_workload(name)
+    _full_parity(wl, make_layer_inputs(wl, "cpu", seed=42))
+
+
+@pytest.mark.parametrize("case", ["one_token", "K_equals_E", "no_shared", "skewed_few_experts",
+                                  "latent_no_shared", "large_tiles"])
+def test_forward_edge_cases(case):
+    if case == "one_token":
+        wl = _custom(T=1)
+    elif case == "K_equals_E":
+        wl = _custom(E=16, K=16, T=33)
+    elif case == "no_shared":
+        wl = _custom(n_shared=0, F_shared=0, T=130)
+    elif case == "skewed_few_experts":
+        wl = _custom(E=40, K=3, T=200)
+    elif case == "latent_no_shared":
+        wl = _custom(d_latent=128, n_shared=0, F_shared=0, T=90, scale=1.0)
+    else:  # enough rows per expert to take the 128-row tiles, ragged tails
+        wl = _custom(E=6, K=2, T=700, d=384, F=192, n_shared=2, F_shared=64)
+    inp = make_layer_inputs(wl, "cpu", seed=5)
+    if case == "skewed_few_experts":
+        inp["b"][:3] = 10.0     # every token picks experts 0, 1, 2; the rest get none
+    _, r, _ = _full_parity(wl, inp, case)
+    if case == "skewed_few_experts":
+        c = r["counts"].cpu().numpy()
+        assert c[:3].tolist() == [200, 200, 200] and c[3:].sum() == 0
+
+
+def test_forward_zero_tokens():
+    wl = _custom(T=0)
+    log("[gpu] forward T=0")
+    inp = make_layer_inputs(wl, "cpu", seed=1)
+    dev = weights_to_device(inp, DEV)
+    out, r = _run_forward(wl, dev)
+    assert out.shape == (0, wl.d)
+    assert r["counts"].cpu().sum() == 0 and r["offsets"].cpu().sum() == 0
+
+
+def test_forward_deterministic_and_independent_of_workspace_contents():
+    wl = get_workload("mid_bf16_t300")
+    log("[gpu] determinism mid_bf16_t300")
+    dev = weights_to_device(make_layer_inputs(wl, "cpu", seed=42), DEV)
+    ws = moe.Workspace()
+    D = moe.desc(T=wl.T, d=wl.d, E=wl.E, K=wl.K, F=wl.F, n_shared=wl.n_shared,
+                 F_shared=wl.F_shared, scale=wl.scale)
+    buf = ws.get(torch.device(DEV), moe.workspace_size(D, True))
+    buf.fill_(0)
+    out1, r1 = _run_forward(wl, dev, workspace=ws)
+    buf.fill_(0xFF)             # NaN patterns everywhere in the scratch
+    out2, r2 = _run_forward(wl, dev, workspace=ws)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    for k in r1:
+        assert torch.equal(r1[k], r2[k]), k
+
+
+# ---------------------------------------------------------------- full sizes, sampled tokens
+def _sampled_tokens(T, ref, counts, idx_eff, n_random=6):
+    rng = np.random.default_rng(0)
+    toks = set(rng.choice(T, size=min(n_random, T), replace=False).tolist())
+    toks.update(np.nonzero(ref["gap"] < TIE)[0][:3].tolist())
+    nz = np.nonzero(counts > 0)[0]
+    hot, cold = nz[np.argmax(counts[nz])], nz[np.argmin(counts[nz])]
+    for e in (hot, cold):
+        toks.add(int(np.nonzero((idx_eff == e).any(1))[0][0]))
+    toks.add(T - 1)
+    return sorted(toks)
+
+
+@pytest.mark.parametrize("name", ["k2_decode_t256", "k2_prefill_t16384", "k3_latent_t4096"])
+def test_forward_parity_full_size_sampled(name):
+    wl = get_workload(name)
+    log(f"[gpu] full-size {name}: generating inputs on the GPU")
+    inp = make_layer_inputs(wl, DEV, seed=42)
+    log(f"[gpu] full-size {name}: moe_forward")
+    out, r = _run_forward(wl, inp)
+    x_h, Wr_h, b_h = host(inp["x"]), host(inp["W_r"]), host(inp["b"])
+    log(f"[cpu] oracle router over all {wl.T} tokens")
+    ref = oracle.router(x_h, Wr_h, b_h, wl.K, wl.scale, want_scores=True)
+    idx_eff, w_eff, st = effective_routing(ref, r["idx"].cpu().numpy(), r["w"].cpu().numpy(),
+                                           b_h.numpy(), wl.K, wl.scale)
+    check_dispatch(r, wl.E)
+    counts = r["counts"].cpu().numpy()
+    toks = _sampled_tokens(wl.T, ref, counts, idx_eff)
+    experts = set(idx_eff[toks].ravel().tolist())
+    log(f"[cpu] oracle experts for {len(toks)} tokens ({len(experts)} experts)")
+    per = {k: [host(inp[k][e]) if e in experts else None for e in range(wl.E)]
+           for k in ("W_gate", "W_up", "W_down")}
+    lay = oracle.Layer(d=wl.d, E=wl.E, K=wl.K, F=wl.F, scale=wl.scale, W_r=Wr_h, b=b_h,
+                       W_gate=per["W_gate"], W_up=per["W_up"], W_down=per["W_down"],
+                       n_shared=wl.n_shared, F_shared=wl.F_shared,
+                       Ws_gate=host(inp["Ws_gate"]), Ws_up=host(inp["Ws_up"]),
+                       Ws_down=host(inp["Ws_down"]), d_latent=wl.d_latent,
+                       W_lat_down=host(inp["W_lat_down"]) if wl.d_latent else None,
+                       W_lat_up=host(inp["W_lat_up"]) if wl.d_latent else None)
+    out_ref = oracle.forward_given_routing(lay, x_h[toks], idx_eff[toks], w_eff[toks])
+    got = out[toks].float().cpu().numpy()
+    err = rel_l2(got, out_ref)
+    per_tok = [rel_l2(got[i], out_ref[i]) for i in range(len(toks))]
+    log(f"  rel_l2={err:.3e} max_token={max(per_tok):.3e} near_tie={st['near_tie']} "
+        f"differ={st['differ']} hist min/mean/max={counts.min()}/{counts.mean():.1f}/{counts.max()}")
+    del inp, out, r
+    torch.cuda.empty_cache()
+    assert err <= 2e-2
