@@ -177,6 +177,9 @@ def main():
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="target seconds of oracle time (0 skips the CPU baseline)")
     ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
+                    help="also run a plain streaming copy (out = in + 0, fp32) of this many GiB "
+                         "three times, to scale HBM byte counters (0 = off)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -187,6 +190,16 @@ def main():
     import fine_grained_sparse_amd as moe
     from moe_inputs import get_workload, make_expert_weights
 
+    if args.calibrate_copy_gib > 0:
+        n = int(args.calibrate_copy_gib * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 0.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x (read {n * 4} B, write {n * 4} B)")
+        del src, dst
+        torch.cuda.empty_cache()
     wl = get_workload(args.workload)
     if wl.router_only:
         sys.exit("choose a whole-layer workload")
