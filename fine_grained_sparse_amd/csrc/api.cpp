@@ -84,7 +84,8 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
 
     // Router: small row tiles for small batches; split K until about a
     // thousand workgroups are in flight, keeping at least 8 K steps each.
-    p.rcfg = p.T <= 1024 ? TILE_SMALL : TILE_LARGE;
+    // (fp32 activations only serve small parity workloads: small tiles)
+    p.rcfg = (p.T <= 1024 || p.dt == DT_F32) ? TILE_SMALL : TILE_LARGE;
     const int64_t rbm = tile_bm(p.rcfg), rbn = tile_bn_out(p.rcfg, EPI_STORE);
     p.rtiles = static_cast<int>(cdiv(p.T, rbm));
     const int64_t wgs = std::max<int64_t>(1, p.rtiles * cdiv(p.E, rbn));
@@ -95,9 +96,9 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
     p.ldz = static_cast<int>(up(p.E, 8));
 
     // Experts: big M tiles once experts average 64 rows or more.
-    p.ecfg = (p.A >= 64ll * p.E) ? TILE_LARGE : TILE_SMALL;
+    p.ecfg = (p.A >= 64ll * p.E && p.dt == DT_BF16) ? TILE_LARGE : TILE_SMALL;
     p.bm = tile_bm(p.ecfg);
-    p.dcfg = p.T >= 1024 ? TILE_LARGE : TILE_SMALL;
+    p.dcfg = (p.T >= 1024 && p.dt == DT_BF16) ? TILE_LARGE : TILE_SMALL;
     p.nch = static_cast<int>(cdiv(p.T, 64));
     p.max_tiles = static_cast<int>(cdiv(p.A, p.bm) + p.E + (p.ns ? cdiv(p.T, p.bm) : 0));
 

@@ -89,17 +89,24 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(const uint64_t* __restri
             ti.expert = e;
             ti.row0 = off + j * bm;
             ti.rows = min(bm, cnt - j * bm);
+            ti.first = toff;
+            ti.count = nt;
+            ti.pad0_ = ti.pad1_ = 0;
             tiles[toff + j] = ti;
         }
     }
     if (e == 0) offsets[E] = total;
     const int nsh = shared_rows > 0 ? (shared_rows + bm - 1) / bm : 0;
+    constexpr int kSharedRun = 8;  // shared-row tiles walked together
     for (int j = threadIdx.x; j < nsh; j += blockDim.x) {
         TileInfo ti;
         ti.group = 1;
         ti.expert = 0;
         ti.row0 = j * bm;
         ti.rows = min(bm, shared_rows - j * bm);
+        ti.first = ttotal + (j / kSharedRun) * kSharedRun;
+        ti.count = min(kSharedRun, nsh - (j / kSharedRun) * kSharedRun);
+        ti.pad0_ = ti.pad1_ = 0;
         tiles[ttotal + j] = ti;
     }
     if (threadIdx.x == 0) *ntiles = ttotal + nsh;

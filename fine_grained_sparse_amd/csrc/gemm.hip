@@ -22,11 +22,8 @@
 
 namespace moe {
 
-int tile_bm(TileCfg cfg) { return cfg == TILE_SMALL ? 16 : 128; }
-int tile_bn_out(TileCfg cfg, Epi epi) {
-    int bn = cfg == TILE_SMALL ? 256 : 128;
-    return epi == EPI_SWIGLU ? bn / 2 : bn;
-}
+int tile_bm(TileCfg cfg);
+int tile_bn_out(TileCfg cfg, Epi epi);
 
 namespace {
 
@@ -255,6 +252,288 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill-sized tiles: 128 x 256 (B rows) per workgroup, 64 x 128 per wave,
+// so each wave issues 32 MFMAs per 64-byte K slab.
+//
+// Operands go from global memory straight into LDS with gfx950's
+// global_load_lds_dwordx4: a wave's instruction moves 64 x 16 B into one
+// contiguous 1 KiB LDS block (lane i at byte 16 i; the LDS address comes
+// from M0).  Three LDS stages: while stage k is read by the MFMA loop, the
+// loads of stages k+1 and k+2 are in flight, so about two compute steps of
+// memory latency are hidden with one workgroup (4 waves, one per SIMD) per
+// CU and no registers holding tiles in flight.
+// A stage holds 128 bytes (64 bf16) of every tile row; a 1 KiB block holds
+// 8 rows.  The 16-byte chunks of row r sit XOR-swizzled (logical chunk c at
+// position c ^ (r & 7)) so the fragment reads of 16 consecutive rows do not
+// collide in LDS banks; lane i of a block therefore loads logical chunk
+// (i & 7) ^ (i >> 3) of row i >> 3.
+// The DMA is issued from inline assembly: the compiler then does not treat
+// it as a pending LDS write (which would make it wait for every load in
+// flight before each LDS read).  Completion is ordered explicitly: each
+// wave waits until only the newer stage's loads are outstanding, then the
+// workgroup barrier publishes every wave's blocks.
+//
+// Workgroup -> tile: the device tile count gives the number of active
+// (M tile, N tile) pairs; XCD x (= block id mod 8) takes the x-th
+// contiguous share of them in the logical order below, so the M tiles of
+// one expert that share each weight slice run side by side on one XCD and
+// fetch the slice from HBM once.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(src) : "memory", "m0");
+}
+
+template <typename TC, int BM, int BN, int WM, int WN, int NST, int EPI>
+__global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const GemmArgs a) {
+    using T = bf16_t;
+    constexpr int ES = 2;
+    constexpr int ROWB = kStageRowBytes;  // 128 bytes of a row per stage
+    constexpr int BKE = ROWB / ES;
+    constexpr int NW = WM * WN;               // waves per workgroup
+    constexpr int NT = 64 * NW;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int MB = TM / 16, NB = TN / 16;
+    constexpr int BNO = EPI == EPI_SWIGLU ? BN / 2 : BN;
+    constexpr int LPW = (BM + BN) / (8 * NW);  // 1 KiB blocks per wave per stage
+    constexpr int STAGE = (BM + BN) * ROWB;
+    // epilogue passes: the fp32 tile goes through LDS in NP column slices
+    constexpr int NP = (BM * (BNO + 4) * 4 <= NST * STAGE) ? 1
+                       : (BM * (BNO / 2 + 4) * 4 <= NST * STAGE) ? 2
+                       : (BM * (BNO / 4 + 4) * 4 <= NST * STAGE) ? 4 : 8;
+    constexpr int WP = BNO / NP;
+    constexpr int EP_STRIDE = WP + 4;
+    constexpr int LDS_BYTES = (NST * STAGE > BM * EP_STRIDE * 4) ? NST * STAGE : BM * EP_STRIDE * 4;
+    static_assert((NW == 4 || NW == 8) && (BM + BN) % (8 * NW) == 0 && BM % 8 == 0, "tile shape");
+    static_assert(EPI != EPI_SWIGLU || (NB % 2 == 0 && (TN / 2) % 8 == 0), "gate/up pairs per wave");
+    static_assert(NST >= 2 && LPW * (NST - 2) < 64, "pipeline depth");
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid / WN, wn = wid % WN;
+
+    const int total = a.tiles ? (*a.ntiles) * a.ntn : static_cast<int>(gridDim.x);
+    const int per = (total + 7) >> 3;
+    const int slot = static_cast<int>(blockIdx.x) >> 3;
+    const int lin = (static_cast<int>(blockIdx.x) & 7) * per + slot;
+    if (slot >= per || lin >= total) return;
+    // Logical order: runs of tiles that share weights (one expert, or up to
+    // 8 dense row tiles), inside a run N tile by N tile with the M tile
+    // fastest.  A run of `cnt` tiles starting at tile `first` occupies the
+    // logical slots [first*ntn, (first+cnt)*ntn), so lin / ntn names a tile
+    // of the run that owns slot lin.
+    int first, cnt;
+    if (a.tiles) {
+        const TileInfo t0 = a.tiles[lin / a.ntn];
+        first = t0.first;
+        cnt = t0.count;
+    } else {
+        const int mtiles = total / a.ntn;
+        first = (lin / a.ntn) & ~7;
+        cnt = min(8, mtiles - first);
+    }
+    const int u = lin - first * a.ntn;
+    const int nt_n = u / cnt;
+    const int mt = first + u % cnt;
+    int gi = 0, expert = 0, row0, rows;
+    if (a.tiles) {
+        const TileInfo ti = a.tiles[mt];
+        gi = ti.group;
+        expert = ti.expert;
+        row0 = ti.row0;
+        rows = ti.rows;
+    } else {
+        row0 = mt * BM;
+        rows = min(BM, a.M - row0);
+        if (rows <= 0) return;
+    }
+    const GemmGroup& G = gi ? a.g[1] : a.g[0];
+    const int N = G.N;
+    const int n0 = nt_n * BNO;
+    if (n0 >= N) return;
+
+    int nk = 0;
+    for (int s = 0; s < G.nseg; ++s) nk += seg_of(G, s).K / BKE;
+    const int chunk = (nk + a.nsplit - 1) / a.nsplit;
+    const int kt0 = min(nk, static_cast<int>(blockIdx.z) * chunk);
+    const int kt1 = min(nk, kt0 + chunk);
+    const int nkt = kt1 - kt0;
+
+    // ---- this lane's source row in each block the wave loads.  Block
+    // q = wid + NW j covers tile rows 8q .. 8q+7 (A rows first, then B rows).
+    const int lrow = lane >> 3;
+    const int lchunk16 = ((lane & 7) ^ lrow) * 16;
+    int srow[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+        const int r = (wid + NW * j) * 8 + lrow;
+        if (r < BM) {
+            const int p = row0 + (r < rows ? r : 0);
+            srow[j] = G.rowmap ? G.rowmap[p] : p;
+        } else {
+            const int qb = r - BM;
+            int n;
+            if (EPI == EPI_SWIGLU) {
+                const int blk = qb / TN, rq = qb % TN, half = TN / 2;
+                n = n0 + blk * half + (rq % half);
+            } else {
+                n = n0 + qb;
+            }
+            srow[j] = n < N ? n : N - 1;
+        }
+    }
+    // whether block q reads A, the gate or the up matrix depends on q alone
+    auto blk_is_a = [&](int j) { return (wid + NW * j) * 8 < BM; };
+    auto blk_is_up = [&](int j) {
+        return EPI == EPI_SWIGLU && ((((wid + NW * j) * 8 - BM) % TN) >= TN / 2);
+    };
+    int cs = 0, ck = kt0;
+    while (cs + 1 < G.nseg && ck >= seg_of(G, cs).K / BKE) {
+        ck -= seg_of(G, cs).K / BKE;
+        ++cs;
+    }
+    const char *pA, *pB, *pBu;
+    int64_t lda, ldb;
+    auto set_seg = [&](int s) {
+        const GemmSeg& S = seg_of(G, s);
+        const int64_t eoff = s == 0 ? static_cast<int64_t>(expert) * G.b_estride * ES : 0;
+        pA = static_cast<const char*>(S.A) + lchunk16;
+        pB = static_cast<const char*>(S.B) + eoff + lchunk16;
+        pBu = static_cast<const char*>(S.Bu) + eoff + lchunk16;
+        lda = S.lda * ES;
+        ldb = S.ldb * ES;
+    };
+    set_seg(cs);
+    const uint32_t lds_base = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(lds)));
+    auto issue = [&](int buf) {
+        const int64_t off = static_cast<int64_t>(ck) * ROWB;
+        const uint32_t dst = lds_base + buf * STAGE + wid * 1024;
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const bool isa = blk_is_a(j);
+            const char* base = isa ? pA : (blk_is_up(j) ? pBu : pB);
+            lds_dma16(base + static_cast<int64_t>(srow[j]) * (isa ? lda : ldb) + off, dst + j * NW * 1024);
+        }
+        ++ck;
+        if (cs + 1 < G.nseg && ck == seg_of(G, cs).K / BKE) {
+            ++cs;
+            ck = 0;
+            set_seg(cs);
+        }
+    };
+
+    f32x4 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // fragment offsets inside a 16-row group for the two 64-byte slabs:
+    // row (lane & 15), logical chunk 4*slab + (lane >> 4), swizzled by row & 7
+    const int frow = lane & 15;
+    const int fo0 = frow * ROWB + ((((lane >> 4) + 0) ^ (lane & 7)) << 4);
+    const int fo1 = frow * ROWB + ((((lane >> 4) + 4) ^ (lane & 7)) << 4);
+
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+        if (s < nkt) issue(s);
+    for (int it = 0; it < nkt; ++it) {
+        if (it + NST - 2 < nkt)
+            wait_vmcnt<LPW * (NST - 2)>();  // the NST-2 newer stages may still be in flight
+        else
+            wait_vmcnt<0>();
+        __syncthreads();  // every wave's blocks of stage `it` have landed
+        if (it + NST - 1 < nkt) issue((it + NST - 1) % NST);  // reuses the stage read at it-1
+        const char* As = lds + (it % NST) * STAGE;
+        const char* Bs = As + BM * ROWB;
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const int fo = sl ? fo1 : fo0;
+            uint4 fa[MB], fb[NB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                fa[i] = *reinterpret_cast<const uint4*>(As + (wm * TM + i * 16) * ROWB + fo);
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                fb[j] = *reinterpret_cast<const uint4*>(Bs + (wn * TN + j * 16) * ROWB + fo);
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j) acc[i][j] = Mfma<T>::run(fa[i], fb[j], acc[i][j]);
+        }
+    }
+
+    // ---- epilogue: accumulators -> LDS (fp32, NP column passes) -> 16-byte stores
+    float* ep = reinterpret_cast<float*>(lds);
+    constexpr int CPR = WP / 8;
+    TC* C = static_cast<TC*>(G.C) + static_cast<int64_t>(blockIdx.z) * a.split_stride;
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+        __syncthreads();
+        if (EPI == EPI_SWIGLU) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB / 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = wm * TM + i * 16 + (lane >> 4) * 4 + r;
+                        const int col = wn * (TN / 2) + j * 16 + (lane & 15) - pass * WP;
+                        if (col >= 0 && col < WP) {
+                            const float g = acc[i][j][r], u = acc[i][j + NB / 2][r];
+                            ep[row * EP_STRIDE + col] = g / (1.0f + expf(-g)) * u;
+                        }
+                    }
+        } else {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = wm * TM + i * 16 + (lane >> 4) * 4 + r;
+                        const int col = wn * TN + j * 16 + (lane & 15) - pass * WP;
+                        if (col >= 0 && col < WP) ep[row * EP_STRIDE + col] = acc[i][j][r];
+                    }
+        }
+        __syncthreads();
+        for (int c = tid; c < BM * CPR; c += NT) {
+            const int r = c / CPR, cc = c % CPR;
+            const int col = n0 + pass * WP + cc * 8;
+            if (r >= rows || col >= N) continue;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = ep[r * EP_STRIDE + cc * 8 + e];
+            TC* dst = C + static_cast<int64_t>(row0 + r) * G.ldc + col;
+            if (col + 8 <= N) {
+                pack8(dst, v);
+            } else {
+                for (int e = 0; e < N - col; ++e) dst[e] = Elem<TC>::from_f32(v[e]);
+            }
+        }
+    }
+}
+
+// prefill tile: BM x BN (B rows), waves WM x WN, NST LDS stages
+constexpr int kBigBM = 128, kBigBN = 256, kBigWM = 2, kBigWN = 2, kBigNST = 3;
+
+}  // namespace
+
+int tile_bm(TileCfg cfg) { return cfg == TILE_SMALL ? 16 : kBigBM; }
+int tile_bn_out(TileCfg cfg, Epi epi) {
+    const int bn = cfg == TILE_SMALL ? 256 : kBigBN;  // B rows (gate + up rows for SwiGLU)
+    return epi == EPI_SWIGLU ? bn / 2 : bn;
+}
+
+namespace {
+
 template <typename T, typename TC, int EPI>
 hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n, hipStream_t stream) {
     const int bno = tile_bn_out(cfg, static_cast<Epi>(EPI));
@@ -263,8 +542,10 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
     dim3 grid(static_cast<unsigned>(max_tiles) * a.ntn, 1, a.nsplit);
     if (cfg == TILE_SMALL)
         hipLaunchKernelGGL((k_gemm<T, TC, 16, 256, 1, 4, EPI>), grid, dim3(256), 0, stream, a);
+    else if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((k_gemm_big<TC, kBigBM, kBigBN, kBigWM, kBigWN, kBigNST, EPI>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, a);
     else
-        hipLaunchKernelGGL((k_gemm<T, TC, 128, 128, 2, 2, EPI>), grid, dim3(256), 0, stream, a);
+        return hipErrorInvalidValue;  // fp32 runs the small tiles only
     return hipGetLastError();
 }
 

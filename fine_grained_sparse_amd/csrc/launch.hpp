@@ -42,8 +42,13 @@ struct GemmGroup {
     int64_t ldc;
 };
 
+// One M tile of a grouped GEMM.  `first` and `count` describe the run of
+// consecutive tiles that share weights (all tiles of one routed expert, or
+// up to 8 tiles of the shared rows); the GEMM walks each run M-tile-fastest
+// so those tiles stream every weight slice together.
 struct TileInfo {
     int32_t group, expert, row0, rows;
+    int32_t first, count, pad0_, pad1_;
 };
 
 struct GemmArgs {

@@ -64,6 +64,10 @@ __global__ __launch_bounds__(256) void k_topk_gate(const float* __restrict__ z, 
             for (int p = 0; p < nsplit; ++p) zz += z[p * split_stride + static_cast<int64_t>(t) * ldz + e];
             s[j] = 1.0f / (1.0f + expf(-zz));  // step 2: per-expert sigmoid
             v[j] = s[j] + b[e];                // step 3: the bias only chooses
+            // A NaN score would never win a comparison and leave the arg-max
+            // on its out-of-range sentinel; rank it below every number so the
+            // K picks are always valid, distinct expert ids.
+            if (!(v[j] == v[j])) v[j] = -INFINITY;
         } else {
             s[j] = 0.f;
             v[j] = -INFINITY;

@@ -203,3 +203,24 @@ def test_forward_parity_full_size_sampled(name):
     del inp, out, r
     torch.cuda.empty_cache()
     assert err <= 2e-2
+
+
+def test_nan_rows_still_route_to_valid_experts():
+    # Unsupported input, but it must not produce invalid expert ids: a NaN
+    # score ranks below every number, so each token still selects K
+    # distinct experts in range and the layer runs to completion.
+    wl = _custom(E=40, K=5, T=96)
+    log("[gpu] NaN rows")
+    inp = make_layer_inputs(wl, "cpu", seed=23)
+    inp["x"][::7] = float("nan")
+    dev = weights_to_device(inp, DEV)
+    idx, w, counts = moe.router(dev["x"], dev["W_r"], dev["b"], wl.K, wl.scale)
+    out, r = _run_forward(wl, dev)
+    gi = idx.cpu().numpy()
+    assert gi.min() >= 0 and gi.max() < wl.E
+    assert np.all(np.diff(gi, axis=1) > 0)
+    assert int(counts.cpu().sum()) == wl.T * wl.K
+    assert np.array_equal(r["idx"].cpu().numpy(), gi)
+    check_dispatch(r, wl.E)
+    ok = np.isfinite(inp["x"].float().numpy()).all(1)
+    assert torch.isfinite(out[torch.from_numpy(ok).to(DEV)].float()).all()
