@@ -289,18 +289,43 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(src) : "memory", "m0");
 }
 
-template <typename TC, int BM, int BN, int WM, int WN, int NST, int EPI>
-__global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const GemmArgs a) {
+// LDS swizzle of a row's 16-byte chunks (position = chunk ^ swz(row)).
+// ds_read_b128 serves 8 lanes per cycle: 8 consecutive rows at one logical
+// chunk must land on 8 different 16-byte bank groups of a 128-byte line.
+// 128-byte rows: chunk ^ (row & 7).  64-byte rows (two per line): the line
+// half is row & 1, so the chunk is flipped by (row >> 1) & 3.
+template <int ROWB>
+__device__ __forceinline__ int swz(int row) {
+    return ROWB == 128 ? (row & 7) : ((row >> 1) & 3);
+}
+
+// Workgroups per CU the LDS ring allows (two when a ring fits in 80 KiB).
+template <int BM, int BN, int NST, int ROWB>
+constexpr int big_occupancy() {
+    return NST * (BM + BN) * ROWB <= 81920 ? 2 : 1;
+}
+
+template <typename TC, int BM, int BN, int WM, int WN, int NST, int ROWB, int EPI>
+__global__ __launch_bounds__(64 * WM * WN, (big_occupancy<BM, BN, NST, ROWB>())) void k_gemm_big(const GemmArgs a) {
     using T = bf16_t;
     constexpr int ES = 2;
-    constexpr int ROWB = kStageRowBytes;  // 128 bytes of a row per stage
+    static_assert(ROWB == 64 || ROWB == 128, "bytes of a row per stage");
     constexpr int BKE = ROWB / ES;
+    constexpr int SLABS = ROWB / 64;           // 64-byte K slabs per stage
+    constexpr int CHUNKS = ROWB / 16;          // 16-byte chunks per row
+    constexpr int RPB = 1024 / ROWB;           // rows per 1 KiB block
     constexpr int NW = WM * WN;               // waves per workgroup
     constexpr int NT = 64 * NW;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int MB = TM / 16, NB = TN / 16;
     constexpr int BNO = EPI == EPI_SWIGLU ? BN / 2 : BN;
-    constexpr int LPW = (BM + BN) / (8 * NW);  // 1 KiB blocks per wave per stage
+    constexpr int NA = BM / RPB, NBB = BN / RPB;  // 1 KiB blocks of A and of B per stage
+    // A blocks are split across the waves, or (fewer A blocks than waves,
+    // small row tiles) loaded by every wave: the copies carry identical
+    // bytes to identical LDS addresses.  B blocks are split across waves.
+    constexpr bool A_ALL = NA < NW;
+    constexpr int LPA = A_ALL ? NA : NA / NW;
+    constexpr int LPW = LPA + NBB / NW;  // 1 KiB blocks per wave per stage
     constexpr int STAGE = (BM + BN) * ROWB;
     // epilogue passes: the fp32 tile goes through LDS in NP column slices
     constexpr int NP = (BM * (BNO + 4) * 4 <= NST * STAGE) ? 1
@@ -309,8 +334,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const GemmArgs a) 
     constexpr int WP = BNO / NP;
     constexpr int EP_STRIDE = WP + 4;
     constexpr int LDS_BYTES = (NST * STAGE > BM * EP_STRIDE * 4) ? NST * STAGE : BM * EP_STRIDE * 4;
-    static_assert((NW == 4 || NW == 8) && (BM + BN) % (8 * NW) == 0 && BM % 8 == 0, "tile shape");
-    static_assert(EPI != EPI_SWIGLU || (NB % 2 == 0 && (TN / 2) % 8 == 0), "gate/up pairs per wave");
+    static_assert((NW == 4 || NW == 8) && BM % RPB == 0 && NBB % NW == 0 && (A_ALL || NA % NW == 0), "tile shape");
+    static_assert(EPI != EPI_SWIGLU || (NB % 2 == 0 && (TN / 2) % RPB == 0), "gate/up pairs per wave");
     static_assert(NST >= 2 && LPW * (NST - 2) < 64, "pipeline depth");
     __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
@@ -318,7 +343,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const GemmArgs a) 
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid / WN, wn = wid % WN;
 
-    const int total = a.tiles ? (*a.ntiles) * a.ntn : static_cast<int>(gridDim.x);
+    const int total = (a.tiles ? *a.ntiles : (a.M + BM - 1) / BM) * a.ntn;  // active (M, N) tile pairs
     const int per = (total + 7) >> 3;
     const int slot = static_cast<int>(blockIdx.x) >> 3;
     const int lin = (static_cast<int>(blockIdx.x) & 7) * per + slot;
@@ -365,14 +390,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const GemmArgs a) 
     const int kt1 = min(nk, kt0 + chunk);
     const int nkt = kt1 - kt0;
 
-    // ---- this lane's source row in each block the wave loads.  Block
-    // q = wid + NW j covers tile rows 8q .. 8q+7 (A rows first, then B rows).
-    const int lrow = lane >> 3;
-    const int lchunk16 = ((lane & 7) ^ lrow) * 16;
+    // ---- this lane's source row in each block the wave loads.  Block q
+    // covers tile rows RPB q .. RPB q + RPB-1 (A rows first, then B rows);
+    // lane i fills LDS position (row i / CHUNKS, chunk i % CHUNKS), which
+    // holds logical chunk (i % CHUNKS) ^ swz(row).  blk(j) is the j-th block
+    // of this wave.
+    const int lrow = lane / CHUNKS;
+    const int lchunk16 = ((lane % CHUNKS) ^ swz<ROWB>(lrow)) * 16;
+    auto blk = [&](int j) { return j < LPA ? (A_ALL ? j : wid + NW * j) : NA + wid + NW * (j - LPA); };
     int srow[LPW];
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-        const int r = (wid + NW * j) * 8 + lrow;
+        const int r = blk(j) * RPB + lrow;
         if (r < BM) {
             const int p = row0 + (r < rows ? r : 0);
             srow[j] = G.rowmap ? G.rowmap[p] : p;
@@ -389,9 +418,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const GemmArgs a) 
         }
     }
     // whether block q reads A, the gate or the up matrix depends on q alone
-    auto blk_is_a = [&](int j) { return (wid + NW * j) * 8 < BM; };
+    auto blk_is_a = [&](int j) { return j < LPA; };
     auto blk_is_up = [&](int j) {
-        return EPI == EPI_SWIGLU && ((((wid + NW * j) * 8 - BM) % TN) >= TN / 2);
+        return EPI == EPI_SWIGLU && (((blk(j) * RPB - BM) % TN) >= TN / 2);
     };
     int cs = 0, ck = kt0;
     while (cs + 1 < G.nseg && ck >= seg_of(G, cs).K / BKE) {
@@ -414,12 +443,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const GemmArgs a) 
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(lds)));
     auto issue = [&](int buf) {
         const int64_t off = static_cast<int64_t>(ck) * ROWB;
-        const uint32_t dst = lds_base + buf * STAGE + wid * 1024;
+        const uint32_t dst = lds_base + buf * STAGE;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const bool isa = blk_is_a(j);
             const char* base = isa ? pA : (blk_is_up(j) ? pBu : pB);
-            lds_dma16(base + static_cast<int64_t>(srow[j]) * (isa ? lda : ldb) + off, dst + j * NW * 1024);
+            lds_dma16(base + static_cast<int64_t>(srow[j]) * (isa ? lda : ldb) + off, dst + blk(j) * 1024);
         }
         ++ck;
         if (cs + 1 < G.nseg && ck == seg_of(G, cs).K / BKE) {
@@ -435,11 +464,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const GemmArgs a) 
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // fragment offsets inside a 16-row group for the two 64-byte slabs:
-    // row (lane & 15), logical chunk 4*slab + (lane >> 4), swizzled by row & 7
+    // fragment offsets inside a 16-row group for each 64-byte slab:
+    // row (lane & 15), logical chunk 4*slab + (lane >> 4), swizzled by row
     const int frow = lane & 15;
-    const int fo0 = frow * ROWB + ((((lane >> 4) + 0) ^ (lane & 7)) << 4);
-    const int fo1 = frow * ROWB + ((((lane >> 4) + 4) ^ (lane & 7)) << 4);
+    const int fo0 = frow * ROWB + ((((lane >> 4) + 0) ^ swz<ROWB>(frow)) << 4);
+    const int fo1 = frow * ROWB + ((((lane >> 4) + 4) ^ swz<ROWB>(frow)) << 4);
 
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
@@ -454,7 +483,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const GemmArgs a) 
         const char* As = lds + (it % NST) * STAGE;
         const char* Bs = As + BM * ROWB;
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
+        for (int sl = 0; sl < SLABS; ++sl) {
             const int fo = sl ? fo1 : fo0;
             uint4 fa[MB], fb[NB];
 #pragma unroll
@@ -521,14 +550,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_big(const GemmArgs a) 
     }
 }
 
+// fp32 operands: register-staged 16 x 256 tiles
+constexpr int kF32BN = 256;
+// decode tile (few rows per expert): 16 x 512, one LDS ring of 4 stages
+constexpr int kSmBM = 16, kSmBN = 512, kSmWM = 1, kSmWN = 4, kSmNST = 4, kSmROWB = 64;
 // prefill tile: BM x BN (B rows), waves WM x WN, NST LDS stages
-constexpr int kBigBM = 128, kBigBN = 256, kBigWM = 2, kBigWN = 2, kBigNST = 3;
+constexpr int kBigBM = 128, kBigBN = 256, kBigWM = 2, kBigWN = 2, kBigNST = 3, kBigROWB = 64;
 
 }  // namespace
 
-int tile_bm(TileCfg cfg) { return cfg == TILE_SMALL ? 16 : kBigBM; }
-int tile_bn_out(TileCfg cfg, Epi epi) {
-    const int bn = cfg == TILE_SMALL ? 256 : kBigBN;  // B rows (gate + up rows for SwiGLU)
+static_assert(kSmBM == 16, "fp32 small tiles share the 16-row M tiling");
+int tile_bm(TileCfg cfg) { return cfg == TILE_SMALL ? kSmBM : kBigBM; }
+int tile_bn_out(TileCfg cfg, Epi epi) {  // bf16 kernels (sizing heuristics only)
+    const int bn = cfg == TILE_SMALL ? kSmBN : kBigBN;  // B rows (gate + up rows for SwiGLU)
     return epi == EPI_SWIGLU ? bn / 2 : bn;
 }
 
@@ -536,14 +570,25 @@ namespace {
 
 template <typename T, typename TC, int EPI>
 hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n, hipStream_t stream) {
-    const int bno = tile_bn_out(cfg, static_cast<Epi>(EPI));
+    // output columns per N tile of the kernel actually launched
+    const int bn = sizeof(T) == 4 ? kF32BN : (cfg == TILE_SMALL ? kSmBN : kBigBN);
+    const int bno = EPI == EPI_SWIGLU ? bn / 2 : bn;
     GemmArgs a = args;
     a.ntn = (max_n + bno - 1) / bno;
-    dim3 grid(static_cast<unsigned>(max_tiles) * a.ntn, 1, a.nsplit);
-    if (cfg == TILE_SMALL)
-        hipLaunchKernelGGL((k_gemm<T, TC, 16, 256, 1, 4, EPI>), grid, dim3(256), 0, stream, a);
+    // The XCD-aware remap sends block b to logical slot (b % 8) * per + b / 8
+    // with per = ceil(active / 8); it covers every active slot only when the
+    // grid holds 8 * per blocks, so round the grid up to a multiple of 8
+    // (blocks past the active slots return at once).
+    const unsigned blocks = static_cast<unsigned>(max_tiles) * a.ntn;
+    dim3 grid((blocks + 7u) & ~7u, 1, a.nsplit);
+    if constexpr (sizeof(T) == 4) {
+        // fp32 operands (small parity workloads): register-staged template
+        if (cfg != TILE_SMALL) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_gemm<T, TC, 16, kF32BN, 1, 4, EPI>), grid, dim3(256), 0, stream, a);
+    } else if (cfg == TILE_SMALL)
+        hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, kSmNST, kSmROWB, EPI>), grid, dim3(64 * kSmWM * kSmWN), 0, stream, a);
     else if constexpr (sizeof(T) == 2)
-        hipLaunchKernelGGL((k_gemm_big<TC, kBigBM, kBigBN, kBigWM, kBigWN, kBigNST, EPI>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_big<TC, kBigBM, kBigBN, kBigWM, kBigWN, kBigNST, kBigROWB, EPI>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, a);
     else
         return hipErrorInvalidValue;  // fp32 runs the small tiles only
     return hipGetLastError();
