@@ -6,15 +6,24 @@ experts, combine with the shared expert) over one batch of seeded synthetic
 input already resident in HBM.  Prints ONE JSON line.
 
 Default workload: the K2-shaped layer at 16384 tokens (prefill-sized
-grouped GEMMs); the 256-token decode-sized batch on the same weights is
-measured in the same run and reported under "also".
+grouped GEMMs).  Measured in the same run and reported under "also": the
+256-token decode batch on the same weights, the router alone at 4096
+tokens, and the K3-shaped latent layer.
 Per-stage durations come from hipEvents the library records at its stage
 boundaries on the launch stream (include/moe.h, MOE_EV_*); the up-projection
-stage is a single kernel (the grouped SwiGLU GEMM).
+stage is a single kernel (the grouped SwiGLU GEMM), the one the "roofline"
+object describes.  Its "traffic" is read from profiles/traffic.md when that
+table holds a row for the workload taken with the current kernel sources
+(otherwise null); `--summarize-counters` writes such rows from two
+rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) of this script.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,10 +36,40 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "traffic.md")
+UP_KERNEL = "grouped SwiGLU up-projection (k_gemm_big, EPI_SWIGLU)"
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    """Hash of the HIP library sources: counters taken on other sources do
+    not describe the kernels that run now."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "fine_grained_sparse_amd", "csrc", "*"))):
+        if p.endswith((".hip", ".hpp", ".cpp")):
+            h.update(os.path.basename(p).encode())
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """GB per dispatch of the up-projection for this workload and source."""
+    if not os.path.exists(TRAFFIC_MD):
+        return None
+    want = source_hash()
+    with open(TRAFFIC_MD) as f:
+        for line in f:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) >= 9 and cells[0] == workload and cells[2] == want:
+                try:
+                    return float(cells[8])
+                except ValueError:
+                    return None
+    return None
 
 
 def work_model(wl, counts):
@@ -54,14 +93,19 @@ def work_model(wl, counts):
     up = dict(
         flops=2.0 * A * din * 2 * F + 2.0 * T * d * 2 * Fsh,
         bytes=(touched * 2 * F * din * es + 2 * Fsh * d * es + T * din * es
-               + A * F * es + T * Fsh * es),
-        unit_flops=2.0 * din * 2 * F, units_flops=A + (T * Fsh / F if F else 0),
-        unit_bytes=2 * F * din * es, units_bytes=touched + (Fsh / F if F else 0))
+               + A * F * es + T * Fsh * es))
     return dict(touched=touched, flops_bf16=flops_routed + flops_shared + flops_latent,
                 flops_router=flops_router, bytes=bytes_step, up=up)
 
 
-def measure(moe, torch, wl, weights, steps, warmup, seed):
+def _events(torch, n, stream):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:        # create the underlying hipEvents before handing them over
+        e.record(stream)
+    return evs
+
+
+def measure_layer(moe, torch, wl, weights, steps, warmup, seed):
     from moe_inputs import make_router_inputs
     dev = torch.device("cuda:0")
     r_in = make_router_inputs(wl, dev, seed=seed)
@@ -74,42 +118,38 @@ def measure(moe, torch, wl, weights, steps, warmup, seed):
     _, routing = moe.forward(x, W_r, b, weights, wl.K, wl.scale, return_routing=True, **kw)
     counts = routing["counts"].cpu().tolist()
     nev = moe.NUM_STAGE_EVENTS
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
-    for row in evs:      # create the underlying hipEvents before handing them over
-        for e in row:
-            e.record(stream)
+    evs = [_events(torch, nev, stream) for _ in range(steps)]
     for _ in range(warmup):
         moe.forward(x, W_r, b, weights, wl.K, wl.scale, **kw)
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
     t0.record(stream)
     for i in range(steps):
         moe.forward(x, W_r, b, weights, wl.K, wl.scale, stage_events=evs[i], **kw)
     t1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / steps
     stages = {}
     for j in range(1, nev):
-        name = moe.STAGES[j]
-        stages[name] = sum(evs[i][j - 1].elapsed_time(evs[i][j]) for i in range(steps)) / steps
+        stages[moe.STAGES[j]] = sum(evs[i][j - 1].elapsed_time(evs[i][j]) for i in range(steps)) / steps
     wm = work_model(wl, counts)
     up_ms = stages["up"]
     up = wm["up"]
-    intensity = up["flops"] / up["bytes"]
-    if intensity >= RIDGE_BF16:
+    traffic = load_traffic(wl.name)
+    if up["flops"] / up["bytes"] >= RIDGE_BF16:
         ach = up["flops"] / (up_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None,
-                    kernel="grouped SwiGLU up-projection (k_gemm, EPI_SWIGLU)",
-                    avg_ms=round(up_ms, 4), algorithmic_tflop=round(up["flops"] / 1e12, 4))
+                    frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=traffic, kernel=UP_KERNEL,
+                    avg_ms=round(up_ms, 4), algorithmic_tflop=round(up["flops"] / 1e12, 4),
+                    algorithmic_gb=round(up["bytes"] / 1e9, 3))
     else:
         ach = up["bytes"] / (up_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=None,
-                    kernel="grouped SwiGLU up-projection (k_gemm, EPI_SWIGLU)",
-                    avg_ms=round(up_ms, 4), algorithmic_gb=round(up["bytes"] / 1e9, 3))
+                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=traffic, kernel=UP_KERNEL,
+                    avg_ms=round(up_ms, 4), algorithmic_gb=round(up["bytes"] / 1e9, 3),
+                    algorithmic_tflop=round(up["flops"] / 1e12, 4))
+    if traffic is not None:
+        roof["traffic_unit"] = "GB per launch"
     layer_s = ms * 1e-3
     layer = dict(tflops_bf16=round(wm["flops_bf16"] / layer_s / 1e12, 2),
                  mfma_frac=round(wm["flops_bf16"] / layer_s / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -119,8 +159,39 @@ def measure(moe, torch, wl, weights, steps, warmup, seed):
                  algorithmic_gb=round(wm["bytes"] / 1e9, 3),
                  touched_experts=wm["touched"],
                  hist_min_mean_max=[min(counts), round(sum(counts) / len(counts), 2), max(counts)])
-    return dict(value=wl.T / layer_s, ms=ms, wall_s=wall, stages={k: round(v, 4) for k, v in stages.items()},
+    return dict(value=wl.T / layer_s, ms=ms, stages={k: round(v, 4) for k, v in stages.items()},
                 roofline=roof, layer=layer, inputs=(x, W_r, b))
+
+
+def measure_router(moe, torch, wl, steps, warmup, seed):
+    """moe_router alone: logits (fp32 accumulation of the exact bf16 x bf16
+    products of x with the three bf16 planes of W_r), top-K gate, counts."""
+    from moe_inputs import make_router_inputs
+    dev = torch.device("cuda:0")
+    r_in = make_router_inputs(wl, dev, seed=seed)
+    x, W_r, b = r_in["x"], r_in["W_r"], r_in["b"]
+    ws = moe.Workspace()
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        moe.router(x, W_r, b, wl.K, wl.scale, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        moe.router(x, W_r, b, wl.K, wl.scale, workspace=ws, stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    fl = 2.0 * wl.T * wl.d * wl.E
+    ach = fl / (ms * 1e-3) / 1e12
+    return dict(value=round(wl.T / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 4),
+                roofline=dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_F32_TFLOPS,
+                              unit="TFLOP/s", frac=round(ach / PEAK_F32_TFLOPS, 4), traffic=None,
+                              kernel="router logits + top-K gate (fp32-accurate, bf16x3 MFMA)",
+                              note="fp32 flops 2*T*d*E against the fp32 matrix peak; executed "
+                                   "as 3 bf16 MFMA passes",
+                              executed_bf16_tflops=round(3 * ach, 2)),
+                config=dict(workload=wl.name, T=wl.T, d=wl.d, E=wl.E, K=wl.K))
 
 
 def cpu_baseline(torch, wl, weights, x, W_r, b, target_s, seed):
@@ -151,13 +222,10 @@ def cpu_baseline(torch, wl, weights, x, W_r, b, target_s, seed):
         oracle.forward(lay, xs, nthreads=nth)
         return len(toks), time.perf_counter() - t
 
-    n1, s1 = run(nth)
-    n = n1
-    s = s1
-    if s1 < target_s / 2:
-        n2 = int(min(wl.T, max(nth, nth * int(target_s / max(s1, 1e-3)))))
-        n2 = min(n2, 32 * nth)
-        if n2 > n1:
+    n, s = run(nth)
+    if s < target_s / 2:
+        n2 = int(min(wl.T, 96 * nth, max(nth, nth * int(target_s / max(s, 1e-3)))))
+        if n2 > n:
             n, s = run(n2)
     return dict(value=round(n / s, 3), unit="tokens/s", cores=nth, kind="oracle",
                 sample=(f"{n} random tokens of the {wl.T}-token batch, whole layer per token "
@@ -166,21 +234,70 @@ def cpu_baseline(torch, wl, weights, x, W_r, b, target_s, seed):
                 seconds=round(s, 2))
 
 
+def summarize_counters(fetch_dir, write_dir, workload):
+    """One markdown row of profiles/traffic.md from two rocprofv3 --pmc passes
+    of this script (FETCH_SIZE, then WRITE_SIZE, run with
+    --calibrate-copy-gib so each pass also holds a plain copy of known size).
+    Kernel names must not be truncated (no -T): the up projection is the
+    k_gemm_big instantiation whose last template argument is EPI_SWIGLU."""
+    def load(d):
+        rows = []
+        for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(p) as f:
+                rows += list(csv.DictReader(f))
+        return rows
+
+    def is_up(name):
+        m = re.search(r"k_gemm_big<([^>]*)>", name)
+        return bool(m) and m.group(1).replace(" ", "").split(",")[-1] == "1"
+
+    out = {}
+    for tag, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = load(d)
+        up = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == tag and is_up(r["Kernel_Name"])]
+        # the copy: elementwise dispatches of 2 GiB read + 2 GiB written each
+        # (torch splits the 4 GiB add in two); the fill before it reads nothing
+        cal = [float(r["Counter_Value"]) for r in rows
+               if r["Counter_Name"] == tag and "elementwise" in r["Kernel_Name"]
+               and int(r.get("Grid_Size", 0) or 0) == 134217728]
+        if tag == "FETCH_SIZE":
+            cal = [c for c in cal if c > 1e5][-3:]
+        else:
+            cal = cal[-3:]
+        if not up or not cal:
+            raise SystemExit(f"{tag}: no up-projection dispatches or no copy calibration in {d}")
+        scale = (2 * 2 ** 30) / (sum(cal) / len(cal) * 1024)
+        out[tag] = (sum(up) / len(up), len(up), scale)
+    f_kib, n, f_sc = out["FETCH_SIZE"]
+    w_kib, _, w_sc = out["WRITE_SIZE"]
+    gb = (f_kib * 1024 * f_sc + w_kib * 1024 * w_sc) / 1e9
+    row = (f"| {workload} | up projection (SwiGLU) | {source_hash()} | {n} | {f_kib:.6g} | "
+           f"{w_kib:.6g} | {f_sc:.3f} | {w_sc:.3f} | {gb:.3f} |")
+    print(row)
+    return row
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="k2_prefill_t16384")
-    ap.add_argument("--also", default="k2_decode_t256",
-                    help="comma-separated extra workloads on the same weights ('' for none)")
+    ap.add_argument("--also", default="k2_decode_t256,k2_router_t4096,k3_latent_t4096",
+                    help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="target seconds of oracle time (0 skips the CPU baseline)")
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run a plain streaming copy (out = in + 0, fp32) of this many GiB "
                          "three times, to scale HBM byte counters (0 = off)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the profiles/traffic.md row of --workload from two rocprofv3 "
+                         "--pmc output directories and exit (no GPU use)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the layer is measured on one GPU's share, see DESIGN.md)", file=sys.stderr)
@@ -207,38 +324,50 @@ def main():
     weights = make_expert_weights(wl, "cuda:0", seed=args.seed)
     torch.cuda.synchronize()
     log(f"[bench] timing {wl.name}: warmup {args.warmup}, steps {args.steps}")
-    main_r = measure(moe, torch, wl, weights, args.steps, args.warmup, args.seed)
+    main_r = measure_layer(moe, torch, wl, weights, args.steps, args.warmup, args.seed)
     log(f"[bench] {wl.name}: {main_r['ms']:.3f} ms/step, stages {main_r['stages']}")
-    also = {}
-    for name in [s for s in args.also.split(",") if s]:
-        awl = get_workload(name)
-        same = (awl.d, awl.E, awl.F, awl.n_shared, awl.F_shared, awl.d_latent, awl.act_dtype) == \
-               (wl.d, wl.E, wl.F, wl.n_shared, wl.F_shared, wl.d_latent, wl.act_dtype)
-        if not same:
-            log(f"[bench] skipping {name}: different weights")
-            continue
-        log(f"[bench] timing {name}")
-        r = measure(moe, torch, awl, weights, max(args.steps, 20), args.warmup, args.seed)
-        log(f"[bench] {name}: {r['ms']:.3f} ms/step, stages {r['stages']}")
-        also[name] = dict(value=round(r["value"], 1), unit="tokens/s", ms_per_step=round(r["ms"], 4),
-                          roofline=r["roofline"], layer=r["layer"], stages_ms=r["stages"],
-                          config=dict(workload=name, T=awl.T))
     cpu = None
     if args.cpu_baseline_seconds > 0:
         log("[bench] CPU baseline (oracle)")
         x, W_r, b = main_r["inputs"]
         cpu = cpu_baseline(torch, wl, weights, x, W_r, b, args.cpu_baseline_seconds, args.seed)
         log(f"[bench] oracle: {cpu['value']} tokens/s on {cpu['cores']} threads")
+    also = {}
+    others = [s for s in args.also.split(",") if s]
+    for name in others:
+        awl = get_workload(name)
+        log(f"[bench] timing {name}")
+        if awl.router_only:
+            r = measure_router(moe, torch, awl, max(args.steps, 50), args.warmup, args.seed)
+            log(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step")
+            also[name] = r
+            continue
+        same = (awl.d, awl.E, awl.F, awl.n_shared, awl.F_shared, awl.d_latent, awl.act_dtype) == \
+               (wl.d, wl.E, wl.F, wl.n_shared, wl.F_shared, wl.d_latent, wl.act_dtype)
+        if not same:
+            del weights
+            torch.cuda.empty_cache()
+            log(f"[bench] generating weights for {name} on the GPU")
+            weights = make_expert_weights(awl, "cuda:0", seed=args.seed)
+            wl = awl
+        r = measure_layer(moe, torch, awl, weights, max(args.steps, 20), args.warmup, args.seed)
+        log(f"[bench] {name}: {r['ms']:.3f} ms/step, stages {r['stages']}")
+        also[name] = dict(value=round(r["value"], 1), unit="tokens/s", ms_per_step=round(r["ms"], 4),
+                          roofline=r["roofline"], layer=r["layer"], stages_ms=r["stages"],
+                          config=dict(workload=name, T=awl.T, d=awl.d, E=awl.E, K=awl.K,
+                                      F=awl.F, n_shared=awl.n_shared, F_shared=awl.F_shared,
+                                      d_latent=awl.d_latent, scale=awl.scale))
+    mw = get_workload(args.workload)
     line = {
         "metric": METRIC, "value": round(main_r["value"], 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(main_r["ms"], 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.act_dtype,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": mw.act_dtype,
         "data": "synthetic (seeded N(0,1) x, N(0,1/fan_in) weights, Zipf(1.1) expert skew)",
-        "config": dict(workload=wl.name, T=wl.T, d=wl.d, E=wl.E, K=wl.K, F=wl.F,
-                       n_shared=wl.n_shared, F_shared=wl.F_shared, d_latent=wl.d_latent,
-                       scale=wl.scale, parallelism="single-gpu"),
+        "config": dict(workload=mw.name, T=mw.T, d=mw.d, E=mw.E, K=mw.K, F=mw.F,
+                       n_shared=mw.n_shared, F_shared=mw.F_shared, d_latent=mw.d_latent,
+                       scale=mw.scale, parallelism="single-gpu"),
         "roofline": main_r["roofline"], "cpu_baseline": cpu, "layer": main_r["layer"],
-        "stages_ms": main_r["stages"], "also": also,
+        "stages_ms": main_r["stages"], "kernel_source": source_hash(), "also": also,
     }
     print(json.dumps(line), flush=True)
 

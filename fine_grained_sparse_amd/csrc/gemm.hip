@@ -552,8 +552,8 @@ __global__ __launch_bounds__(64 * WM * WN, (big_occupancy<BM, BN, NST, ROWB>()))
 
 // fp32 operands: register-staged 16 x 256 tiles
 constexpr int kF32BN = 256;
-// decode tile (few rows per expert): 16 x 512, one LDS ring of 4 stages
-constexpr int kSmBM = 16, kSmBN = 512, kSmWM = 1, kSmWN = 4, kSmNST = 4, kSmROWB = 64;
+// decode tile (few rows per expert): 16 x 512, two stages of 128-byte row pieces
+constexpr int kSmBM = 16, kSmBN = 512, kSmWM = 1, kSmWN = 4, kSmNST = 2, kSmROWB = 128;
 // prefill tile: BM x BN (B rows), waves WM x WN, NST LDS stages
 constexpr int kBigBM = 128, kBigBN = 256, kBigWM = 2, kBigWN = 2, kBigNST = 3, kBigROWB = 64;
 
