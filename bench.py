@@ -37,7 +37,9 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "traffic.md")
-UP_KERNEL = "grouped SwiGLU up-projection (k_gemm_big, EPI_SWIGLU)"
+CAL_REPS = 3                # streaming copies of --calibrate-copy-gib each
+WEIGHTS_NOTE = {"frag16": "bf16, fragment-block layout (moe_pack_weights once at load, untimed)",
+                "rows": "bf16, row-major"}
 
 
 def log(msg):
@@ -56,20 +58,45 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """GB per dispatch of the up-projection for this workload and source."""
+def load_traffic(workload: str, layout: str):
+    """GB per dispatch of the up-projection for this workload, weight layout
+    and kernel source (a row of profiles/traffic.md), else None."""
     if not os.path.exists(TRAFFIC_MD):
         return None
     want = source_hash()
     with open(TRAFFIC_MD) as f:
         for line in f:
             cells = [c.strip() for c in line.strip().strip("|").split("|")]
-            if len(cells) >= 9 and cells[0] == workload and cells[2] == want:
+            if len(cells) >= 10 and cells[0] == workload and cells[1] == layout and cells[3] == want:
                 try:
-                    return float(cells[8])
+                    return float(cells[9])
                 except ValueError:
                     return None
     return None
+
+
+def up_kernel(wl, layout):
+    """The kernel the library runs for the up projection of this workload."""
+    big_rows = wl.T * wl.K >= 64 * wl.E and wl.act_dtype == "bf16"
+    if big_rows and layout == "frag16":
+        return "k_gemm_wide (128x512, register-fed packed weights)"
+    return "k_gemm_big (" + ("128x256" if big_rows else "16x512") + ", weights through LDS)"
+
+
+def is_up_kernel(name):
+    """Kernel name (untruncated) of an up-projection dispatch: the SwiGLU
+    instantiation of k_gemm_wide<TC, EPI, NSEG> or of
+    k_gemm_big<TC, BM, BN, WM, WN, NST, ROWB, EPI, PK>."""
+    m = re.search(r"k_gemm_(wide|big)<([^>]*)>", name)
+    if not m:
+        return False
+    args = m.group(2).replace(" ", "").split(",")
+    return (args[1] if m.group(1) == "wide" else args[7]) == "1"
+
+
+def get_workload_light(name):
+    from moe_inputs import get_workload
+    return get_workload(name)
 
 
 def work_model(wl, counts):
@@ -105,7 +132,17 @@ def _events(torch, n, stream):
     return evs
 
 
-def measure_layer(moe, torch, wl, weights, steps, warmup, seed):
+def prepare(moe, torch, wl, rows, layout):
+    """The weights the layer reads: row-major as generated, or packed once
+    (a one-time load step, not part of the timed forward)."""
+    if layout == "rows":
+        return rows
+    packed = moe.pack_weights(rows, n_shared=wl.n_shared)
+    torch.cuda.synchronize()
+    return packed
+
+
+def measure_layer(moe, torch, wl, weights, steps, warmup, seed, layout):
     from moe_inputs import make_router_inputs
     dev = torch.device("cuda:0")
     r_in = make_router_inputs(wl, dev, seed=seed)
@@ -135,17 +172,18 @@ def measure_layer(moe, torch, wl, weights, steps, warmup, seed):
     wm = work_model(wl, counts)
     up_ms = stages["up"]
     up = wm["up"]
-    traffic = load_traffic(wl.name)
+    traffic = load_traffic(wl.name, layout)
+    kernel = up_kernel(wl, layout)
     if up["flops"] / up["bytes"] >= RIDGE_BF16:
         ach = up["flops"] / (up_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=traffic, kernel=UP_KERNEL,
+                    frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=traffic, kernel=kernel,
                     avg_ms=round(up_ms, 4), algorithmic_tflop=round(up["flops"] / 1e12, 4),
                     algorithmic_gb=round(up["bytes"] / 1e9, 3))
     else:
         ach = up["bytes"] / (up_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=traffic, kernel=UP_KERNEL,
+                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=traffic, kernel=kernel,
                     avg_ms=round(up_ms, 4), algorithmic_gb=round(up["bytes"] / 1e9, 3),
                     algorithmic_tflop=round(up["flops"] / 1e12, 4))
     if traffic is not None:
@@ -234,12 +272,13 @@ def cpu_baseline(torch, wl, weights, x, W_r, b, target_s, seed):
                 seconds=round(s, 2))
 
 
-def summarize_counters(fetch_dir, write_dir, workload):
+def summarize_counters(fetch_dir, write_dir, workload, layout, copy_gib):
     """One markdown row of profiles/traffic.md from two rocprofv3 --pmc passes
-    of this script (FETCH_SIZE, then WRITE_SIZE, run with
-    --calibrate-copy-gib so each pass also holds a plain copy of known size).
-    Kernel names must not be truncated (no -T): the up projection is the
-    k_gemm_big instantiation whose last template argument is EPI_SWIGLU."""
+    of this script (FETCH_SIZE, then WRITE_SIZE), each run with
+    --calibrate-copy-gib so that it also holds CAL_REPS streaming copies
+    (torch.neg, fp32) of known size.  Kernel names must not be truncated
+    (no -T; see is_up_kernel).  Counter rows of a kernel split into several
+    dispatches (the large copy) are summed."""
     def load(d):
         rows = []
         for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -247,32 +286,24 @@ def summarize_counters(fetch_dir, write_dir, workload):
                 rows += list(csv.DictReader(f))
         return rows
 
-    def is_up(name):
-        m = re.search(r"k_gemm_big<([^>]*)>", name)
-        return bool(m) and m.group(1).replace(" ", "").split(",")[-1] == "1"
-
+    if copy_gib <= 0:
+        raise SystemExit("--calibrate-copy-gib must name the copy size the passes ran with")
+    copy_bytes = CAL_REPS * (int(copy_gib * (1 << 30)) // 4) * 4   # read (= written) by the copies
     out = {}
     for tag, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rows = load(d)
-        up = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == tag and is_up(r["Kernel_Name"])]
-        # the copy: elementwise dispatches of 2 GiB read + 2 GiB written each
-        # (torch splits the 4 GiB add in two); the fill before it reads nothing
-        cal = [float(r["Counter_Value"]) for r in rows
-               if r["Counter_Name"] == tag and "elementwise" in r["Kernel_Name"]
-               and int(r.get("Grid_Size", 0) or 0) == 134217728]
-        if tag == "FETCH_SIZE":
-            cal = [c for c in cal if c > 1e5][-3:]
-        else:
-            cal = cal[-3:]
+        rows = [r for r in load(d) if r["Counter_Name"] == tag]
+        up = [float(r["Counter_Value"]) for r in rows if is_up_kernel(r["Kernel_Name"])]
+        cal = [float(r["Counter_Value"]) for r in rows if "neg_kernel" in r["Kernel_Name"]]
         if not up or not cal:
             raise SystemExit(f"{tag}: no up-projection dispatches or no copy calibration in {d}")
-        scale = (2 * 2 ** 30) / (sum(cal) / len(cal) * 1024)
+        scale = copy_bytes / (sum(cal) * 1024)
         out[tag] = (sum(up) / len(up), len(up), scale)
     f_kib, n, f_sc = out["FETCH_SIZE"]
     w_kib, _, w_sc = out["WRITE_SIZE"]
     gb = (f_kib * 1024 * f_sc + w_kib * 1024 * w_sc) / 1e9
-    row = (f"| {workload} | up projection (SwiGLU) | {source_hash()} | {n} | {f_kib:.6g} | "
-           f"{w_kib:.6g} | {f_sc:.3f} | {w_sc:.3f} | {gb:.3f} |")
+    wl = get_workload_light(workload)
+    row = (f"| {workload} | {layout} | {up_kernel(wl, layout).split(' ')[0]} | {source_hash()} | {n} | "
+           f"{f_kib:.6g} | {w_kib:.6g} | {f_sc:.3f} | {w_sc:.3f} | {gb:.3f} |")
     print(row)
     return row
 
@@ -288,15 +319,18 @@ def main():
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="target seconds of oracle time (0 skips the CPU baseline)")
     ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--layout", choices=("frag16", "rows"), default="frag16",
+                    help="weight layout the layer reads: packed once at load (frag16, "
+                         "moe_pack_weights, outside the timed steps) or row-major")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
-                    help="also run a plain streaming copy (out = in + 0, fp32) of this many GiB "
+                    help="also run a plain streaming copy (out = -in, fp32) of this many GiB "
                          "three times, to scale HBM byte counters (0 = off)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the profiles/traffic.md row of --workload from two rocprofv3 "
                          "--pmc output directories and exit (no GPU use)")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, args.workload)
+        summarize_counters(*args.summarize_counters, args.workload, args.layout, args.calibrate_copy_gib)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -311,27 +345,32 @@ def main():
         n = int(args.calibrate_copy_gib * (1 << 30)) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.add(src, 0.0, out=dst)
+        for _ in range(CAL_REPS):
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        log(f"[bench] copy calibration: 3 x (read {n * 4} B, write {n * 4} B)")
+        log(f"[bench] copy calibration: {CAL_REPS} x (read {n * 4} B, write {n * 4} B)")
         del src, dst
         torch.cuda.empty_cache()
     wl = get_workload(args.workload)
     if wl.router_only:
         sys.exit("choose a whole-layer workload")
     log(f"[bench] generating weights for {wl.name} on the GPU")
-    weights = make_expert_weights(wl, "cuda:0", seed=args.seed)
+    rows = make_expert_weights(wl, "cuda:0", seed=args.seed)
+    weights = prepare(moe, torch, wl, rows, args.layout)
+    if args.cpu_baseline_seconds <= 0:
+        del rows
+        rows = None
     torch.cuda.synchronize()
     log(f"[bench] timing {wl.name}: warmup {args.warmup}, steps {args.steps}")
-    main_r = measure_layer(moe, torch, wl, weights, args.steps, args.warmup, args.seed)
+    main_r = measure_layer(moe, torch, wl, weights, args.steps, args.warmup, args.seed, args.layout)
     log(f"[bench] {wl.name}: {main_r['ms']:.3f} ms/step, stages {main_r['stages']}")
     cpu = None
     if args.cpu_baseline_seconds > 0:
         log("[bench] CPU baseline (oracle)")
         x, W_r, b = main_r["inputs"]
-        cpu = cpu_baseline(torch, wl, weights, x, W_r, b, args.cpu_baseline_seconds, args.seed)
+        cpu = cpu_baseline(torch, wl, rows, x, W_r, b, args.cpu_baseline_seconds, args.seed)
         log(f"[bench] oracle: {cpu['value']} tokens/s on {cpu['cores']} threads")
+    rows = None
     also = {}
     others = [s for s in args.also.split(",") if s]
     for name in others:
@@ -348,15 +387,17 @@ def main():
             del weights
             torch.cuda.empty_cache()
             log(f"[bench] generating weights for {name} on the GPU")
-            weights = make_expert_weights(awl, "cuda:0", seed=args.seed)
+            weights = prepare(moe, torch, awl, make_expert_weights(awl, "cuda:0", seed=args.seed),
+                              args.layout)
             wl = awl
-        r = measure_layer(moe, torch, awl, weights, max(args.steps, 20), args.warmup, args.seed)
+        r = measure_layer(moe, torch, awl, weights, max(args.steps, 20), args.warmup, args.seed, args.layout)
         log(f"[bench] {name}: {r['ms']:.3f} ms/step, stages {r['stages']}")
         also[name] = dict(value=round(r["value"], 1), unit="tokens/s", ms_per_step=round(r["ms"], 4),
                           roofline=r["roofline"], layer=r["layer"], stages_ms=r["stages"],
                           config=dict(workload=name, T=awl.T, d=awl.d, E=awl.E, K=awl.K,
                                       F=awl.F, n_shared=awl.n_shared, F_shared=awl.F_shared,
-                                      d_latent=awl.d_latent, scale=awl.scale))
+                                      d_latent=awl.d_latent, scale=awl.scale,
+                                      weights=WEIGHTS_NOTE[args.layout]))
     mw = get_workload(args.workload)
     line = {
         "metric": METRIC, "value": round(main_r["value"], 1), "unit": "tokens/s", "n_gpus": 1,
@@ -365,7 +406,8 @@ def main():
         "data": "synthetic (seeded N(0,1) x, N(0,1/fan_in) weights, Zipf(1.1) expert skew)",
         "config": dict(workload=mw.name, T=mw.T, d=mw.d, E=mw.E, K=mw.K, F=mw.F,
                        n_shared=mw.n_shared, F_shared=mw.F_shared, d_latent=mw.d_latent,
-                       scale=mw.scale, parallelism="single-gpu"),
+                       scale=mw.scale, weights=WEIGHTS_NOTE[args.layout],
+                       parallelism="single-gpu"),
         "roofline": main_r["roofline"], "cpu_baseline": cpu, "layer": main_r["layer"],
         "stages_ms": main_r["stages"], "kernel_source": source_hash(), "also": also,
     }

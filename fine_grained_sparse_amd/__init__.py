@@ -23,10 +23,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
+MOE_LAYOUT_ROWS, MOE_LAYOUT_FRAG16 = 0, 1
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
            4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_UNSUPPORTED", 6: "MOE_ERR_HIP"}
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
-EXPORTS = ("moe_workspace_size", "moe_router", "moe_forward", "moe_status_str")
+EXPORTS = ("moe_workspace_size", "moe_router", "moe_forward", "moe_pack_weights", "moe_status_str")
+WEIGHT_NAMES = ("W_gate", "W_up", "W_down", "Ws_gate", "Ws_up", "Ws_down", "W_lat_down", "W_lat_up")
 STAGES = ("start", "router", "dispatch", "latent", "up", "down", "end")
 NUM_STAGE_EVENTS = len(STAGES)
 
@@ -43,13 +45,11 @@ class LayerDesc(ctypes.Structure):
                 ("K", ctypes.c_int32), ("F", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("F_shared", ctypes.c_int32), ("d_latent", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("act_dtype", ctypes.c_int32),
-                ("w_dtype", ctypes.c_int32)]
+                ("w_dtype", ctypes.c_int32), ("w_layout", ctypes.c_int32)]
 
 
 class ExpertWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in
-                ("W_gate", "W_up", "W_down", "Ws_gate", "Ws_up", "Ws_down",
-                 "W_lat_down", "W_lat_up")]
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
 
 
 _lib = None
@@ -73,6 +73,9 @@ def lib():
                                   ctypes.POINTER(ExpertWeights), vp, vp, vp, vp, vp, vp,
                                   vp, ctypes.c_size_t, vp, vp]
         L.moe_forward.restype = ctypes.c_int
+        L.moe_pack_weights.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(ExpertWeights),
+                                       ctypes.POINTER(ExpertWeights), vp]
+        L.moe_pack_weights.restype = ctypes.c_int
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -80,9 +83,9 @@ def lib():
 
 
 def desc(*, T, d, E, K, F=0, n_shared=0, F_shared=0, d_latent=0, scale=2.827,
-         act_dtype=MOE_BF16, w_dtype=None):
+         act_dtype=MOE_BF16, w_dtype=None, w_layout=MOE_LAYOUT_ROWS):
     return LayerDesc(T, d, E, K, F, n_shared, F_shared, d_latent, scale, act_dtype,
-                     act_dtype if w_dtype is None else w_dtype)
+                     act_dtype if w_dtype is None else w_dtype, w_layout)
 
 
 def workspace_size(layer_desc: LayerDesc, forward: bool) -> int:
@@ -157,23 +160,8 @@ def router(x, W_r, b, K, scale=2.827, *, counts=True, workspace=None, stream=Non
     return idx, w, cnt
 
 
-def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
-            return_routing=False, workspace=None, stream=None, stage_events=None):
-    """moe_forward: the whole layer.  `weights` holds W_gate [E,F,d_in],
-    W_up [E,F,d_in], W_down [E,d_in,F] and optionally Ws_gate/Ws_up
-    [n_shared*F_shared, d], Ws_down [d, n_shared*F_shared], W_lat_down
-    [d_latent, d], W_lat_up [d, d_latent].  Returns out [T, d], or
-    (out, routing dict) with return_routing=True.  `stage_events` (optional)
-    is a sequence of NUM_STAGE_EVENTS already-created torch.cuda.Event
-    objects recorded at the stage boundaries listed in include/moe.h."""
-    _need(x, "x")
-    if x.dim() != 2 or x.dtype not in _DT:
-        raise ValueError("x must be [T, d] fp32 or bf16")
-    T, d = x.shape
-    dev, dt = x.device, x.dtype
-    E = W_r.shape[0]
-    _need(W_r, "W_r", torch.float32, (E, d), dev)
-    _need(b, "b", torch.float32, (E,), dev)
+def _weights_desc(weights, T, d, E, K, scale, dt, dev, n_shared):
+    """Validate the weight tensors; return (LayerDesc, ExpertWeights)."""
     Wg, Wu, Wd = weights["W_gate"], weights["W_up"], weights["W_down"]
     _need(Wg, "W_gate", dt, device=dev)
     if Wg.dim() != 3 or Wg.shape[0] != E:
@@ -199,8 +187,55 @@ def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
         _need(Wsg, "Ws_gate", dt, (ns * Fs, d), dev)
         _need(Wsu, "Ws_up", dt, (ns * Fs, d), dev)
         _need(Wsd, "Ws_down", dt, (d, ns * Fs), dev)
+    layout = int(weights.get("layout", MOE_LAYOUT_ROWS))
     D = desc(T=T, d=d, E=E, K=K, F=F, n_shared=ns, F_shared=Fs, d_latent=d_lat,
-             scale=scale, act_dtype=_DT[dt])
+             scale=scale, act_dtype=_DT[dt], w_layout=layout)
+    W = ExpertWeights(*[None if t is None else t.data_ptr() for t in
+                        (Wg, Wu, Wd, Wsg, Wsu, Wsd, Wl_d, Wl_u)])
+    return D, W
+
+
+def pack_weights(weights, *, n_shared=None, stream=None):
+    """moe_pack_weights: bf16 row-major weights -> a new dict of tensors of
+    the same shapes in MOE_LAYOUT_FRAG16, with "layout" set.  Run once, e.g.
+    at model load; the packed tensors are what forward() then reads."""
+    if int(weights.get("layout", MOE_LAYOUT_ROWS)) != MOE_LAYOUT_ROWS:
+        raise ValueError("weights are already packed")
+    Wg = weights["W_gate"]
+    if Wg.dtype != torch.bfloat16:
+        raise TypeError("only bf16 weights have a packed layout")
+    E, F, din = Wg.shape
+    d = weights["W_lat_down"].shape[1] if weights.get("W_lat_down") is not None else din
+    D, src = _weights_desc(weights, 1, d, E, 1, 1.0, Wg.dtype, Wg.device, n_shared)
+    out = {k: (torch.empty_like(weights[k]) if weights.get(k) is not None else None) for k in WEIGHT_NAMES}
+    dst = ExpertWeights(*[None if out[k] is None else out[k].data_ptr() for k in WEIGHT_NAMES])
+    rc = lib().moe_pack_weights(ctypes.byref(D), ctypes.byref(src), ctypes.byref(dst), _stream(stream))
+    if rc:
+        raise MoeError("moe_pack_weights", rc)
+    out["layout"] = MOE_LAYOUT_FRAG16
+    return out
+
+
+def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
+            return_routing=False, workspace=None, stream=None, stage_events=None):
+    """moe_forward: the whole layer.  `weights` holds W_gate [E,F,d_in],
+    W_up [E,F,d_in], W_down [E,d_in,F] and optionally Ws_gate/Ws_up
+    [n_shared*F_shared, d], Ws_down [d, n_shared*F_shared], W_lat_down
+    [d_latent, d], W_lat_up [d, d_latent], plus "layout" (MOE_LAYOUT_ROWS
+    when absent; pack_weights returns MOE_LAYOUT_FRAG16 weights).  Returns
+    out [T, d], or (out, routing dict) with return_routing=True.
+    `stage_events` (optional) is a sequence of NUM_STAGE_EVENTS
+    already-created torch.cuda.Event objects recorded at the stage
+    boundaries listed in include/moe.h."""
+    _need(x, "x")
+    if x.dim() != 2 or x.dtype not in _DT:
+        raise ValueError("x must be [T, d] fp32 or bf16")
+    T, d = x.shape
+    dev, dt = x.device, x.dtype
+    E = W_r.shape[0]
+    _need(W_r, "W_r", torch.float32, (E, d), dev)
+    _need(b, "b", torch.float32, (E,), dev)
+    D, W = _weights_desc(weights, T, d, E, K, scale, dt, dev, n_shared)
     nbytes = workspace_size(D, True)
     if nbytes == 0:
         raise MoeError("moe_workspace_size", 2)
@@ -208,8 +243,6 @@ def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
         out = torch.empty((T, d), dtype=dt, device=dev)
     else:
         _need(out, "out", dt, (T, d), dev)
-    W = ExpertWeights(*[None if t is None else t.data_ptr() for t in
-                        (Wg, Wu, Wd, Wsg, Wsu, Wsd, Wl_d, Wl_u)])
     routing = None
     if return_routing:
         routing = dict(idx=torch.empty((T, K), dtype=torch.int32, device=dev),
@@ -233,5 +266,6 @@ def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
     return (out, routing) if return_routing else out
 
 
-__all__ = ["router", "forward", "workspace_size", "desc", "lib", "MoeError",
-           "LayerDesc", "ExpertWeights", "Workspace", "MOE_F32", "MOE_BF16", "EXPORTS"]
+__all__ = ["router", "forward", "pack_weights", "workspace_size", "desc", "lib", "MoeError",
+           "LayerDesc", "ExpertWeights", "Workspace", "MOE_F32", "MOE_BF16", "MOE_LAYOUT_ROWS",
+           "MOE_LAYOUT_FRAG16", "EXPORTS", "WEIGHT_NAMES"]

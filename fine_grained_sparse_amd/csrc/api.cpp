@@ -12,6 +12,8 @@
 //   latent:  R = sum_k w_k Y[pos_k];  out = [Hs | R] [Ws_down | W_lat_up]^T
 // Nothing is read back to the host: the grouped GEMM grids are sized by
 // the worst case and tiles past the device-side tile count exit at once.
+// Weight GEMMs at prefill sizes use the register-fed WIDE tile when the
+// weights are packed (MOE_LAYOUT_FRAG16), the LDS tile otherwise.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -33,6 +35,7 @@ struct Plan {
     float scale;
     int64_t A;                                // assignments T*K
     DType dt;
+    bool packed;                              // weights in MOE_LAYOUT_FRAG16
     int64_t es;                               // element size
     // router
     TileCfg rcfg;
@@ -52,6 +55,9 @@ moe_status check_desc(const moe_layer_desc* D, bool forward) {
     if (!D) return MOE_ERR_NULL;
     if (D->act_dtype != MOE_F32 && D->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (forward && D->w_dtype != D->act_dtype) return MOE_ERR_UNSUPPORTED;
+    if (forward && D->w_layout != MOE_LAYOUT_ROWS &&
+        !(D->w_layout == MOE_LAYOUT_FRAG16 && D->w_dtype == MOE_BF16))
+        return MOE_ERR_UNSUPPORTED;
     if (D->T < 0 || D->E < 1 || D->E > 1024 || D->K < 1 || D->K > 16 || D->K > D->E) return MOE_ERR_SHAPE;
     if (D->d <= 0 || D->d % 64) return MOE_ERR_SHAPE;
     if (static_cast<int64_t>(D->T) * D->K >= (int64_t{1} << 31)) return MOE_ERR_SHAPE;
@@ -95,10 +101,13 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
     p.nsplit = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(16, ns)));
     p.ldz = static_cast<int>(up(p.E, 8));
 
-    // Experts: big M tiles once experts average 64 rows or more.
-    p.ecfg = (p.A >= 64ll * p.E && p.dt == DT_BF16) ? TILE_LARGE : TILE_SMALL;
+    // Experts: big M tiles once experts average 64 rows or more (the
+    // register-fed WIDE tile on packed weights, the LDS tile otherwise).
+    p.packed = forward && D->w_layout == MOE_LAYOUT_FRAG16;
+    const TileCfg big = p.packed ? TILE_WIDE : TILE_LARGE;
+    p.ecfg = (p.A >= 64ll * p.E && p.dt == DT_BF16) ? big : TILE_SMALL;
     p.bm = tile_bm(p.ecfg);
-    p.dcfg = (p.T >= 1024 && p.dt == DT_BF16) ? TILE_LARGE : TILE_SMALL;
+    p.dcfg = (p.T >= 1024 && p.dt == DT_BF16) ? big : TILE_SMALL;
     p.nch = static_cast<int>(cdiv(p.T, 64));
     p.max_tiles = static_cast<int>(cdiv(p.A, p.bm) + p.E + (p.ns ? cdiv(p.T, p.bm) : 0));
 
@@ -175,7 +184,7 @@ moe_status run_router(const Plan& p, const void* x, const float* W_r, const floa
     g.M = p.T;
     g.nsplit = p.nsplit;
     g.split_stride = static_cast<int64_t>(p.T) * p.ldz;
-    MOE_HIP(launch_gemm(g, p.dt, true, EPI_STORE, p.rcfg, p.rtiles, p.E, s));
+    MOE_HIP(launch_gemm(g, p.dt, true, EPI_STORE, p.rcfg, p.rtiles, p.E, false, s));
     if (counts_atomic) MOE_HIP(launch_fill_i32(counts_atomic, 0, p.E, s));
     MOE_HIP(launch_topk_gate(z, p.nsplit, g.split_stride, p.ldz, b, p.T, p.E, p.K, p.scale, idx, w,
                              counts_atomic, s));
@@ -224,7 +233,7 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
         g.g[0].ldc = p.dl;
         g.M = p.T;
         MOE_HIP(launch_gemm(g, p.dt, false, EPI_STORE, p.dcfg, static_cast<int>(cdiv(p.T, tile_bm(p.dcfg))), p.dl,
-                            s));
+                            p.packed, s));
         xin = xlat;
     }
     MOE_HIP(record(ev, MOE_EV_LATENT, s));
@@ -248,7 +257,7 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
         S1.ldc = p.Fsh;
         g.tiles = tiles;
         g.ntiles = ntiles;
-        MOE_HIP(launch_gemm(g, p.dt, false, EPI_SWIGLU, p.ecfg, p.max_tiles, std::max(p.F, p.Fsh), s));
+        MOE_HIP(launch_gemm(g, p.dt, false, EPI_SWIGLU, p.ecfg, p.max_tiles, std::max(p.F, p.Fsh), p.packed, s));
     }
     MOE_HIP(record(ev, MOE_EV_UP, s));
     // down projection: routed -> Y[sorted rows]; shared (K2 form) -> Y[A + t]
@@ -274,7 +283,7 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
         }
         g.tiles = tiles;
         g.ntiles = ntiles;
-        MOE_HIP(launch_gemm(g, p.dt, false, EPI_STORE, p.ecfg, p.max_tiles, p.din, s));
+        MOE_HIP(launch_gemm(g, p.dt, false, EPI_STORE, p.ecfg, p.max_tiles, p.din, p.packed, s));
     }
     MOE_HIP(record(ev, MOE_EV_DOWN, s));
     if (!latent) {
@@ -295,7 +304,8 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
     G.C = out;
     G.ldc = p.d;
     g.M = p.T;
-    MOE_HIP(launch_gemm(g, p.dt, false, EPI_STORE, p.dcfg, static_cast<int>(cdiv(p.T, tile_bm(p.dcfg))), p.d, s));
+    MOE_HIP(launch_gemm(g, p.dt, false, EPI_STORE, p.dcfg, static_cast<int>(cdiv(p.T, tile_bm(p.dcfg))), p.d,
+                        p.packed, s));
     MOE_HIP(record(ev, MOE_EV_END, s));
     return MOE_OK;
 }
@@ -374,6 +384,45 @@ moe_status moe_forward(const moe_layer_desc* desc, const void* x, const float* W
     if (workspace_bytes < static_cast<size_t>(p.total)) return MOE_ERR_WORKSPACE;
     return run_forward(p, x, W_r, b, W, out, topk_idx, topk_w, expert_counts, expert_offsets, sorted_token,
                        workspace, s, stage_events);
+}
+
+moe_status moe_pack_weights(const moe_layer_desc* desc, const moe_expert_weights* src,
+                            const moe_expert_weights* dst, void* stream) {
+    if (!desc || !src || !dst) return MOE_ERR_NULL;
+    moe_layer_desc D = *desc;
+    D.w_layout = MOE_LAYOUT_ROWS;  // the layout of src; dst gets FRAG16
+    moe_status st = check_desc(&D, true);
+    if (st != MOE_OK) return st;
+    if (D.w_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    const int din = D.d_latent ? D.d_latent : D.d, Fsh = D.n_shared * D.F_shared;
+    struct Mat {
+        const void* s;
+        const void* d;
+        int64_t count;
+        int rows, cols;
+    };
+    const Mat mats[] = {
+        {src->W_gate, dst->W_gate, D.E, D.F, din},     {src->W_up, dst->W_up, D.E, D.F, din},
+        {src->W_down, dst->W_down, D.E, din, D.F},     {src->Ws_gate, dst->Ws_gate, 1, Fsh, D.d},
+        {src->Ws_up, dst->Ws_up, 1, Fsh, D.d},         {src->Ws_down, dst->Ws_down, 1, D.d, Fsh},
+        {src->W_lat_down, dst->W_lat_down, 1, D.d_latent, D.d},
+        {src->W_lat_up, dst->W_lat_up, 1, D.d, D.d_latent},
+    };
+    for (const Mat& m : mats) {  // validate everything before enqueueing
+        if (!m.s) continue;
+        if (!m.d) return MOE_ERR_NULL;
+        if (!aligned16(m.s) || !aligned16(m.d)) return MOE_ERR_ALIGN;
+        if (m.rows <= 0 || m.cols <= 0) return MOE_ERR_SHAPE;
+        const uintptr_t bytes = static_cast<uintptr_t>(m.count) * m.rows * m.cols * 2;
+        const uintptr_t a = reinterpret_cast<uintptr_t>(m.s), b = reinterpret_cast<uintptr_t>(m.d);
+        if (a < b + bytes && b < a + bytes) return MOE_ERR_SHAPE;  // overlapping buffers
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (const Mat& m : mats)
+        if (m.s)
+            MOE_HIP(launch_pack_frag16(static_cast<const uint16_t*>(m.s), static_cast<uint16_t*>(const_cast<void*>(m.d)),
+                                       m.count, m.rows, m.cols, s));
+    return MOE_OK;
 }
 
 }  // extern "C"

@@ -299,60 +299,25 @@ __device__ __forceinline__ int swz(int row) {
     return ROWB == 128 ? (row & 7) : ((row >> 1) & 3);
 }
 
-// Workgroups per CU the LDS ring allows (two when a ring fits in 80 KiB).
-template <int BM, int BN, int NST, int ROWB>
-constexpr int big_occupancy() {
-    return NST * (BM + BN) * ROWB <= 81920 ? 2 : 1;
-}
+// Which (M tile, N tile) pair a block computes.  Blocks go to the eight
+// XCDs round robin (block b runs on XCD b % 8), so block b takes logical
+// slot (b % 8) * per + b / 8: each XCD walks one contiguous stretch of the
+// logical order.  That order is: runs of tiles that share weights (one
+// expert, or up to 8 dense row tiles), inside a run N tile by N tile with
+// the M tile fastest.  A run of `cnt` tiles starting at tile `first`
+// occupies slots [first*ntn, (first+cnt)*ntn), so slot / ntn names a tile of
+// the run that owns the slot.  Returns false for blocks without work.
+struct Job {
+    int gi, expert, row0, rows, n0;
+};
 
-template <typename TC, int BM, int BN, int WM, int WN, int NST, int ROWB, int EPI>
-__global__ __launch_bounds__(64 * WM * WN, (big_occupancy<BM, BN, NST, ROWB>())) void k_gemm_big(const GemmArgs a) {
-    using T = bf16_t;
-    constexpr int ES = 2;
-    static_assert(ROWB == 64 || ROWB == 128, "bytes of a row per stage");
-    constexpr int BKE = ROWB / ES;
-    constexpr int SLABS = ROWB / 64;           // 64-byte K slabs per stage
-    constexpr int CHUNKS = ROWB / 16;          // 16-byte chunks per row
-    constexpr int RPB = 1024 / ROWB;           // rows per 1 KiB block
-    constexpr int NW = WM * WN;               // waves per workgroup
-    constexpr int NT = 64 * NW;
-    constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int MB = TM / 16, NB = TN / 16;
-    constexpr int BNO = EPI == EPI_SWIGLU ? BN / 2 : BN;
-    constexpr int NA = BM / RPB, NBB = BN / RPB;  // 1 KiB blocks of A and of B per stage
-    // A blocks are split across the waves, or (fewer A blocks than waves,
-    // small row tiles) loaded by every wave: the copies carry identical
-    // bytes to identical LDS addresses.  B blocks are split across waves.
-    constexpr bool A_ALL = NA < NW;
-    constexpr int LPA = A_ALL ? NA : NA / NW;
-    constexpr int LPW = LPA + NBB / NW;  // 1 KiB blocks per wave per stage
-    constexpr int STAGE = (BM + BN) * ROWB;
-    // epilogue passes: the fp32 tile goes through LDS in NP column slices
-    constexpr int NP = (BM * (BNO + 4) * 4 <= NST * STAGE) ? 1
-                       : (BM * (BNO / 2 + 4) * 4 <= NST * STAGE) ? 2
-                       : (BM * (BNO / 4 + 4) * 4 <= NST * STAGE) ? 4 : 8;
-    constexpr int WP = BNO / NP;
-    constexpr int EP_STRIDE = WP + 4;
-    constexpr int LDS_BYTES = (NST * STAGE > BM * EP_STRIDE * 4) ? NST * STAGE : BM * EP_STRIDE * 4;
-    static_assert((NW == 4 || NW == 8) && BM % RPB == 0 && NBB % NW == 0 && (A_ALL || NA % NW == 0), "tile shape");
-    static_assert(EPI != EPI_SWIGLU || (NB % 2 == 0 && (TN / 2) % RPB == 0), "gate/up pairs per wave");
-    static_assert(NST >= 2 && LPW * (NST - 2) < 64, "pipeline depth");
-    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wid / WN, wn = wid % WN;
-
+template <int BM, int BNO>
+__device__ __forceinline__ bool pick_job(const GemmArgs& a, Job& jb) {
     const int total = (a.tiles ? *a.ntiles : (a.M + BM - 1) / BM) * a.ntn;  // active (M, N) tile pairs
     const int per = (total + 7) >> 3;
     const int slot = static_cast<int>(blockIdx.x) >> 3;
     const int lin = (static_cast<int>(blockIdx.x) & 7) * per + slot;
-    if (slot >= per || lin >= total) return;
-    // Logical order: runs of tiles that share weights (one expert, or up to
-    // 8 dense row tiles), inside a run N tile by N tile with the M tile
-    // fastest.  A run of `cnt` tiles starting at tile `first` occupies the
-    // logical slots [first*ntn, (first+cnt)*ntn), so lin / ntn names a tile
-    // of the run that owns slot lin.
+    if (slot >= per || lin >= total) return false;
     int first, cnt;
     if (a.tiles) {
         const TileInfo t0 = a.tiles[lin / a.ntn];
@@ -364,145 +329,37 @@ __global__ __launch_bounds__(64 * WM * WN, (big_occupancy<BM, BN, NST, ROWB>()))
         cnt = min(8, mtiles - first);
     }
     const int u = lin - first * a.ntn;
-    const int nt_n = u / cnt;
     const int mt = first + u % cnt;
-    int gi = 0, expert = 0, row0, rows;
+    jb.gi = 0;
+    jb.expert = 0;
     if (a.tiles) {
         const TileInfo ti = a.tiles[mt];
-        gi = ti.group;
-        expert = ti.expert;
-        row0 = ti.row0;
-        rows = ti.rows;
+        jb.gi = ti.group;
+        jb.expert = ti.expert;
+        jb.row0 = ti.row0;
+        jb.rows = ti.rows;
     } else {
-        row0 = mt * BM;
-        rows = min(BM, a.M - row0);
-        if (rows <= 0) return;
+        jb.row0 = mt * BM;
+        jb.rows = min(BM, a.M - jb.row0);
+        if (jb.rows <= 0) return false;
     }
-    const GemmGroup& G = gi ? a.g[1] : a.g[0];
+    jb.n0 = (u / cnt) * BNO;
+    return jb.n0 < (jb.gi ? a.g[1].N : a.g[0].N);
+}
+
+// Accumulators -> C.  Wave (wm, wn) holds output block rows wm*TM + 16 i +
+// 4 (lane / 16) + r, columns wn*TN + 16 j + lane % 16 (for SwiGLU, block
+// columns j < NB/2 are the gate and j + NB/2 the matching up columns, and
+// the output column is wn*TN/2 + 16 j + lane % 16).  The fp32 tile goes
+// through LDS in column passes of WP and leaves as 16-byte row stores.
+template <typename TC, int EPI, int BM, int BNO, int TM, int TN, int MB, int NB, int WP, int NT>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[MB][NB], char* lds, int wm, int wn, const GemmGroup& G,
+                                           TC* C, int row0, int rows, int n0) {
+    constexpr int NP = BNO / WP, EP_STRIDE = WP + 4, CPR = WP / 8;
+    static_assert(BNO % WP == 0 && WP % 8 == 0, "epilogue passes");
+    const int tid = threadIdx.x, lane = tid & 63;
     const int N = G.N;
-    const int n0 = nt_n * BNO;
-    if (n0 >= N) return;
-
-    int nk = 0;
-    for (int s = 0; s < G.nseg; ++s) nk += seg_of(G, s).K / BKE;
-    const int chunk = (nk + a.nsplit - 1) / a.nsplit;
-    const int kt0 = min(nk, static_cast<int>(blockIdx.z) * chunk);
-    const int kt1 = min(nk, kt0 + chunk);
-    const int nkt = kt1 - kt0;
-
-    // ---- this lane's source row in each block the wave loads.  Block q
-    // covers tile rows RPB q .. RPB q + RPB-1 (A rows first, then B rows);
-    // lane i fills LDS position (row i / CHUNKS, chunk i % CHUNKS), which
-    // holds logical chunk (i % CHUNKS) ^ swz(row).  blk(j) is the j-th block
-    // of this wave.
-    const int lrow = lane / CHUNKS;
-    const int lchunk16 = ((lane % CHUNKS) ^ swz<ROWB>(lrow)) * 16;
-    auto blk = [&](int j) { return j < LPA ? (A_ALL ? j : wid + NW * j) : NA + wid + NW * (j - LPA); };
-    int srow[LPW];
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-        const int r = blk(j) * RPB + lrow;
-        if (r < BM) {
-            const int p = row0 + (r < rows ? r : 0);
-            srow[j] = G.rowmap ? G.rowmap[p] : p;
-        } else {
-            const int qb = r - BM;
-            int n;
-            if (EPI == EPI_SWIGLU) {
-                const int blk = qb / TN, rq = qb % TN, half = TN / 2;
-                n = n0 + blk * half + (rq % half);
-            } else {
-                n = n0 + qb;
-            }
-            srow[j] = n < N ? n : N - 1;
-        }
-    }
-    // whether block q reads A, the gate or the up matrix depends on q alone
-    auto blk_is_a = [&](int j) { return j < LPA; };
-    auto blk_is_up = [&](int j) {
-        return EPI == EPI_SWIGLU && (((blk(j) * RPB - BM) % TN) >= TN / 2);
-    };
-    int cs = 0, ck = kt0;
-    while (cs + 1 < G.nseg && ck >= seg_of(G, cs).K / BKE) {
-        ck -= seg_of(G, cs).K / BKE;
-        ++cs;
-    }
-    const char *pA, *pB, *pBu;
-    int64_t lda, ldb;
-    auto set_seg = [&](int s) {
-        const GemmSeg& S = seg_of(G, s);
-        const int64_t eoff = s == 0 ? static_cast<int64_t>(expert) * G.b_estride * ES : 0;
-        pA = static_cast<const char*>(S.A) + lchunk16;
-        pB = static_cast<const char*>(S.B) + eoff + lchunk16;
-        pBu = static_cast<const char*>(S.Bu) + eoff + lchunk16;
-        lda = S.lda * ES;
-        ldb = S.ldb * ES;
-    };
-    set_seg(cs);
-    const uint32_t lds_base = static_cast<uint32_t>(
-        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(lds)));
-    auto issue = [&](int buf) {
-        const int64_t off = static_cast<int64_t>(ck) * ROWB;
-        const uint32_t dst = lds_base + buf * STAGE;
-#pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-            const bool isa = blk_is_a(j);
-            const char* base = isa ? pA : (blk_is_up(j) ? pBu : pB);
-            lds_dma16(base + static_cast<int64_t>(srow[j]) * (isa ? lda : ldb) + off, dst + blk(j) * 1024);
-        }
-        ++ck;
-        if (cs + 1 < G.nseg && ck == seg_of(G, cs).K / BKE) {
-            ++cs;
-            ck = 0;
-            set_seg(cs);
-        }
-    };
-
-    f32x4 acc[MB][NB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // fragment offsets inside a 16-row group for each 64-byte slab:
-    // row (lane & 15), logical chunk 4*slab + (lane >> 4), swizzled by row
-    const int frow = lane & 15;
-    const int fo0 = frow * ROWB + ((((lane >> 4) + 0) ^ swz<ROWB>(frow)) << 4);
-    const int fo1 = frow * ROWB + ((((lane >> 4) + 4) ^ swz<ROWB>(frow)) << 4);
-
-#pragma unroll
-    for (int s = 0; s < NST - 1; ++s)
-        if (s < nkt) issue(s);
-    for (int it = 0; it < nkt; ++it) {
-        if (it + NST - 2 < nkt)
-            wait_vmcnt<LPW * (NST - 2)>();  // the NST-2 newer stages may still be in flight
-        else
-            wait_vmcnt<0>();
-        __syncthreads();  // every wave's blocks of stage `it` have landed
-        if (it + NST - 1 < nkt) issue((it + NST - 1) % NST);  // reuses the stage read at it-1
-        const char* As = lds + (it % NST) * STAGE;
-        const char* Bs = As + BM * ROWB;
-#pragma unroll
-        for (int sl = 0; sl < SLABS; ++sl) {
-            const int fo = sl ? fo1 : fo0;
-            uint4 fa[MB], fb[NB];
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-                fa[i] = *reinterpret_cast<const uint4*>(As + (wm * TM + i * 16) * ROWB + fo);
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-                fb[j] = *reinterpret_cast<const uint4*>(Bs + (wn * TN + j * 16) * ROWB + fo);
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-#pragma unroll
-                for (int j = 0; j < NB; ++j) acc[i][j] = Mfma<T>::run(fa[i], fb[j], acc[i][j]);
-        }
-    }
-
-    // ---- epilogue: accumulators -> LDS (fp32, NP column passes) -> 16-byte stores
     float* ep = reinterpret_cast<float*>(lds);
-    constexpr int CPR = WP / 8;
-    TC* C = static_cast<TC*>(G.C) + static_cast<int64_t>(blockIdx.z) * a.split_stride;
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
         __syncthreads();
@@ -550,28 +407,403 @@ __global__ __launch_bounds__(64 * WM * WN, (big_occupancy<BM, BN, NST, ROWB>()))
     }
 }
 
+// Workgroups per CU the LDS ring allows (two when a ring fits in 80 KiB).
+template <int BM, int BN, int NST, int ROWB>
+constexpr int big_occupancy() {
+    return NST * (BM + BN) * ROWB <= 81920 ? 2 : 1;
+}
+
+template <typename TC, int BM, int BN, int WM, int WN, int NST, int ROWB, int EPI, bool PK>
+__global__ __launch_bounds__(64 * WM * WN, (big_occupancy<BM, BN, NST, ROWB>())) void k_gemm_big(const GemmArgs a) {
+    using T = bf16_t;
+    constexpr int ES = 2;
+    static_assert(ROWB == 64 || ROWB == 128, "bytes of a row per stage");
+    constexpr int BKE = ROWB / ES;
+    constexpr int SLABS = ROWB / 64;           // 64-byte K slabs per stage
+    constexpr int CHUNKS = ROWB / 16;          // 16-byte chunks per row
+    constexpr int RPB = 1024 / ROWB;           // rows per 1 KiB block
+    constexpr int NW = WM * WN;               // waves per workgroup
+    constexpr int NT = 64 * NW;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int MB = TM / 16, NB = TN / 16;
+    constexpr int BNO = EPI == EPI_SWIGLU ? BN / 2 : BN;
+    constexpr int NA = BM / RPB, NBB = BN / RPB;  // 1 KiB blocks of A and of B per stage
+    // A blocks are split across the waves, or (fewer A blocks than waves,
+    // small row tiles) loaded by every wave: the copies carry identical
+    // bytes to identical LDS addresses.  B blocks are split across waves.
+    constexpr bool A_ALL = NA < NW;
+    constexpr int LPA = A_ALL ? NA : NA / NW;
+    constexpr int LPW = LPA + NBB / NW;  // 1 KiB blocks per wave per stage
+    constexpr int STAGE = (BM + BN) * ROWB;
+    // epilogue passes: the fp32 tile goes through LDS in NP column slices
+    constexpr int NP = (BM * (BNO + 4) * 4 <= NST * STAGE) ? 1
+                       : (BM * (BNO / 2 + 4) * 4 <= NST * STAGE) ? 2
+                       : (BM * (BNO / 4 + 4) * 4 <= NST * STAGE) ? 4 : 8;
+    constexpr int WP = BNO / NP;
+    constexpr int EP_STRIDE = WP + 4;
+    constexpr int LDS_BYTES = (NST * STAGE > BM * EP_STRIDE * 4) ? NST * STAGE : BM * EP_STRIDE * 4;
+    static_assert((NW == 4 || NW == 8) && BM % RPB == 0 && NBB % NW == 0 && (A_ALL || NA % NW == 0), "tile shape");
+    static_assert(EPI != EPI_SWIGLU || (NB % 2 == 0 && (TN / 2) % RPB == 0), "gate/up pairs per wave");
+    static_assert(NST >= 2 && LPW * (NST - 2) < 64, "pipeline depth");
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid / WN, wn = wid % WN;
+
+    Job jb;
+    if (!pick_job<BM, BNO>(a, jb)) return;
+    const int expert = jb.expert, row0 = jb.row0, rows = jb.rows, n0 = jb.n0;
+    const GemmGroup& G = jb.gi ? a.g[1] : a.g[0];
+    const int N = G.N;
+
+    int nk = 0;
+    for (int s = 0; s < G.nseg; ++s) nk += seg_of(G, s).K / BKE;
+    const int chunk = (nk + a.nsplit - 1) / a.nsplit;
+    const int kt0 = min(nk, static_cast<int>(blockIdx.z) * chunk);
+    const int kt1 = min(nk, kt0 + chunk);
+    const int nkt = kt1 - kt0;
+
+    // ---- this lane's source row in each block the wave loads.  Block q
+    // covers tile rows RPB q .. RPB q + RPB-1 (A rows first, then B rows);
+    // lane i fills LDS position (row i / CHUNKS, chunk i % CHUNKS), which
+    // holds logical chunk (i % CHUNKS) ^ swz(row).  blk(j) is the j-th block
+    // of this wave.  Packed weights (PK): B block q' = q - NA is the
+    // 16-row x 32-K fragment block (row block q' / SLABS, slab q' % SLABS),
+    // 1 KiB stored contiguously in lane order; srow holds its row block.
+    const int lrow = lane / CHUNKS;
+    const int lchunk16 = ((lane % CHUNKS) ^ swz<ROWB>(lrow)) * 16;
+    auto blk = [&](int j) { return j < LPA ? (A_ALL ? j : wid + NW * j) : NA + wid + NW * (j - LPA); };
+    int srow[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+        const int r = blk(j) * RPB + lrow;
+        if (j < LPA) {
+            const int p = row0 + (r < rows ? r : 0);
+            srow[j] = G.rowmap ? G.rowmap[p] : p;
+        } else if (PK) {
+            const int rb = (blk(j) - NA) / SLABS;  // row block inside the B tile
+            int nb;
+            if (EPI == EPI_SWIGLU) {
+                const int per = TN / 16, half = TN / 32;
+                nb = n0 / 16 + (rb / per) * half + (rb % per) % half;
+            } else {
+                nb = n0 / 16 + rb;
+            }
+            srow[j] = nb < N / 16 ? nb : N / 16 - 1;
+        } else {
+            const int qb = r - BM;
+            int n;
+            if (EPI == EPI_SWIGLU) {
+                const int blk = qb / TN, rq = qb % TN, half = TN / 2;
+                n = n0 + blk * half + (rq % half);
+            } else {
+                n = n0 + qb;
+            }
+            srow[j] = n < N ? n : N - 1;
+        }
+    }
+    // whether block q reads A, the gate or the up matrix depends on q alone
+    auto blk_is_a = [&](int j) { return j < LPA; };
+    auto blk_is_up = [&](int j) {
+        if (PK) return EPI == EPI_SWIGLU && ((blk(j) - NA) / SLABS) % (TN / 16) >= TN / 32;
+        return EPI == EPI_SWIGLU && (((blk(j) * RPB - BM) % TN) >= TN / 2);
+    };
+    auto blk_slab = [&](int j) { return (blk(j) - NA) % SLABS; };
+    int cs = 0, ck = kt0;
+    while (cs + 1 < G.nseg && ck >= seg_of(G, cs).K / BKE) {
+        ck -= seg_of(G, cs).K / BKE;
+        ++cs;
+    }
+    const char *pA, *pB, *pBu;
+    int64_t lda, ldb;  // packed weights: ldb = bytes per row block (K / 32 fragment blocks)
+    auto set_seg = [&](int s) {
+        const GemmSeg& S = seg_of(G, s);
+        const int64_t eoff = s == 0 ? static_cast<int64_t>(expert) * G.b_estride * ES : 0;
+        const int bl = PK ? lane * 16 : lchunk16;
+        pA = static_cast<const char*>(S.A) + lchunk16;
+        pB = static_cast<const char*>(S.B) + eoff + bl;
+        pBu = static_cast<const char*>(S.Bu) + eoff + bl;
+        lda = S.lda * ES;
+        ldb = PK ? static_cast<int64_t>(S.K) * 32 : S.ldb * ES;
+    };
+    set_seg(cs);
+    const uint32_t lds_base = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(lds)));
+    auto issue = [&](int buf) {
+        const int64_t off = static_cast<int64_t>(ck) * ROWB;
+        const uint32_t dst = lds_base + buf * STAGE;
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const bool isa = blk_is_a(j);
+            const char* base = isa ? pA : (blk_is_up(j) ? pBu : pB);
+            const int64_t koff = (PK && !isa) ? (static_cast<int64_t>(ck) * SLABS + blk_slab(j)) * 1024 : off;
+            lds_dma16(base + static_cast<int64_t>(srow[j]) * (isa ? lda : ldb) + koff, dst + blk(j) * 1024);
+        }
+        ++ck;
+        if (cs + 1 < G.nseg && ck == seg_of(G, cs).K / BKE) {
+            ++cs;
+            ck = 0;
+            set_seg(cs);
+        }
+    };
+
+    f32x4 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // fragment offsets inside a 16-row group for each 64-byte slab:
+    // row (lane & 15), logical chunk 4*slab + (lane >> 4), swizzled by row
+    const int frow = lane & 15;
+    const int fo0 = frow * ROWB + ((((lane >> 4) + 0) ^ swz<ROWB>(frow)) << 4);
+    const int fo1 = frow * ROWB + ((((lane >> 4) + 4) ^ swz<ROWB>(frow)) << 4);
+
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+        if (s < nkt) issue(s);
+    for (int it = 0; it < nkt; ++it) {
+        if (it + NST - 2 < nkt)
+            wait_vmcnt<LPW * (NST - 2)>();  // the NST-2 newer stages may still be in flight
+        else
+            wait_vmcnt<0>();
+        __syncthreads();  // every wave's blocks of stage `it` have landed
+        if (it + NST - 1 < nkt) issue((it + NST - 1) % NST);  // reuses the stage read at it-1
+        const char* As = lds + (it % NST) * STAGE;
+        const char* Bs = As + BM * ROWB;
+#pragma unroll
+        for (int sl = 0; sl < SLABS; ++sl) {
+            const int fo = sl ? fo1 : fo0;
+            uint4 fa[MB], fb[NB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                fa[i] = *reinterpret_cast<const uint4*>(As + (wm * TM + i * 16) * ROWB + fo);
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                fb[j] = PK ? *reinterpret_cast<const uint4*>(Bs + ((wn * TN / 16 + j) * SLABS + sl) * 1024 + lane * 16)
+                           : *reinterpret_cast<const uint4*>(Bs + (wn * TN + j * 16) * ROWB + fo);
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j) acc[i][j] = Mfma<T>::run(fa[i], fb[j], acc[i][j]);
+        }
+    }
+
+    // ---- epilogue
+    TC* C = static_cast<TC*>(G.C) + static_cast<int64_t>(blockIdx.z) * a.split_stride;
+    store_tile<TC, EPI, BM, BNO, TM, TN, MB, NB, WP, NT>(acc, lds, wm, wn, G, C, row0, rows, n0);
+}
+
+// Prefill tile for packed weights: 128 A rows x 512 B rows per workgroup
+// of four waves; wave w owns B rows [128 w, 128 w + 128), a 128 x 128
+// output block held in 64 accumulators of 16x16.  Only A is shared between
+// the waves, so only A goes through LDS (DMA into a ring of three 64-K
+// slots).  Each wave loads its own B fragments from global memory straight
+// into registers one stage ahead, a fragment being reloaded with the next
+// stage as soon as its last MFMA of this stage has issued.  In the packed
+// layout a fragment (16 rows x 32 K) is one contiguous KiB in lane order, so
+// each of these loads reads eight whole 128-byte lines: the vector memory
+// path on gfx950 is limited by the lines an instruction touches, and a
+// row-major fragment (16 rows x 64 bytes) touches twice as many.
+//
+// NSEG K segments (1, or 2 for a sum of two products).  Memory operations
+// per stage and lane, in issue order: NAB A DMA loads for stage it + 2
+// (after the barrier), then the 2 NB B loads of stage it + 1 among the
+// MFMAs; the prologue issues A(0), A(1), B(0).  Every stage issues the same
+// loads (past the last stage they re-read it), so from the second stage on
+// the loads younger than A(it) are the 2 NB of its own iteration plus one
+// full iteration, a compile-time count; the first stage (younger: A(1) and
+// B(0)) is peeled with its own count.
+template <typename TC, int EPI, int NSEG>
+__global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
+    using T = bf16_t;
+    constexpr int ES = 2, BM = 128, BN = 512, NW = 4, TN = BN / NW;
+    constexpr int MB = BM / 16, NB = TN / 16;
+    constexpr int ROWB = 128, BKE = ROWB / ES;  // a stage is 64 K = two 32-K slabs
+    constexpr int NST = 3;                     // A slots: it (read), it+1 (landing), it+2 (issued)
+    constexpr int STAGE = BM * ROWB;
+    constexpr int BNO = EPI == EPI_SWIGLU ? BN / 2 : BN;
+    constexpr int NAB = STAGE / 1024 / NW;  // 1 KiB A blocks per wave per stage
+    constexpr int LOADS = NAB + 2 * NB;     // vector loads per lane per stage
+    constexpr int kWaitA = 2 * NB + LOADS, kWaitA0 = NAB + 2 * NB;
+    static_assert(kWaitA < 64 && (NSEG == 1 || NSEG == 2), "vmcnt range; segments");
+    constexpr int WP = 256;
+    constexpr int EP_BYTES = BM * (WP + 4) * 4;
+    constexpr int LDS_BYTES = NST * STAGE > EP_BYTES ? NST * STAGE : EP_BYTES;
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+
+    Job jb;
+    if (!pick_job<BM, BNO>(a, jb)) return;
+    const GemmGroup& G = jb.gi ? a.g[1] : a.g[0];
+    const int N = G.N, row0 = jb.row0, rows = jb.rows, n0 = jb.n0;
+    const int nk0 = G.seg[0].K / BKE;
+    const int nkt = nk0 + (NSEG == 2 ? G.seg[1].K / BKE : 0);  // >= 1
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // A: block q of a stage holds tile rows 8q .. 8q+7 (128 bytes each, the
+    // 16-byte chunk c of row r at position c ^ (r & 7)); lane i fills row
+    // 8q + i/8, position i%8.  This wave loads blocks wid + NW j.
+    const int achunk = ((lane & 7) ^ (lane >> 3)) << 4;
+    int arow[NAB];
+#pragma unroll
+    for (int j = 0; j < NAB; ++j) {
+        const int r = (wid + NW * j) * 8 + (lane >> 3);
+        const int p = row0 + (r < rows ? r : 0);
+        arow[j] = G.rowmap ? G.rowmap[p] : p;
+    }
+    const char* asrc[NAB];  // segment 0 row addresses
+#pragma unroll
+    for (int j = 0; j < NAB; ++j)
+        asrc[j] = static_cast<const char*>(G.seg[0].A) + static_cast<int64_t>(arow[j]) * G.seg[0].lda * ES + achunk;
+    const uint32_t lds_base = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(lds)));
+    auto issue_a = [&](int kt, int slot) {
+        const uint32_t dst = lds_base + slot * STAGE;
+        if (NSEG == 1) {
+#pragma unroll
+            for (int j = 0; j < NAB; ++j) lds_dma16(asrc[j] + kt * ROWB, dst + (wid + NW * j) * 1024);
+        } else {
+            const bool s1 = kt >= nk0;
+            const GemmSeg& S = s1 ? G.seg[1] : G.seg[0];
+            const char* base = static_cast<const char*>(S.A) + (kt - (s1 ? nk0 : 0)) * ROWB + achunk;
+            const int64_t lda = S.lda * ES;
+#pragma unroll
+            for (int j = 0; j < NAB; ++j) lds_dma16(base + arow[j] * lda, dst + (wid + NW * j) * 1024);
+        }
+    };
+
+    // B: fragment j of this wave is row block rb[j] (16 rows); for SwiGLU,
+    // j < NB/2 are gate row blocks and j + NB/2 the same blocks of the up
+    // matrix.  Fragment block (row block r, slab k) of a [rows, K] matrix
+    // sits at byte (r (K/32) + k) 1024; lane l reads its 16 bytes at 16 l.
+    int rb[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int nb = EPI == EPI_SWIGLU ? (n0 + wid * (TN / 2)) / 16 + j % (NB / 2) : (n0 + wid * TN) / 16 + j;
+        rb[j] = nb < N / 16 ? nb : N / 16 - 1;
+    }
+    const int64_t eoff = static_cast<int64_t>(jb.expert) * G.b_estride * ES;  // segment 0 only
+    auto load_b = [&](int kt, int sl, int j) {
+        const bool s1 = NSEG == 2 && kt >= nk0;
+        const GemmSeg& S = s1 ? G.seg[1] : G.seg[0];
+        const char* m = static_cast<const char*>((EPI == EPI_SWIGLU && j >= NB / 2) ? S.Bu : S.B) + (s1 ? 0 : eoff);
+        const uint32_t blk = static_cast<uint32_t>(rb[j]) * static_cast<uint32_t>(S.K / 32) +
+                             static_cast<uint32_t>((kt - (s1 ? nk0 : 0)) * 2 + sl);
+        return *reinterpret_cast<const uint4*>(m + blk * 1024u + lane * 16);
+    };
+
+    f32x4 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // A fragment of a slab: row (lane & 15), logical chunk 4 slab + lane/16
+    const int frow = lane & 15;
+    const int fo0 = frow * ROWB + ((((lane >> 4) + 0) ^ (frow & 7)) << 4);
+    const int fo1 = frow * ROWB + ((((lane >> 4) + 4) ^ (frow & 7)) << 4);
+
+    uint4 fb[2][NB];  // B fragments of the current stage, refilled with the next
+    // one K stage: wait for its A, compute it from LDS A and register B
+    auto step = [&](int it, auto wait_a) {
+        wait_a();
+        __syncthreads();  // A(it) of every wave has landed; slot (it+2)%3 is free
+        issue_a(min(it + 2, nkt - 1), (it + 2) % NST);
+        const int kb = min(it + 1, nkt - 1);
+        const char* As = lds + (it % NST) * STAGE;
+        uint4 fa[2][MB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) fa[0][i] = *reinterpret_cast<const uint4*>(As + i * 16 * ROWB + fo0);
+        // The order below is the schedule: a B fragment is reloaded right
+        // after its last MFMA of the stage (the scheduler would otherwise
+        // sink the loads to the next use and expose their latency), and the
+        // second slab's A fragments are read while the first slab computes.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+#pragma unroll
+                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa[sl][i], fb[sl][j], acc[i][j]);
+                fb[sl][j] = load_b(kb, sl, j);
+                if (sl == 0 && j == 1) {
+#pragma unroll
+                    for (int i = 0; i < MB; ++i)
+                        fa[1][i] = *reinterpret_cast<const uint4*>(As + i * 16 * ROWB + fo1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    issue_a(0, 0);
+    issue_a(min(1, nkt - 1), 1);
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) fb[sl][j] = load_b(0, sl, j);
+    step(0, [] { wait_vmcnt<kWaitA0>(); });
+    for (int it = 1; it < nkt; ++it) step(it, [] { wait_vmcnt<kWaitA>(); });
+    wait_vmcnt<0>();  // no DMA may land in LDS once the epilogue reuses it
+
+    store_tile<TC, EPI, BM, BNO, BM, TN, MB, NB, WP, 256>(acc, lds, 0, wid, G, static_cast<TC*>(G.C), row0, rows,
+                                                          n0);
+}
+
 // fp32 operands: register-staged 16 x 256 tiles
 constexpr int kF32BN = 256;
 // decode tile (few rows per expert): 16 x 512, two stages of 128-byte row pieces
 constexpr int kSmBM = 16, kSmBN = 512, kSmWM = 1, kSmWN = 4, kSmNST = 2, kSmROWB = 128;
 // prefill tile: BM x BN (B rows), waves WM x WN, NST LDS stages
 constexpr int kBigBM = 128, kBigBN = 256, kBigWM = 2, kBigWN = 2, kBigNST = 3, kBigROWB = 64;
+// prefill expert tile with register-fed weights: 128 x 512
+constexpr int kWideBM = 128, kWideBN = 512;
 
 }  // namespace
 
 static_assert(kSmBM == 16, "fp32 small tiles share the 16-row M tiling");
+static_assert(kBigBM == kWideBM, "prefill tiles share the tile table's 128-row M tiling");
 int tile_bm(TileCfg cfg) { return cfg == TILE_SMALL ? kSmBM : kBigBM; }
 int tile_bn_out(TileCfg cfg, Epi epi) {  // bf16 kernels (sizing heuristics only)
-    const int bn = cfg == TILE_SMALL ? kSmBN : kBigBN;  // B rows (gate + up rows for SwiGLU)
+    // B rows per N tile (gate + up rows for SwiGLU)
+    const int bn = cfg == TILE_SMALL ? kSmBN : (cfg == TILE_WIDE ? kWideBN : kBigBN);
     return epi == EPI_SWIGLU ? bn / 2 : bn;
 }
 
 namespace {
 
+// What the wide kernel handles: packed weights, one or two K segments per
+// group (multiples of 64), no split K, fragment-block byte offsets in 31 bits.
+bool wide_fits(const GemmArgs& a) {
+    if (a.nsplit != 1) return false;
+    for (int g = 0; g < 2; ++g) {
+        const GemmGroup& G = a.g[g];
+        if (G.N == 0) continue;
+        if (G.nseg < 1 || G.nseg > 2 || G.N % 16 != 0) return false;
+        for (int s = 0; s < G.nseg; ++s)
+            if (G.seg[s].K < 64 || G.seg[s].K % 64 != 0 ||
+                static_cast<int64_t>(G.N) * G.seg[s].K * 2 >= (int64_t{1} << 31))
+                return false;
+    }
+    return true;
+}
+
+int max_nseg(const GemmArgs& a) {
+    return a.g[0].nseg > a.g[1].nseg ? a.g[0].nseg : a.g[1].nseg;
+}
+
 template <typename T, typename TC, int EPI>
-hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n, hipStream_t stream) {
+hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n, bool packed, hipStream_t stream) {
+    if constexpr (sizeof(T) == 4) {
+        if (packed || cfg != TILE_SMALL) return hipErrorInvalidValue;  // fp32 runs the small tiles only
+    }
+    if (cfg == TILE_WIDE && !(packed && wide_fits(args))) cfg = TILE_LARGE;
     // output columns per N tile of the kernel actually launched
-    const int bn = sizeof(T) == 4 ? kF32BN : (cfg == TILE_SMALL ? kSmBN : kBigBN);
+    const int bn = sizeof(T) == 4 ? kF32BN
+                   : (cfg == TILE_SMALL ? kSmBN : (cfg == TILE_WIDE ? kWideBN : kBigBN));
     const int bno = EPI == EPI_SWIGLU ? bn / 2 : bn;
     GemmArgs a = args;
     a.ntn = (max_n + bno - 1) / bno;
@@ -582,30 +814,47 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
     const unsigned blocks = static_cast<unsigned>(max_tiles) * a.ntn;
     dim3 grid((blocks + 7u) & ~7u, 1, a.nsplit);
     if constexpr (sizeof(T) == 4) {
-        // fp32 operands (small parity workloads): register-staged template
-        if (cfg != TILE_SMALL) return hipErrorInvalidValue;
         hipLaunchKernelGGL((k_gemm<T, TC, 16, kF32BN, 1, 4, EPI>), grid, dim3(256), 0, stream, a);
-    } else if (cfg == TILE_SMALL)
-        hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, kSmNST, kSmROWB, EPI>), grid, dim3(64 * kSmWM * kSmWN), 0, stream, a);
-    else if constexpr (sizeof(T) == 2)
-        hipLaunchKernelGGL((k_gemm_big<TC, kBigBM, kBigBN, kBigWM, kBigWN, kBigNST, kBigROWB, EPI>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, a);
-    else
-        return hipErrorInvalidValue;  // fp32 runs the small tiles only
+    } else {
+        if (cfg == TILE_WIDE) {
+            if (max_nseg(a) == 1)
+                hipLaunchKernelGGL((k_gemm_wide<TC, EPI, 1>), grid, dim3(256), 0, stream, a);
+            else
+                hipLaunchKernelGGL((k_gemm_wide<TC, EPI, 2>), grid, dim3(256), 0, stream, a);
+        } else if (cfg == TILE_SMALL) {
+            if (packed)
+                hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, kSmNST, kSmROWB, EPI, true>), grid,
+                                   dim3(64 * kSmWM * kSmWN), 0, stream, a);
+            else
+                hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, kSmNST, kSmROWB, EPI, false>), grid,
+                                   dim3(64 * kSmWM * kSmWN), 0, stream, a);
+        } else {
+            if (packed)
+                hipLaunchKernelGGL((k_gemm_big<TC, kBigBM, kBigBN, kBigWM, kBigWN, kBigNST, kBigROWB, EPI, true>), grid,
+                                   dim3(64 * kBigWM * kBigWN), 0, stream, a);
+            else
+                hipLaunchKernelGGL((k_gemm_big<TC, kBigBM, kBigBN, kBigWM, kBigWN, kBigNST, kBigROWB, EPI, false>),
+                                   grid, dim3(64 * kBigWM * kBigWN), 0, stream, a);
+        }
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& args, DType dt, bool out_f32, Epi epi, TileCfg cfg, int max_tiles,
-                       int max_n, hipStream_t stream) {
+                       int max_n, bool packed, hipStream_t stream) {
     if (max_tiles <= 0 || max_n <= 0) return hipSuccess;
     if (dt == DT_F32) {
-        if (epi == EPI_SWIGLU) return launch_t<float, float, EPI_SWIGLU>(args, cfg, max_tiles, max_n, stream);
-        return launch_t<float, float, EPI_STORE>(args, cfg, max_tiles, max_n, stream);
+        if (epi == EPI_SWIGLU) return launch_t<float, float, EPI_SWIGLU>(args, cfg, max_tiles, max_n, packed, stream);
+        return launch_t<float, float, EPI_STORE>(args, cfg, max_tiles, max_n, packed, stream);
     }
-    if (out_f32) return launch_t<bf16_t, float, EPI_STORE>(args, cfg, max_tiles, max_n, stream);
-    if (epi == EPI_SWIGLU) return launch_t<bf16_t, bf16_t, EPI_SWIGLU>(args, cfg, max_tiles, max_n, stream);
-    return launch_t<bf16_t, bf16_t, EPI_STORE>(args, cfg, max_tiles, max_n, stream);
+    if (out_f32) {
+        if (packed) return hipErrorInvalidValue;  // fp32 output: the router, on row-major planes
+        return launch_t<bf16_t, float, EPI_STORE>(args, cfg, max_tiles, max_n, false, stream);
+    }
+    if (epi == EPI_SWIGLU) return launch_t<bf16_t, bf16_t, EPI_SWIGLU>(args, cfg, max_tiles, max_n, packed, stream);
+    return launch_t<bf16_t, bf16_t, EPI_STORE>(args, cfg, max_tiles, max_n, packed, stream);
 }
 
 }  // namespace moe

@@ -10,8 +10,10 @@ namespace moe {
 enum DType { DT_F32 = 0, DT_BF16 = 1 };
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1 };
 // Tile shapes of the grouped GEMM: SMALL streams weights for a few rows
-// per expert (decode-sized batches), LARGE is the MFMA-bound prefill tile.
-enum TileCfg { TILE_SMALL = 0, TILE_LARGE = 1 };
+// per expert (decode-sized batches); LARGE (128 x 256, both operands through
+// LDS) and WIDE (128 x 512, weights fed to registers) are the prefill tiles.
+// All bf16 prefill tiles are 128 rows, so one tile table serves both.
+enum TileCfg { TILE_SMALL = 0, TILE_LARGE = 1, TILE_WIDE = 2 };
 
 int tile_bm(TileCfg cfg);         // rows per M tile
 int tile_bn_out(TileCfg cfg, Epi epi);  // output columns per N tile
@@ -64,9 +66,16 @@ struct GemmArgs {
 // Launch C = epi(A * B^T) for element type `dt`; `out_f32` selects an fp32
 // output (the router logits) instead of the element type.  `max_tiles` is
 // the grid's M extent (upper bound of the device tile count when grouped).
+// `packed`: every B is in the fragment-block layout of moe_pack_weights
+// (bf16 only); WIDE tiles need it and fall back to LARGE without it.
 hipError_t launch_gemm(const GemmArgs& args, DType dt, bool out_f32, Epi epi,
-                       TileCfg cfg, int max_tiles, int max_n,
+                       TileCfg cfg, int max_tiles, int max_n, bool packed,
                        hipStream_t stream);
+
+// Row-major [rows, cols] bf16 matrices (count of them, consecutive) -> the
+// fragment-block layout: block (rows/16) x (cols/32) of 1 KiB each.
+hipError_t launch_pack_frag16(const uint16_t* src, uint16_t* dst, int64_t count, int rows, int cols,
+                              hipStream_t stream);
 
 // W_r (fp32) -> three bf16 planes with hi + mid + lo == W_r exactly.
 hipError_t launch_split3(const float* W, int64_t n, uint16_t* hi,

@@ -75,7 +75,22 @@ typedef struct {
     int32_t act_dtype; /* moe_dtype of x, out and the intermediates           */
     int32_t w_dtype;   /* moe_dtype of expert, shared and latent weights;     */
                        /* must equal act_dtype (W_r and b are always fp32)    */
+    int32_t w_layout;  /* moe_weight_layout of those weights (bf16 may be     */
+                       /* MOE_LAYOUT_FRAG16; fp32 must be MOE_LAYOUT_ROWS)    */
 } moe_layer_desc;
+
+/* Storage of the expert, shared and latent weight matrices.
+ *   MOE_LAYOUT_ROWS: row-major [rows, cols] (nn.Linear [out, in]).
+ *   MOE_LAYOUT_FRAG16 (bf16 only): each [rows, cols] matrix as
+ *     (rows/16) x (cols/32) blocks of 16 rows x 32 columns, block (i, j) at
+ *     element offset (i * (cols/32) + j) * 512; inside a block, element
+ *     (r, c) at ((c / 8) * 16 + r) * 8 + c % 8.  A block is then exactly
+ *     the B operand of one v_mfma_f32_16x16x32_bf16 in lane order (lane l
+ *     holds row l % 16, columns 8 (l / 16) .. 8 (l / 16) + 7), so the GEMMs
+ *     read weights as whole 1 KiB blocks.  Stacked matrices (W_gate etc.)
+ *     keep their per-expert stride rows * cols; the sizes of all buffers
+ *     are those of the row-major layout.  moe_pack_weights converts.       */
+typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_FRAG16 = 1 } moe_weight_layout;
 
 /* Expert weights, nn.Linear layout [out, in]; d_in = d_latent ? d_latent : d.
  *   W_gate, W_up [E, F, d_in];  W_down [E, d_in, F]
@@ -140,6 +155,16 @@ moe_status moe_forward(const moe_layer_desc *desc, const void *x,
                        int32_t *sorted_token, void *workspace,
                        size_t workspace_bytes, void *stream,
                        void *const *stage_events);
+
+/* Rewrite row-major bf16 weights into MOE_LAYOUT_FRAG16 (a pure
+ * permutation of each matrix; done once, e.g. when a model is loaded).
+ * Every non-NULL matrix of `src` (row-major, shapes from `desc`, whose
+ * w_layout is ignored) is written to the same member of `dst`, which must
+ * then be non-NULL, 16-byte aligned, of the same size and not overlap it.
+ * Requires w_dtype == MOE_BF16.  Enqueued on `stream` like the other calls. */
+moe_status moe_pack_weights(const moe_layer_desc *desc,
+                            const moe_expert_weights *src,
+                            const moe_expert_weights *dst, void *stream);
 
 /* Static text for a status code.                                            */
 const char *moe_status_str(moe_status status);

@@ -91,3 +91,14 @@ def weights_to_device(inp, device):
 def expert_weights(inp):
     return {k: inp.get(k) for k in ("W_gate", "W_up", "W_down", "Ws_gate", "Ws_up",
                                     "Ws_down", "W_lat_down", "W_lat_up")}
+
+
+def frag16_reference(w):
+    """include/moe.h MOE_LAYOUT_FRAG16 of [..., R, C] as a reshape/permute:
+    block (i, j) of 16 rows x 32 columns at element (i * C/32 + j) * 512,
+    element (r, c) of a block at ((c / 8) * 16 + r) * 8 + c % 8."""
+    *lead, R, C = w.shape
+    v = w.reshape(*lead, R // 16, 16, C // 32, 4, 8)
+    n = len(lead)
+    perm = list(range(n)) + [n + 0, n + 2, n + 3, n + 1, n + 4]   # (i, j, c/8, r, c%8)
+    return v.permute(*perm).reshape(w.shape)

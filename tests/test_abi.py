@@ -30,7 +30,7 @@ def _declared():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == sorted(["moe_forward", "moe_router", "moe_status_str",
+    assert _declared() == sorted(["moe_forward", "moe_pack_weights", "moe_router", "moe_status_str",
                                   "moe_workspace_size"])
 
 
@@ -123,6 +123,32 @@ def test_forward_rejects_bad_arguments():
     assert _forward(_k2(w_dtype=moe.MOE_F32)) == UNSUP
     assert _forward(_k2(F=2000)) == SHAPE
     assert _forward(_k2(n_shared=1, F_shared=0)) == SHAPE
+    # the packed layout is bf16-only; unknown layouts are refused
+    assert _forward(_k2(act_dtype=moe.MOE_F32, w_layout=moe.MOE_LAYOUT_FRAG16)) == UNSUP
+    assert _forward(_k2(w_layout=7)) == UNSUP
+    assert _forward(_k2(w_layout=moe.MOE_LAYOUT_FRAG16), out=None) == NULL
+
+
+def _pack(D, src, dst):
+    return moe.lib().moe_pack_weights(None if D is None else ctypes.byref(D),
+                                      None if src is None else ctypes.byref(src),
+                                      None if dst is None else ctypes.byref(dst), None)
+
+
+def test_pack_weights_rejects_bad_arguments():
+    D = _k2()
+    W = lambda *p: moe.ExpertWeights(*p)  # noqa: E731
+    far = FAKE + (1 << 40)                 # a second fake region, far from the first
+    src = W(FAKE, None, None, None, None, None, None, None)
+    assert _pack(None, src, src) == NULL
+    assert _pack(D, None, src) == NULL
+    # a source matrix needs a destination
+    assert _pack(D, src, W(None, far, None, None, None, None, None, None)) == NULL
+    assert _pack(D, src, W(far + 8, None, None, None, None, None, None, None)) == ALIGN
+    # in place / overlapping buffers
+    assert _pack(D, src, W(FAKE + 4096, None, None, None, None, None, None, None)) == SHAPE
+    assert _pack(_k2(act_dtype=moe.MOE_F32), src, W(far, None, None, None, None, None, None, None)) == UNSUP
+    assert _pack(_k2(F=100), src, W(far, None, None, None, None, None, None, None)) == SHAPE
 
 
 def test_zero_tokens_accepts_null_data_pointers():

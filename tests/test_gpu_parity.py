@@ -29,18 +29,25 @@ def _custom(**kw):
     return Workload(**base)
 
 
-def _run_forward(wl, dev, **kw):
-    out, r = moe.forward(dev["x"], dev["W_r"], dev["b"], expert_weights(dev), wl.K, wl.scale,
+def _weights(wl, dev, packed):
+    w = expert_weights(dev)
+    return moe.pack_weights(w, n_shared=wl.n_shared) if packed else w
+
+
+def _run_forward(wl, dev, packed=False, weights=None, **kw):
+    w = weights if weights is not None else _weights(wl, dev, packed)
+    out, r = moe.forward(dev["x"], dev["W_r"], dev["b"], w, wl.K, wl.scale,
                          n_shared=wl.n_shared, return_routing=True, **kw)
     torch.cuda.synchronize()
     return out, r
 
 
-def _full_parity(wl, inp, seed_note=""):
+def _full_parity(wl, inp, seed_note="", packed=False):
     """Run the layer on the GPU and compare every token with the oracle."""
-    log(f"[gpu] forward {wl.name} T={wl.T} d={wl.d} E={wl.E} K={wl.K} {seed_note}")
+    log(f"[gpu] forward {wl.name} T={wl.T} d={wl.d} E={wl.E} K={wl.K} "
+        f"{'packed ' if packed else ''}{seed_note}")
     dev = weights_to_device(inp, DEV)
-    out, r = _run_forward(wl, dev)
+    out, r = _run_forward(wl, dev, packed)
     ref = oracle.router(inp["x"], inp["W_r"], inp["b"], wl.K, wl.scale, want_scores=True)
     idx_eff, w_eff, st = effective_routing(ref, r["idx"].cpu().numpy(), r["w"].cpu().numpy(),
                                            inp["b"].numpy(), wl.K, wl.scale)
@@ -97,16 +104,18 @@ def test_router_all_tied_and_K1():
 
 
 # ---------------------------------------------------------------- whole layer, every token
-@pytest.mark.parametrize("name", ["tiny_fp32_t128", "mid_fp32_t77", "mid_bf16_t300",
-                                  "mid_latent_t200"])
-def test_forward_parity_every_token(name):
+@pytest.mark.parametrize("name,packed", [("tiny_fp32_t128", False), ("mid_fp32_t77", False),
+                                         ("mid_bf16_t300", False), ("mid_latent_t200", False),
+                                         ("mid_bf16_t300", True), ("mid_latent_t200", True)])
+def test_forward_parity_every_token(name, packed):
     wl = get_workload(name)
-    _full_parity(wl, make_layer_inputs(wl, "cpu", seed=42))
+    _full_parity(wl, make_layer_inputs(wl, "cpu", seed=42), packed=packed)
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["rows", "packed"])
 @pytest.mark.parametrize("case", ["one_token", "K_equals_E", "no_shared", "skewed_few_experts",
-                                  "latent_no_shared", "large_tiles"])
-def test_forward_edge_cases(case):
+                                  "latent_no_shared", "large_tiles", "large_tiles_latent"])
+def test_forward_edge_cases(case, packed):
     if case == "one_token":
         wl = _custom(T=1)
     elif case == "K_equals_E":
@@ -117,12 +126,16 @@ def test_forward_edge_cases(case):
         wl = _custom(E=40, K=3, T=200)
     elif case == "latent_no_shared":
         wl = _custom(d_latent=128, n_shared=0, F_shared=0, T=90, scale=1.0)
-    else:  # enough rows per expert to take the 128-row tiles, ragged tails
+    elif case == "large_tiles":  # enough rows per expert for the 128-row tiles, ragged tails
         wl = _custom(E=6, K=2, T=700, d=384, F=192, n_shared=2, F_shared=64)
+    else:  # 128-row tiles for the experts and the dense latent maps (T >= 1024), two
+        # K segments in the last GEMM, N tails inside a 512-wide tile
+        wl = _custom(E=5, K=2, T=1100, d=320, F=192, n_shared=1, F_shared=128, d_latent=192,
+                     scale=1.0)
     inp = make_layer_inputs(wl, "cpu", seed=5)
     if case == "skewed_few_experts":
         inp["b"][:3] = 10.0     # every token picks experts 0, 1, 2; the rest get none
-    _, r, _ = _full_parity(wl, inp, case)
+    _, r, _ = _full_parity(wl, inp, case, packed=packed)
     if case == "skewed_few_experts":
         c = r["counts"].cpu().numpy()
         assert c[:3].tolist() == [200, 200, 200] and c[3:].sum() == 0
@@ -168,13 +181,19 @@ def _sampled_tokens(T, ref, counts, idx_eff, n_random=6):
     return sorted(toks)
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["rows", "packed"])
 @pytest.mark.parametrize("name", ["k2_decode_t256", "k2_prefill_t16384", "k3_latent_t4096"])
-def test_forward_parity_full_size_sampled(name):
+def test_forward_parity_full_size_sampled(name, packed):
     wl = get_workload(name)
     log(f"[gpu] full-size {name}: generating inputs on the GPU")
     inp = make_layer_inputs(wl, DEV, seed=42)
-    log(f"[gpu] full-size {name}: moe_forward")
-    out, r = _run_forward(wl, inp)
+    w = None
+    if packed:
+        log(f"[gpu] full-size {name}: packing the weights")
+        w = moe.pack_weights(expert_weights(inp), n_shared=wl.n_shared)
+    log(f"[gpu] full-size {name}: moe_forward ({'packed' if packed else 'row-major'} weights)")
+    out, r = _run_forward(wl, inp, weights=w)
+    del w
     x_h, Wr_h, b_h = host(inp["x"]), host(inp["W_r"]), host(inp["b"])
     log(f"[cpu] oracle router over all {wl.T} tokens")
     ref = oracle.router(x_h, Wr_h, b_h, wl.K, wl.scale, want_scores=True)
