@@ -85,13 +85,15 @@ def up_kernel(wl, layout):
 
 def is_up_kernel(name):
     """Kernel name (untruncated) of an up-projection dispatch: the SwiGLU
-    instantiation of k_gemm_wide<TC, EPI, NSEG> or of
+    instantiation of k_gemm_wide<TC, EPI, NSEG, BM> or of
     k_gemm_big<TC, BM, BN, WM, WN, NST, ROWB, EPI, PK>."""
     m = re.search(r"k_gemm_(wide|big)<([^>]*)>", name)
     if not m:
         return False
     args = m.group(2).replace(" ", "").split(",")
-    return (args[1] if m.group(1) == "wide" else args[7]) == "1"
+    if m.group(1) == "wide":          # k_gemm_wide<TC, EPI, NSEG, BM>
+        return args[1] == "1"
+    return args[7] == "1"
 
 
 def get_workload_light(name):
@@ -100,11 +102,13 @@ def get_workload_light(name):
 
 
 def work_model(wl, counts):
-    """Algorithmic flops and bytes of one forward step and of its up-projection
-    kernel.  Bytes: weights of the experts that received tokens read once,
-    shared / router / latent weights, x read and out written once (temporaries
-    excluded).  Flops: the selected experts' SwiGLU, the shared experts, the
-    latent maps; the router counted apart (fp32-class)."""
+    """Algorithmic flops and bytes of one forward step and of the
+    up-projection kernel (routed rows + shared experts).  Bytes: weights of
+    the experts that received
+    tokens read once, shared / router / latent weights, x read and out
+    written once (temporaries excluded).  Flops: the selected experts'
+    SwiGLU, the shared experts, the latent maps; the router counted apart
+    (fp32-class)."""
     es = 2 if wl.act_dtype == "bf16" else 4
     din, F, d, T = wl.d_in, wl.F, wl.d, wl.T
     Fsh = wl.n_shared * wl.F_shared
@@ -117,6 +121,7 @@ def work_model(wl, counts):
     flops_router = 2.0 * T * d * wl.E
     bytes_step = (touched * w_expert + 3 * d * Fsh * es + wl.E * d * 4 + wl.E * 4
                   + 2 * d * wl.d_latent * es + 2 * T * d * es)
+
     up = dict(
         flops=2.0 * A * din * 2 * F + 2.0 * T * d * 2 * Fsh,
         bytes=(touched * 2 * F * din * es + 2 * Fsh * d * es + T * din * es

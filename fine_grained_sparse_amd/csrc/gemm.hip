@@ -598,7 +598,7 @@ __global__ __launch_bounds__(64 * WM * WN, (big_occupancy<BM, BN, NST, ROWB>()))
 // Prefill tile for packed weights: 128 A rows x 512 B rows per workgroup
 // of four waves; wave w owns B rows [128 w, 128 w + 128), a 128 x 128
 // output block held in 64 accumulators of 16x16.  Only A is shared between
-// the waves, so only A goes through LDS (DMA into a ring of three 64-K
+// the waves, so only A goes through LDS (DMA into a ring of four 64-K
 // slots).  Each wave loads its own B fragments from global memory straight
 // into registers one stage ahead, a fragment being reloaded with the next
 // stage as soon as its last MFMA of this stage has issued.  In the packed
@@ -607,27 +607,34 @@ __global__ __launch_bounds__(64 * WM * WN, (big_occupancy<BM, BN, NST, ROWB>()))
 // path on gfx950 is limited by the lines an instruction touches, and a
 // row-major fragment (16 rows x 64 bytes) touches twice as many.
 //
-// NSEG K segments (1, or 2 for a sum of two products).  Memory operations
-// per stage and lane, in issue order: NAB A DMA loads for stage it + 2
-// (after the barrier), then the 2 NB B loads of stage it + 1 among the
-// MFMAs; the prologue issues A(0), A(1), B(0).  Every stage issues the same
-// loads (past the last stage they re-read it), so from the second stage on
-// the loads younger than A(it) are the 2 NB of its own iteration plus one
-// full iteration, a compile-time count; the first stage (younger: A(1) and
-// B(0)) is peeled with its own count.
-template <typename TC, int EPI, int NSEG>
+// NSEG K segments (1, or 2 for a sum of two products).  Per stage and lane
+// the memory operations are, in issue order: NB B loads of the next stage
+// among the first slab's MFMAs, NAB A DMA loads for stage it + NST (after the
+// barrier between the slabs), NB B loads among the second slab's MFMAs.
+// Every stage issues the same loads (past the last stage they re-read it),
+// so the loads younger than A(it + 1) at its wait are a compile-time count
+// (the first stages, after a prologue of A(0..NST-1) and B(0), have their own).
+template <typename TC, int EPI, int NSEG, int BM>
 __global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
     using T = bf16_t;
-    constexpr int ES = 2, BM = 128, BN = 512, NW = 4, TN = BN / NW;
+    static_assert(BM == 128 || BM == 64, "row tiles");
+    constexpr int ES = 2, BN = 512, NW = 4, TN = BN / NW;
     constexpr int MB = BM / 16, NB = TN / 16;
     constexpr int ROWB = 128, BKE = ROWB / ES;  // a stage is 64 K = two 32-K slabs
-    constexpr int NST = 3;                     // A slots: it (read), it+1 (landing), it+2 (issued)
+    constexpr int NST = 4;                     // A slots: stages it .. it+3 (it+4 after the barrier)
     constexpr int STAGE = BM * ROWB;
     constexpr int BNO = EPI == EPI_SWIGLU ? BN / 2 : BN;
     constexpr int NAB = STAGE / 1024 / NW;  // 1 KiB A blocks per wave per stage
     constexpr int LOADS = NAB + 2 * NB;     // vector loads per lane per stage
-    constexpr int kWaitA = 2 * NB + LOADS, kWaitA0 = NAB + 2 * NB;
-    static_assert(kWaitA < 64 && (NSEG == 1 || NSEG == 2), "vmcnt range; segments");
+    // A(it + 1) is waited for between the slabs of stage it.  Loads younger
+    // than it: once A(it + 1) came from stage it + 1 - NST, that stage's
+    // second-slab B loads, NST - 2 whole stages and the first-slab B loads
+    // of stage it; before that (A from the prologue: A(0..NST-1), B(0)),
+    // the later prologue loads, the stages so far and the first slab.
+    constexpr int kWaitA = 2 * NB + (NST - 2) * LOADS;
+    constexpr int kY0 = NAB * (NST - 2) + 3 * NB, kY1 = NAB * (NST - 3) + 3 * NB + LOADS;
+    constexpr int kWait0 = kY0 < kWaitA ? kY0 : kWaitA, kWait1 = kY1 < kWaitA ? kY1 : kWaitA;
+    static_assert(kWaitA < 64 && (NSEG == 1 || NSEG == 2) && (NST == 3 || NST == 4), "vmcnt range; shape");
     constexpr int WP = 256;
     constexpr int EP_BYTES = BM * (WP + 4) * 4;
     constexpr int LDS_BYTES = NST * STAGE > EP_BYTES ? NST * STAGE : EP_BYTES;
@@ -654,10 +661,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
         const int p = row0 + (r < rows ? r : 0);
         arow[j] = G.rowmap ? G.rowmap[p] : p;
     }
+    // Everything the loop needs from the group, held in registers: the DMA
+    // asm clobbers memory, so fields read through G inside the loop would be
+    // reloaded (scalar loads, which also blunt the LDS wait counts) every
+    // stage.
+    const char* const sA0 = static_cast<const char*>(G.seg[0].A);
+    const char* const sA1 = static_cast<const char*>(G.seg[NSEG - 1].A);
+    const int64_t lda0 = G.seg[0].lda * ES, lda1 = G.seg[NSEG - 1].lda * ES;
+    const int64_t eoff = static_cast<int64_t>(jb.expert) * G.b_estride * ES;  // segment 0 only
+    const char* const sB0 = static_cast<const char*>(G.seg[0].B) + eoff;
+    const char* const sU0 = EPI == EPI_SWIGLU ? static_cast<const char*>(G.seg[0].Bu) + eoff : sB0;
+    const char* const sB1 = static_cast<const char*>(G.seg[NSEG - 1].B);
+    const char* const sU1 = EPI == EPI_SWIGLU ? static_cast<const char*>(G.seg[NSEG - 1].Bu) : sB1;
+    const uint32_t kb0 = static_cast<uint32_t>(G.seg[0].K / 32), kb1 = static_cast<uint32_t>(G.seg[NSEG - 1].K / 32);
+
     const char* asrc[NAB];  // segment 0 row addresses
 #pragma unroll
-    for (int j = 0; j < NAB; ++j)
-        asrc[j] = static_cast<const char*>(G.seg[0].A) + static_cast<int64_t>(arow[j]) * G.seg[0].lda * ES + achunk;
+    for (int j = 0; j < NAB; ++j) asrc[j] = sA0 + static_cast<int64_t>(arow[j]) * lda0 + achunk;
     const uint32_t lds_base = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(lds)));
     auto issue_a = [&](int kt, int slot) {
@@ -667,9 +687,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
             for (int j = 0; j < NAB; ++j) lds_dma16(asrc[j] + kt * ROWB, dst + (wid + NW * j) * 1024);
         } else {
             const bool s1 = kt >= nk0;
-            const GemmSeg& S = s1 ? G.seg[1] : G.seg[0];
-            const char* base = static_cast<const char*>(S.A) + (kt - (s1 ? nk0 : 0)) * ROWB + achunk;
-            const int64_t lda = S.lda * ES;
+            const char* base = (s1 ? sA1 : sA0) + (kt - (s1 ? nk0 : 0)) * ROWB + achunk;
+            const int64_t lda = s1 ? lda1 : lda0;
 #pragma unroll
             for (int j = 0; j < NAB; ++j) lds_dma16(base + arow[j] * lda, dst + (wid + NW * j) * 1024);
         }
@@ -685,12 +704,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
         const int nb = EPI == EPI_SWIGLU ? (n0 + wid * (TN / 2)) / 16 + j % (NB / 2) : (n0 + wid * TN) / 16 + j;
         rb[j] = nb < N / 16 ? nb : N / 16 - 1;
     }
-    const int64_t eoff = static_cast<int64_t>(jb.expert) * G.b_estride * ES;  // segment 0 only
     auto load_b = [&](int kt, int sl, int j) {
         const bool s1 = NSEG == 2 && kt >= nk0;
-        const GemmSeg& S = s1 ? G.seg[1] : G.seg[0];
-        const char* m = static_cast<const char*>((EPI == EPI_SWIGLU && j >= NB / 2) ? S.Bu : S.B) + (s1 ? 0 : eoff);
-        const uint32_t blk = static_cast<uint32_t>(rb[j]) * static_cast<uint32_t>(S.K / 32) +
+        const bool up = EPI == EPI_SWIGLU && j >= NB / 2;
+        const char* m = s1 ? (up ? sU1 : sB1) : (up ? sU0 : sB0);
+        const uint32_t blk = static_cast<uint32_t>(rb[j]) * (s1 ? kb1 : kb0) +
                              static_cast<uint32_t>((kt - (s1 ? nk0 : 0)) * 2 + sl);
         return *reinterpret_cast<const uint4*>(m + blk * 1024u + lane * 16);
     };
@@ -707,46 +725,63 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
     const int fo1 = frow * ROWB + ((((lane >> 4) + 4) ^ (frow & 7)) << 4);
 
     uint4 fb[2][NB];  // B fragments of the current stage, refilled with the next
-    // one K stage: wait for its A, compute it from LDS A and register B
-    auto step = [&](int it, auto wait_a) {
-        wait_a();
-        __syncthreads();  // A(it) of every wave has landed; slot (it+2)%3 is free
-        issue_a(min(it + 2, nkt - 1), (it + 2) % NST);
-        const int kb = min(it + 1, nkt - 1);
-        const char* As = lds + (it % NST) * STAGE;
-        uint4 fa[2][MB];
+    uint4 fa0[MB];    // A fragments of the first slab of the current stage
+    auto read_a = [&](uint4 (&fa)[MB], int stage, int fo) {
+        const char* As = lds + (stage % NST) * STAGE;
 #pragma unroll
-        for (int i = 0; i < MB; ++i) fa[0][i] = *reinterpret_cast<const uint4*>(As + i * 16 * ROWB + fo0);
-        // The order below is the schedule: a B fragment is reloaded right
-        // after its last MFMA of the stage (the scheduler would otherwise
-        // sink the loads to the next use and expose their latency), and the
-        // second slab's A fragments are read while the first slab computes.
+        for (int i = 0; i < MB; ++i) fa[i] = *reinterpret_cast<const uint4*>(As + i * 16 * ROWB + fo);
+    };
+    // One K stage.  The order below is the schedule (the scheduler would
+    // otherwise sink the B loads to their next use and expose their
+    // latency): a B fragment is reloaded with the next stage right after its
+    // last MFMA here; the second slab's A fragments are read early in the
+    // first slab; the barrier sits between the slabs, after which the slot
+    // of this stage (read by every wave) takes A(it + NST) and the next
+    // stage's first A fragments are read while the second slab computes.
+    auto step = [&](int it, auto wait_next) {
+        const int kb = min(it + 1, nkt - 1);
+        uint4 fa1[MB];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
+        for (int j = 0; j < NB; ++j) {
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
+            for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa0[i], fb[0][j], acc[i][j]);
+            fb[0][j] = load_b(kb, 0, j);
+            if (j == 1) read_a(fa1, it, fo1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_next();      // this wave's A(it + 1) has landed
+        __syncthreads();  // ... every wave's; every wave is done reading slot it % 3
+        issue_a(min(it + NST, nkt - 1), it % NST);
+        read_a(fa0, it + 1, fo0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa[sl][i], fb[sl][j], acc[i][j]);
-                fb[sl][j] = load_b(kb, sl, j);
-                if (sl == 0 && j == 1) {
+        for (int j = 0; j < NB; ++j) {
 #pragma unroll
-                    for (int i = 0; i < MB; ++i)
-                        fa[1][i] = *reinterpret_cast<const uint4*>(As + i * 16 * ROWB + fo1);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa1[i], fb[1][j], acc[i][j]);
+            fb[1][j] = load_b(kb, 1, j);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    issue_a(0, 0);
-    issue_a(min(1, nkt - 1), 1);
+#pragma unroll
+    for (int p = 0; p < NST; ++p) issue_a(min(p, nkt - 1), p);
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
         for (int j = 0; j < NB; ++j) fb[sl][j] = load_b(0, sl, j);
-    step(0, [] { wait_vmcnt<kWaitA0>(); });
-    for (int it = 1; it < nkt; ++it) step(it, [] { wait_vmcnt<kWaitA>(); });
+    wait_vmcnt<(NST - 1) * NAB + 2 * NB>();  // A(0): younger are A(1..NST-1) and B(0)
+    __syncthreads();
+    read_a(fa0, 0, fo0);
+    for (int it = 0; it < nkt; ++it)
+        step(it, [it] {
+            if (it >= NST - 2)
+                wait_vmcnt<kWaitA>();
+            else if (it == 0)
+                wait_vmcnt<kWait0>();
+            else
+                wait_vmcnt<kWait1>();
+        });
     wait_vmcnt<0>();  // no DMA may land in LDS once the epilogue reuses it
 
     store_tile<TC, EPI, BM, BNO, BM, TN, MB, NB, WP, 256>(acc, lds, 0, wid, G, static_cast<TC*>(G.C), row0, rows,
@@ -801,9 +836,9 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
         if (packed || cfg != TILE_SMALL) return hipErrorInvalidValue;  // fp32 runs the small tiles only
     }
     if (cfg == TILE_WIDE && !(packed && wide_fits(args))) cfg = TILE_LARGE;
+    const bool wide = cfg == TILE_WIDE;
     // output columns per N tile of the kernel actually launched
-    const int bn = sizeof(T) == 4 ? kF32BN
-                   : (cfg == TILE_SMALL ? kSmBN : (cfg == TILE_WIDE ? kWideBN : kBigBN));
+    const int bn = sizeof(T) == 4 ? kF32BN : (cfg == TILE_SMALL ? kSmBN : (wide ? kWideBN : kBigBN));
     const int bno = EPI == EPI_SWIGLU ? bn / 2 : bn;
     GemmArgs a = args;
     a.ntn = (max_n + bno - 1) / bno;
@@ -818,9 +853,9 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
     } else {
         if (cfg == TILE_WIDE) {
             if (max_nseg(a) == 1)
-                hipLaunchKernelGGL((k_gemm_wide<TC, EPI, 1>), grid, dim3(256), 0, stream, a);
+                hipLaunchKernelGGL((k_gemm_wide<TC, EPI, 1, kWideBM>), grid, dim3(256), 0, stream, a);
             else
-                hipLaunchKernelGGL((k_gemm_wide<TC, EPI, 2>), grid, dim3(256), 0, stream, a);
+                hipLaunchKernelGGL((k_gemm_wide<TC, EPI, 2, kWideBM>), grid, dim3(256), 0, stream, a);
         } else if (cfg == TILE_SMALL) {
             if (packed)
                 hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, kSmNST, kSmROWB, EPI, true>), grid,

@@ -114,7 +114,8 @@ def test_forward_parity_every_token(name, packed):
 
 @pytest.mark.parametrize("packed", [False, True], ids=["rows", "packed"])
 @pytest.mark.parametrize("case", ["one_token", "K_equals_E", "no_shared", "skewed_few_experts",
-                                  "latent_no_shared", "large_tiles", "large_tiles_latent"])
+                                  "latent_no_shared", "large_tiles", "large_tiles_latent",
+                                  "half_tiles"])
 def test_forward_edge_cases(case, packed):
     if case == "one_token":
         wl = _custom(T=1)
@@ -128,17 +129,26 @@ def test_forward_edge_cases(case, packed):
         wl = _custom(d_latent=128, n_shared=0, F_shared=0, T=90, scale=1.0)
     elif case == "large_tiles":  # enough rows per expert for the 128-row tiles, ragged tails
         wl = _custom(E=6, K=2, T=700, d=384, F=192, n_shared=2, F_shared=64)
-    else:  # 128-row tiles for the experts and the dense latent maps (T >= 1024), two
-        # K segments in the last GEMM, N tails inside a 512-wide tile
+    elif case == "large_tiles_latent":  # 128-row tiles for the experts and the dense
+        # latent maps (T >= 1024), two K segments in the last GEMM, N tails inside a
+        # 512-wide tile
         wl = _custom(E=5, K=2, T=1100, d=320, F=192, n_shared=1, F_shared=128, d_latent=192,
                      scale=1.0)
+    else:  # half_tiles: expert 0 gets four full 128-row tiles + 8 rows, the others ~35
+        # rows each: 128-row tiles that are mostly padding
+        wl = _custom(E=16, K=2, T=520, d=256, F=128, n_shared=1, F_shared=128)
     inp = make_layer_inputs(wl, "cpu", seed=5)
     if case == "skewed_few_experts":
         inp["b"][:3] = 10.0     # every token picks experts 0, 1, 2; the rest get none
+    if case == "half_tiles":
+        inp["b"][0] = 10.0
     _, r, _ = _full_parity(wl, inp, case, packed=packed)
     if case == "skewed_few_experts":
         c = r["counts"].cpu().numpy()
         assert c[:3].tolist() == [200, 200, 200] and c[3:].sum() == 0
+    if case == "half_tiles":
+        c = r["counts"].cpu().numpy()
+        assert c[0] == 520 and 0 < c[1:].max() <= 64
 
 
 def test_forward_zero_tokens():
