@@ -47,14 +47,17 @@ def log(msg):
 
 
 def source_hash() -> str:
-    """Hash of the HIP library sources: counters taken on other sources do
-    not describe the kernels that run now."""
+    """Hash of the HIP library sources with comments and whitespace removed:
+    counters taken on other code do not describe the kernels that run now."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "fine_grained_sparse_amd", "csrc", "*"))):
         if p.endswith((".hip", ".hpp", ".cpp")):
+            with open(p) as f:
+                code = f.read()
+            code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+            code = re.sub(r"//[^\n]*", " ", code)
             h.update(os.path.basename(p).encode())
-            with open(p, "rb") as f:
-                h.update(f.read())
+            h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,22 +1,24 @@
-// Grouped GEMM on gfx950 MFMA for the MoE layer.
-//
-// One kernel template computes C = epi(A * B^T) over a list of tiles:
+// Grouped GEMM on gfx950 MFMA for the MoE layer: C = epi(A * B^T) over a
+// table of tiles.
 //   - routed experts: each tile is up to BM consecutive rows of the
 //     expert-sorted assignment space; A rows are gathered through a row map
 //     (sorted position -> token) while they are loaded, B is that expert's
 //     [N, K] weight matrix;
 //   - dense groups (shared experts, latent maps, router): plain row tiles.
 // The SwiGLU epilogue computes H = silu(A Wg^T) * (A Wu^T) with the gate and
-// up tiles held by the same lanes (the expert form of the llm-arch-kb
+// up columns held by the same lanes (the expert form of the llm-arch-kb
 // "Kimi K2 MoE" entry, section 2: three matrices per expert).
 //
-// Data flow per workgroup (256 threads = 4 waves of 64):
-//   global --(16 B per lane, coalesced rows)--> registers --> LDS (two
-//   stages, 144-byte padded rows) --> MFMA fragments --> fp32 accumulators
-//   --> LDS epilogue tile --> 16-byte coalesced stores.
-// A K stage is 128 bytes of each row (64 bf16 or 32 fp32); each 64-byte
-// slab of a stage feeds one v_mfma_f32_16x16x32_bf16 (or four
-// v_mfma_f32_16x16x4_f32) per 16x16 block.
+// Three kernels:
+//   k_gemm       fp32 operands (small parity workloads): register-staged
+//                16 x 256 tiles, four v_mfma_f32_16x16x4_f32 per fragment.
+//   k_gemm_big   bf16, both operands DMA'd into an LDS ring
+//                (global_load_lds_dwordx4): 16 x 512 decode tiles, 128 x 256
+//                prefill tiles on row-major weights, the router logits.
+//   k_gemm_wide  bf16 prefill tiles on packed weights: 128 x 512, A through
+//                LDS, each wave's weight fragments straight into registers.
+// One 64-byte K slab feeds one v_mfma_f32_16x16x32_bf16 per 16x16 block; a
+// lane supplies row lane % 16 and the 16-byte K chunk lane / 16 of it.
 #include "common.hpp"
 #include "launch.hpp"
 
