@@ -49,10 +49,12 @@ def lib():
         vp, i32 = ctypes.c_void_p, ctypes.c_int32
         L.oracle_router.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp,
                                     ctypes.c_float, vp, vp, vp, vp, i32]
+        L.oracle_router_grouped.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp,
+                                            ctypes.c_float, vp, vp, vp, vp, vp, i32]
         L.oracle_dispatch.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_forward_given_routing.argtypes = [vp, i32, vp, vp, vp, vp, i32]
         L.oracle_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32]
-        for f in (L.oracle_router, L.oracle_dispatch,
+        for f in (L.oracle_router, L.oracle_router_grouped, L.oracle_dispatch,
                   L.oracle_forward_given_routing, L.oracle_forward):
             f.restype = ctypes.c_int
         _lib = L
@@ -122,6 +124,28 @@ def router(x, W_r, b, K, scale, nthreads=None, want_scores=False):
                              _ptr(scores), nthreads or default_threads())
     _check(rc, "oracle_router")
     return dict(idx=idx, w=w, gap=gap, scores=scores)
+
+
+def router_grouped(x, W_r, b, K, scale, n_group, topk_group, nthreads=None, want_scores=False):
+    """Group-limited router.  Returns dict(idx, w, gap, group_gap, scores) as
+    router() plus group_gap [T] (kept-group margin, +inf if all kept)."""
+    xa, xdt = _host(x, "x")
+    Wa, _ = _host(W_r, "W_r")
+    ba, _ = _host(b, "b")
+    if Wa.dtype != np.float32 or ba.dtype != np.float32:
+        raise OracleError("W_r and b are fp32")
+    T, d = xa.shape
+    E = Wa.shape[0]
+    idx = np.zeros((T, K), np.int32)
+    w = np.zeros((T, K), np.float64)
+    gap = np.zeros((T,), np.float64)
+    ggap = np.zeros((T,), np.float64)
+    scores = np.zeros((T, E), np.float64) if want_scores else None
+    rc = lib().oracle_router_grouped(T, d, E, K, n_group, topk_group, xdt, _ptr(xa), _ptr(Wa),
+                                     _ptr(ba), float(scale), _ptr(idx), _ptr(w), _ptr(gap),
+                                     _ptr(ggap), _ptr(scores), nthreads or default_threads())
+    _check(rc, "oracle_router_grouped")
+    return dict(idx=idx, w=w, gap=gap, group_gap=ggap, scores=scores)
 
 
 def dispatch(idx, E):

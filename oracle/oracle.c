@@ -117,6 +117,147 @@ int oracle_router(int32_t T, int32_t d, int32_t E, int32_t K, int32_t x_dtype,
     return ORACLE_OK;
 }
 
+/* One token of the group-limited router [P3 MoEGate forward, the noaux_tc
+ * branch; P3 "one group here" for K2].  Same steps 1, 2 and 4 as
+ * route_one; step 3 becomes:
+ *   - the E experts form n_group contiguous groups of E / n_group;
+ *   - a group's score is the sum of its two largest biased scores v;
+ *   - the topk_group groups of largest score are kept (ties toward the
+ *     lower group index: the excerpt's unsorted topk leaves them open);
+ *   - every expert outside the kept groups takes the value 0.0 (the
+ *     excerpt's masked_fill(..., 0.0), not minus infinity), the others keep v;
+ *   - the K experts of largest such value are selected (ties toward the
+ *     lower expert index).
+ * gap: v'_(K) - v'_(K+1) of the masked values; group_gap: the kept groups'
+ * smallest score minus the largest dropped one (+inf when all are kept). */
+static void route_one_grouped(int32_t d, int32_t E, int32_t K, int32_t n_group,
+                              int32_t topk_group, int32_t x_dtype,
+                              const void *x, size_t xrow, const float *W_r,
+                              const float *b, float scale, double *s,
+                              double *v, double *gs, char *gkeep, char *chosen,
+                              int32_t *sel, double *w, double *gap,
+                              double *group_gap)
+{
+    const int32_t per = E / n_group;
+    for (int32_t e = 0; e < E; ++e) {
+        double z = 0.0;
+        for (int32_t j = 0; j < d; ++j)
+            z += elem(x, x_dtype, xrow + (size_t)j) * (double)W_r[(size_t)e * d + j];
+        s[e] = sigmoid(z);
+        v[e] = s[e] + (double)b[e];
+        chosen[e] = 0;
+    }
+    /* group scores: the two largest v of each group, summed */
+    for (int32_t g = 0; g < n_group; ++g) {
+        double m1 = -INFINITY, m2 = -INFINITY;
+        for (int32_t e = g * per; e < (g + 1) * per; ++e) {
+            if (v[e] > m1) {
+                m2 = m1;
+                m1 = v[e];
+            } else if (v[e] > m2) {
+                m2 = v[e];
+            }
+        }
+        gs[g] = m1 + m2;
+        gkeep[g] = 0;
+    }
+    /* keep topk_group groups: rounds of "largest unkept score", scanning g
+     * upward with a strict comparison (ties toward the lower group index) */
+    double last_kept = INFINITY;
+    for (int32_t k = 0; k < topk_group; ++k) {
+        int32_t best = -1;
+        for (int32_t g = 0; g < n_group; ++g)
+            if (!gkeep[g] && (best < 0 || gs[g] > gs[best]))
+                best = g;
+        gkeep[best] = 1;
+        last_kept = gs[best];
+    }
+    if (group_gap) {
+        double next = -INFINITY;
+        for (int32_t g = 0; g < n_group; ++g)
+            if (!gkeep[g] && gs[g] > next)
+                next = gs[g];
+        *group_gap = (topk_group == n_group) ? INFINITY : last_kept - next;
+    }
+    /* experts of dropped groups take 0.0 */
+    for (int32_t e = 0; e < E; ++e)
+        if (!gkeep[e / per])
+            v[e] = 0.0;
+    for (int32_t k = 0; k < K; ++k) {
+        int32_t best = -1;
+        for (int32_t e = 0; e < E; ++e)
+            if (!chosen[e] && (best < 0 || v[e] > v[best]))
+                best = e;
+        chosen[best] = 1;
+        sel[k] = best;
+    }
+    if (gap) {
+        double vk = v[sel[K - 1]];
+        double next = -INFINITY;
+        for (int32_t e = 0; e < E; ++e)
+            if (!chosen[e] && v[e] > next)
+                next = v[e];
+        *gap = (K == E) ? INFINITY : vk - next;
+    }
+    for (int32_t i = 1; i < K; ++i) {
+        int32_t key = sel[i], j = i - 1;
+        while (j >= 0 && sel[j] > key) {
+            sel[j + 1] = sel[j];
+            --j;
+        }
+        sel[j + 1] = key;
+    }
+    double den = 0.0;
+    for (int32_t k = 0; k < K; ++k)
+        den += s[sel[k]];
+    den += 1e-20;
+    for (int32_t k = 0; k < K; ++k)
+        w[k] = (s[sel[k]] / den) * (double)scale;
+}
+
+int oracle_router_grouped(int32_t T, int32_t d, int32_t E, int32_t K,
+                          int32_t n_group, int32_t topk_group, int32_t x_dtype,
+                          const void *x, const float *W_r, const float *b,
+                          float scale, int32_t *topk_idx, double *topk_w,
+                          double *gap, double *group_gap, double *scores,
+                          int32_t nthreads)
+{
+    if (T < 0 || d <= 0 || E <= 0 || K < 1 || K > E || n_group < 1 ||
+        E % n_group != 0 || topk_group < 1 || topk_group > n_group ||
+        (n_group > 1 && E / n_group < 2))
+        return ORACLE_ERR_SHAPE;
+    if (x_dtype != ORACLE_F32 && x_dtype != ORACLE_BF16)
+        return ORACLE_ERR_SHAPE;
+    if (T > 0 && (!x || !W_r || !b || !topk_idx || !topk_w))
+        return ORACLE_ERR_NULL;
+    int nt = nthreads > 0 ? nthreads : 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int32_t t = 0; t < T; ++t) {
+        double *s = (double *)malloc(sizeof(double) * (size_t)E);
+        double *v = (double *)malloc(sizeof(double) * (size_t)E);
+        double *gs = (double *)malloc(sizeof(double) * (size_t)n_group);
+        char *gkeep = (char *)malloc((size_t)n_group);
+        char *chosen = (char *)malloc((size_t)E);
+        double g = 0.0, gg = 0.0;
+        route_one_grouped(d, E, K, n_group, topk_group, x_dtype, x,
+                          (size_t)t * d, W_r, b, scale, s, v, gs, gkeep, chosen,
+                          topk_idx + (size_t)t * K, topk_w + (size_t)t * K, &g,
+                          &gg);
+        if (gap)
+            gap[t] = g;
+        if (group_gap)
+            group_gap[t] = gg;
+        if (scores)
+            memcpy(scores + (size_t)t * E, s, sizeof(double) * (size_t)E);
+        free(s);
+        free(v);
+        free(gs);
+        free(gkeep);
+        free(chosen);
+    }
+    return ORACLE_OK;
+}
+
 int oracle_dispatch(int32_t T, int32_t E, int32_t K, const int32_t *topk_idx,
                     int32_t *counts, int32_t *offsets, int32_t *sorted_token,
                     int32_t *pos)

@@ -86,6 +86,23 @@ int oracle_router(int32_t T, int32_t d, int32_t E, int32_t K, int32_t x_dtype,
  * sorted_token [T*K] (for e ascending, every token t that selected e, in
  * ascending t), pos [T, K] (position of assignment (t, slot k) in
  * sorted_token).                                                             */
+/* Group-limited router [P3 MoEGate forward, noaux_tc branch].  As
+ * oracle_router, except for the choice: experts form n_group contiguous
+ * groups; a group scores the sum of its two largest v = s + b; the
+ * topk_group best groups are kept (ties toward the lower group index);
+ * experts of the other groups take the value 0.0; the K largest values are
+ * selected (ties toward the lower expert index).  n_group = 1 (or
+ * topk_group = n_group) is oracle_router.  Requires E % n_group == 0,
+ * 1 <= topk_group <= n_group and, for n_group > 1, at least 2 experts per
+ * group.  group_gap [T] (nullable): smallest kept group score minus the
+ * largest dropped one (+inf if all groups are kept).                        */
+int oracle_router_grouped(int32_t T, int32_t d, int32_t E, int32_t K,
+                          int32_t n_group, int32_t topk_group, int32_t x_dtype,
+                          const void *x, const float *W_r, const float *b,
+                          float scale, int32_t *topk_idx, double *topk_w,
+                          double *gap, double *group_gap, double *scores,
+                          int32_t nthreads);
+
 int oracle_dispatch(int32_t T, int32_t E, int32_t K, const int32_t *topk_idx,
                     int32_t *counts, int32_t *offsets, int32_t *sorted_token,
                     int32_t *pos);

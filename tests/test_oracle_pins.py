@@ -398,3 +398,97 @@ def test_missing_expert_is_an_error():
     lay2 = oracle.layer_from_inputs(wl, inp, experts=used - {min(used)})
     with pytest.raises(oracle.OracleError):
         oracle.forward_given_routing(lay2, inp["x"], r["idx"], r["w"])
+
+
+# --------------------------------------------------------------------------
+# Group-limited selection (router card, MoEGate excerpt, noaux_tc branch:
+# group score = sum of the two largest biased scores of the group, keep
+# topk_group groups, masked_fill(..., 0.0) on the others, top-K)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_fp32_t128", "mid_bf16_t300"])
+def test_grouped_router_with_one_group_or_all_groups_is_the_plain_router(name):
+    wl = get_workload(name)
+    r = make_router_inputs(wl, "cpu", seed=11)
+    plain = oracle.router(r["x"], r["W_r"], r["b"], wl.K, wl.scale)
+    for n_group, topk_group in ((1, 1), (4, 4), (8, 8)):
+        g = oracle.router_grouped(r["x"], r["W_r"], r["b"], wl.K, wl.scale, n_group, topk_group)
+        assert np.array_equal(g["idx"], plain["idx"]), (n_group, topk_group)
+        assert np.array_equal(g["w"], plain["w"]), (n_group, topk_group)
+        assert np.all(np.isinf(g["group_gap"]))
+
+
+def _designed_router(s_target, b):
+    # x = e_0 and W_r[e, 0] = logit(s_e): sigmoid(z_e) = s_e up to the fp32
+    # rounding of the logit (relative 1e-7).
+    z = [math.log(p / (1.0 - p)) for p in s_target]
+    x = _f32([[1.0, 0.0]])
+    W_r = _f32([[zz, 3.0] for zz in z])
+    return x, W_r, _f32(b)
+
+
+def test_grouped_worked_example_closed_form():
+    # 8 experts in 4 groups of 2, no bias: v = s.
+    #   s      = (.9, .1 | .5, .5 | .8, .05 | .3, .2)
+    #   groups:   1.0     1.0      .85        .5
+    # topk_group = 2 keeps groups 0 and 1 (.8 in group 2 is the third best
+    # expert overall but its group loses), so K = 3 picks {0, 2, 3}
+    # (.9, .5, .5): w = 2.827 * (.9, .5, .5) / 1.9.  group_gap = 1.0 - .85.
+    s = [0.9, 0.1, 0.5, 0.5, 0.8, 0.05, 0.3, 0.2]
+    x, W_r, b = _designed_router(s, [0.0] * 8)
+    g = oracle.router_grouped(x, W_r, b, 3, 2.827, 4, 2, want_scores=True)
+    assert g["idx"].tolist() == [[0, 2, 3]]
+    np.testing.assert_allclose(g["w"][0], SCALE32 * np.array([0.9, 0.5, 0.5]) / 1.9, rtol=1e-6)
+    np.testing.assert_allclose(g["group_gap"][0], 0.15, rtol=1e-5)
+    # the plain router would take expert 4 (.8) instead of 2
+    p = oracle.router(x, W_r, b, 3, 2.827)
+    assert p["idx"].tolist() == [[0, 2, 4]]
+
+
+def test_grouped_ties_between_groups_go_to_the_lower_group():
+    # W_r = 0 makes every s exactly 1/2, so v = 1/2 + b exactly; groups of 2
+    # score (1 + .6 + .4, 1 + .4 + .6, 1 + .1 + .1) = (2, 2, 1.2): groups 0
+    # and 1 tie, topk_group = 1 keeps group 0, and K = 2 takes {0, 1}.
+    g = oracle.router_grouped(_f32([[1.0, 0.0]]), _f32([[0.0, 0.0]] * 6),
+                              _f32([0.6, 0.4, 0.4, 0.6, 0.1, 0.1]), 2, 1.0, 3, 1)
+    assert g["idx"].tolist() == [[0, 1]]
+    assert g["group_gap"][0] == 0.0
+
+
+def test_grouped_masked_experts_take_zero_not_minus_infinity():
+    # Biased scores below zero inside the kept group lose to the 0.0 the
+    # excerpt writes into the dropped groups (masked_fill with 0.0):
+    #   s = .5 everywhere (z = 0), b = (-.6, -.7 | -.9, -.95)
+    #   v = (-.1, -.2 | -.4, -.45); group scores -.3 | -.85 -> keep group 0;
+    #   masked values (-.1, -.2, 0, 0): top-2 = {2, 3}, both from the
+    #   dropped group, the ties at 0.0 going to the lower index.
+    g = oracle.router_grouped(_f32([[1.0, 0.0]]), _f32([[0.0, 0.0]] * 4),
+                              _f32([-0.6, -0.7, -0.9, -0.95]), 2, 1.0, 2, 1)
+    assert g["idx"].tolist() == [[2, 3]]
+    np.testing.assert_allclose(g["w"][0], [0.5, 0.5], rtol=1e-12)
+
+
+def test_grouped_selection_matches_bruteforce_over_all_subsets():
+    # Exhaustive search instead of rounds of arg-max: the kept groups are the
+    # topk_group-subset of largest total group score, the selected experts
+    # the K-subset of largest total masked value (the lexicographically
+    # smallest one on equal totals, i.e. ties toward lower indices).  The
+    # bias spans +-0.5 so that some biased scores are negative and the
+    # 0.0 of the dropped groups matters.
+    wl = _small(T=40, E=12, K=3, bias_range=0.5)
+    r = make_router_inputs(wl, "cpu", seed=19)
+    n_group, topk_group = 4, 2
+    g = oracle.router_grouped(r["x"], r["W_r"], r["b"], wl.K, wl.scale, n_group, topk_group,
+                              want_scores=True)
+    s = g["scores"]
+    v = s + r["b"].double().numpy()[None, :]
+    per = wl.E // n_group
+    for t in range(wl.T):
+        gsc = [np.sort(v[t, q * per:(q + 1) * per])[-2:].sum() for q in range(n_group)]
+        keep = max(itertools.combinations(range(n_group), topk_group),
+                   key=lambda c: (sum(gsc[q] for q in c), [-q for q in c]))
+        vm = np.array([v[t, e] if e // per in keep else 0.0 for e in range(wl.E)])
+        best = max(itertools.combinations(range(wl.E), wl.K),
+                   key=lambda c: (sum(vm[e] for e in c), [-e for e in c]))
+        assert g["idx"][t].tolist() == list(best), t
+        np.testing.assert_allclose(g["w"][t], s[t, list(best)] / s[t, list(best)].sum() * SCALE32,
+                                   rtol=1e-12)
