@@ -45,7 +45,8 @@ class LayerDesc(ctypes.Structure):
                 ("K", ctypes.c_int32), ("F", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("F_shared", ctypes.c_int32), ("d_latent", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("act_dtype", ctypes.c_int32),
-                ("w_dtype", ctypes.c_int32), ("w_layout", ctypes.c_int32)]
+                ("w_dtype", ctypes.c_int32), ("w_layout", ctypes.c_int32),
+                ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32)]
 
 
 class ExpertWeights(ctypes.Structure):
@@ -83,9 +84,9 @@ def lib():
 
 
 def desc(*, T, d, E, K, F=0, n_shared=0, F_shared=0, d_latent=0, scale=2.827,
-         act_dtype=MOE_BF16, w_dtype=None, w_layout=MOE_LAYOUT_ROWS):
+         act_dtype=MOE_BF16, w_dtype=None, w_layout=MOE_LAYOUT_ROWS, n_group=1, topk_group=1):
     return LayerDesc(T, d, E, K, F, n_shared, F_shared, d_latent, scale, act_dtype,
-                     act_dtype if w_dtype is None else w_dtype, w_layout)
+                     act_dtype if w_dtype is None else w_dtype, w_layout, n_group, topk_group)
 
 
 def workspace_size(layer_desc: LayerDesc, forward: bool) -> int:
@@ -133,9 +134,11 @@ class Workspace:
 _default_ws = Workspace()
 
 
-def router(x, W_r, b, K, scale=2.827, *, counts=True, workspace=None, stream=None):
+def router(x, W_r, b, K, scale=2.827, *, counts=True, workspace=None, stream=None,
+           n_group=1, topk_group=1):
     """moe_router: returns (topk_idx int32 [T,K], topk_w fp32 [T,K],
-    expert_counts int32 [E] or None).  Slots are in ascending expert id."""
+    expert_counts int32 [E] or None).  Slots are in ascending expert id.
+    n_group > 1 limits the choice to the topk_group best expert groups."""
     _need(x, "x")
     if x.dim() != 2 or x.dtype not in _DT:
         raise ValueError("x must be [T, d] fp32 or bf16")
@@ -145,7 +148,8 @@ def router(x, W_r, b, K, scale=2.827, *, counts=True, workspace=None, stream=Non
     E = W_r.shape[0]
     _need(W_r, "W_r", torch.float32, (E, d))
     _need(b, "b", torch.float32, (E,), dev)
-    D = desc(T=T, d=d, E=E, K=K, scale=scale, act_dtype=_DT[x.dtype])
+    D = desc(T=T, d=d, E=E, K=K, scale=scale, act_dtype=_DT[x.dtype], n_group=n_group,
+             topk_group=topk_group)
     nbytes = workspace_size(D, False)
     if nbytes == 0:
         raise MoeError("moe_workspace_size", 2)
@@ -160,7 +164,7 @@ def router(x, W_r, b, K, scale=2.827, *, counts=True, workspace=None, stream=Non
     return idx, w, cnt
 
 
-def _weights_desc(weights, T, d, E, K, scale, dt, dev, n_shared):
+def _weights_desc(weights, T, d, E, K, scale, dt, dev, n_shared, n_group=1, topk_group=1):
     """Validate the weight tensors; return (LayerDesc, ExpertWeights)."""
     Wg, Wu, Wd = weights["W_gate"], weights["W_up"], weights["W_down"]
     _need(Wg, "W_gate", dt, device=dev)
@@ -189,7 +193,8 @@ def _weights_desc(weights, T, d, E, K, scale, dt, dev, n_shared):
         _need(Wsd, "Ws_down", dt, (d, ns * Fs), dev)
     layout = int(weights.get("layout", MOE_LAYOUT_ROWS))
     D = desc(T=T, d=d, E=E, K=K, F=F, n_shared=ns, F_shared=Fs, d_latent=d_lat,
-             scale=scale, act_dtype=_DT[dt], w_layout=layout)
+             scale=scale, act_dtype=_DT[dt], w_layout=layout, n_group=n_group,
+             topk_group=topk_group)
     W = ExpertWeights(*[None if t is None else t.data_ptr() for t in
                         (Wg, Wu, Wd, Wsg, Wsu, Wsd, Wl_d, Wl_u)])
     return D, W
@@ -217,7 +222,8 @@ def pack_weights(weights, *, n_shared=None, stream=None):
 
 
 def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
-            return_routing=False, workspace=None, stream=None, stage_events=None):
+            return_routing=False, workspace=None, stream=None, stage_events=None,
+            n_group=1, topk_group=1):
     """moe_forward: the whole layer.  `weights` holds W_gate [E,F,d_in],
     W_up [E,F,d_in], W_down [E,d_in,F] and optionally Ws_gate/Ws_up
     [n_shared*F_shared, d], Ws_down [d, n_shared*F_shared], W_lat_down
@@ -226,7 +232,8 @@ def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
     out [T, d], or (out, routing dict) with return_routing=True.
     `stage_events` (optional) is a sequence of NUM_STAGE_EVENTS
     already-created torch.cuda.Event objects recorded at the stage
-    boundaries listed in include/moe.h."""
+    boundaries listed in include/moe.h.  n_group > 1 limits the routing to
+    the topk_group best expert groups (as router())."""
     _need(x, "x")
     if x.dim() != 2 or x.dtype not in _DT:
         raise ValueError("x must be [T, d] fp32 or bf16")
@@ -235,7 +242,7 @@ def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
     E = W_r.shape[0]
     _need(W_r, "W_r", torch.float32, (E, d), dev)
     _need(b, "b", torch.float32, (E,), dev)
-    D, W = _weights_desc(weights, T, d, E, K, scale, dt, dev, n_shared)
+    D, W = _weights_desc(weights, T, d, E, K, scale, dt, dev, n_shared, n_group, topk_group)
     nbytes = workspace_size(D, True)
     if nbytes == 0:
         raise MoeError("moe_workspace_size", 2)

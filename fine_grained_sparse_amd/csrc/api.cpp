@@ -32,6 +32,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Plan {
     int T, d, E, K, F, ns, Fs, dl, din, Fsh;  // Fsh = n_shared * F_shared
+    int ng, tg;                               // expert groups, groups kept (1, 1: plain top-K)
     float scale;
     int64_t A;                                // assignments T*K
     DType dt;
@@ -61,6 +62,12 @@ moe_status check_desc(const moe_layer_desc* D, bool forward) {
     if (D->T < 0 || D->E < 1 || D->E > 1024 || D->K < 1 || D->K > 16 || D->K > D->E) return MOE_ERR_SHAPE;
     if (D->d <= 0 || D->d % 64) return MOE_ERR_SHAPE;
     if (static_cast<int64_t>(D->T) * D->K >= (int64_t{1} << 31)) return MOE_ERR_SHAPE;
+    if (D->n_group > 1) {  // group-limited choice
+        if (D->n_group > 64 || D->E % D->n_group || D->E / D->n_group < 2) return MOE_ERR_SHAPE;
+        if (D->topk_group < 1 || D->topk_group > D->n_group) return MOE_ERR_SHAPE;
+    } else if (D->n_group < 0) {
+        return MOE_ERR_SHAPE;
+    }
     if (static_cast<int64_t>(D->T) * D->d >= (int64_t{1} << 40)) return MOE_ERR_SHAPE;
     if (forward) {
         if (D->F <= 0 || D->F % 64) return MOE_ERR_SHAPE;
@@ -78,6 +85,8 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
     p.E = D->E;
     p.K = D->K;
     p.scale = D->scale;
+    p.ng = D->n_group > 1 ? D->n_group : 1;
+    p.tg = D->n_group > 1 ? D->topk_group : 1;
     p.F = forward ? D->F : 0;
     p.ns = forward ? D->n_shared : 0;
     p.Fs = p.ns ? D->F_shared : 0;
@@ -186,7 +195,7 @@ moe_status run_router(const Plan& p, const void* x, const float* W_r, const floa
     g.split_stride = static_cast<int64_t>(p.T) * p.ldz;
     MOE_HIP(launch_gemm(g, p.dt, true, EPI_STORE, p.rcfg, p.rtiles, p.E, false, s));
     if (counts_atomic) MOE_HIP(launch_fill_i32(counts_atomic, 0, p.E, s));
-    MOE_HIP(launch_topk_gate(z, p.nsplit, g.split_stride, p.ldz, b, p.T, p.E, p.K, p.scale, idx, w,
+    MOE_HIP(launch_topk_gate(z, p.nsplit, g.split_stride, p.ldz, b, p.T, p.E, p.K, p.ng, p.tg, p.scale, idx, w,
                              counts_atomic, s));
     return MOE_OK;
 }

@@ -81,12 +81,14 @@ hipError_t launch_pack_frag16(const uint16_t* src, uint16_t* dst, int64_t count,
 hipError_t launch_split3(const float* W, int64_t n, uint16_t* hi,
                          uint16_t* mid, uint16_t* lo, hipStream_t stream);
 
-// Sigmoid, biased top-K, renormalise and scale; z holds nsplit partial
+// Sigmoid, biased top-K (limited to the topk_group best of n_group expert
+// groups when n_group > 1), renormalise and scale; z holds nsplit partial
 // logit planes of [T, ldz].  counts (nullable) gets +1 per selection.
 hipError_t launch_topk_gate(const float* z, int nsplit, int64_t split_stride,
                             int ldz, const float* b, int T, int E, int K,
-                            float scale, int32_t* idx, float* w,
-                            int32_t* counts, hipStream_t stream);
+                            int n_group, int topk_group, float scale,
+                            int32_t* idx, float* w, int32_t* counts,
+                            hipStream_t stream);
 
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n,
                            hipStream_t stream);

@@ -1,6 +1,7 @@
 // Router kernels of the MoE layer (OpenModelAtlas "Kimi K2 · Router": the
 // four steps z = x W_r, s = sigmoid(z), top-K of s + b, renormalised and
-// scaled weights; the MoEGate excerpt computes the logits in fp32).
+// scaled weights; the MoEGate excerpt computes the logits in fp32 and, with
+// more than one expert group, limits the choice to the best groups).
 //
 // The logits themselves come from the grouped GEMM (gemm.hip).  For bf16
 // activations the fp32 router weight is split exactly into three bf16
@@ -47,10 +48,69 @@ __device__ __forceinline__ bool better(float v, int e, float bv, int be) {
 // them), so inside a lane the expert index rises with j.  K rounds of a
 // wave-wide (value, index) arg-max pick the set; slot order is then the
 // ascending expert id (rank of each pick among the picks).
+// Group-limited choice (router card, MoEGate excerpt, noaux_tc branch):
+// the E experts form n_group contiguous groups of `per`; a group scores the
+// sum of its two largest biased scores; the topk_group best groups are kept
+// (ties toward the lower group index); every expert of a dropped group
+// takes the value 0.0 (the excerpt's masked_fill), the others keep theirs.
+// n_group <= 64: lane g ends up holding group g's score.
+template <int J>
+__device__ __forceinline__ void limit_to_groups(float (&v)[J], int lane, int E, int n_group, int per,
+                                                int topk_group) {
+    float gscore = -INFINITY;
+    for (int g = 0; g < n_group; ++g) {
+        float m1 = -INFINITY, m2 = -INFINITY;  // two largest of this lane's members of g
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int e = j * 64 + lane;
+            if (e < E && e / per == g) {
+                if (v[j] > m1) {
+                    m2 = m1;
+                    m1 = v[j];
+                } else if (v[j] > m2) {
+                    m2 = v[j];
+                }
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {  // merge the lanes' pairs
+            const float o1 = __shfl_xor(m1, off), o2 = __shfl_xor(m2, off);
+            const float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
+            m1 = fmaxf(m1, o1);
+            m2 = n2;
+        }
+        if (lane == g) gscore = m1 + m2;
+    }
+    bool kept = false;
+    for (int k = 0; k < topk_group; ++k) {
+        const bool cand = lane < n_group && !kept;
+        float bv = cand ? gscore : -INFINITY;
+        int bg = cand ? lane : 0x7fffffff;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int og = __shfl_xor(bg, off);
+            if (ov > bv || (ov == bv && og < bg)) {
+                bv = ov;
+                bg = og;
+            }
+        }
+        if (lane == bg) kept = true;
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int e = j * 64 + lane;
+        const int g = (e < E ? e : E - 1) / per;
+        const bool keep = __shfl(kept ? 1 : 0, g) != 0;
+        if (e < E && !keep) v[j] = 0.0f;
+    }
+}
+
 template <int J>
 __global__ __launch_bounds__(256) void k_topk_gate(const float* __restrict__ z, int nsplit, int64_t split_stride,
                                                    int ldz, const float* __restrict__ b, int T, int E, int K,
-                                                   float scale, int32_t* __restrict__ idx, float* __restrict__ w,
+                                                   int n_group, int topk_group, float scale,
+                                                   int32_t* __restrict__ idx, float* __restrict__ w,
                                                    int32_t* __restrict__ counts) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -73,6 +133,7 @@ __global__ __launch_bounds__(256) void k_topk_gate(const float* __restrict__ z, 
             v[j] = -INFINITY;
         }
     }
+    if (n_group > 1) limit_to_groups<J>(v, lane, E, n_group, E / n_group, topk_group);
     uint32_t taken = 0;
     int my_e = 0;
     float my_s = 0.f, den = 0.f;
@@ -137,20 +198,28 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t stream)
 }
 
 hipError_t launch_topk_gate(const float* z, int nsplit, int64_t split_stride, int ldz, const float* b, int T, int E,
-                            int K, float scale, int32_t* idx, float* w, int32_t* counts, hipStream_t stream) {
+                            int K, int n_group, int topk_group, float scale, int32_t* idx, float* w, int32_t* counts,
+                            hipStream_t stream) {
     if (T <= 0) return hipSuccess;
+    if (n_group < 1 || n_group > 64 || E % n_group || topk_group < 1 || topk_group > n_group ||
+        (n_group > 1 && E / n_group < 2))
+        return hipErrorInvalidValue;
     const dim3 grid((T + 3) / 4), block(256);
     const int J = (E + 63) / 64;
+#define MOE_TOPK(JJ)                                                                                           \
+    hipLaunchKernelGGL(k_topk_gate<JJ>, grid, block, 0, stream, z, nsplit, split_stride, ldz, b, T, E, K, n_group, \
+                       topk_group, scale, idx, w, counts)
     if (J <= 1)
-        hipLaunchKernelGGL(k_topk_gate<1>, grid, block, 0, stream, z, nsplit, split_stride, ldz, b, T, E, K, scale, idx, w, counts);
+        MOE_TOPK(1);
     else if (J <= 2)
-        hipLaunchKernelGGL(k_topk_gate<2>, grid, block, 0, stream, z, nsplit, split_stride, ldz, b, T, E, K, scale, idx, w, counts);
+        MOE_TOPK(2);
     else if (J <= 4)
-        hipLaunchKernelGGL(k_topk_gate<4>, grid, block, 0, stream, z, nsplit, split_stride, ldz, b, T, E, K, scale, idx, w, counts);
+        MOE_TOPK(4);
     else if (J <= 8)
-        hipLaunchKernelGGL(k_topk_gate<8>, grid, block, 0, stream, z, nsplit, split_stride, ldz, b, T, E, K, scale, idx, w, counts);
+        MOE_TOPK(8);
     else
-        hipLaunchKernelGGL(k_topk_gate<16>, grid, block, 0, stream, z, nsplit, split_stride, ldz, b, T, E, K, scale, idx, w, counts);
+        MOE_TOPK(16);
+#undef MOE_TOPK
     return hipGetLastError();
 }
 

@@ -77,6 +77,8 @@ typedef struct {
                        /* must equal act_dtype (W_r and b are always fp32)    */
     int32_t w_layout;  /* moe_weight_layout of those weights (bf16 may be     */
                        /* MOE_LAYOUT_FRAG16; fp32 must be MOE_LAYOUT_ROWS)    */
+    int32_t n_group;   /* group-limited choice: expert groups (0 or 1: none)  */
+    int32_t topk_group;/* groups kept per token when n_group > 1              */
 } moe_layer_desc;
 
 /* Storage of the expert, shared and latent weight matrices.
@@ -113,7 +115,13 @@ size_t moe_workspace_size(const moe_layer_desc *desc, int for_forward);
  *   x [T, d] (act_dtype), W_r [E, d] fp32, b [E] fp32
  *   -> topk_idx [T, K] int32 (ascending expert id within each token),
  *      topk_w [T, K] fp32, expert_counts [E] int32 (nullable: tokens per
- *      expert).                                                              */
+ *      expert).
+ * With n_group > 1 (the excerpt's group-limited branch): the experts form
+ * n_group contiguous groups, a group scores the sum of its two largest
+ * s + b, the topk_group best groups are kept (ties toward the lower group
+ * index) and the experts of the other groups compete with the value 0.0
+ * (the excerpt's masked_fill) in the top-K.  Requires n_group <= 64,
+ * E % n_group == 0, E / n_group >= 2 and 1 <= topk_group <= n_group.        */
 moe_status moe_router(const moe_layer_desc *desc, const void *x,
                       const float *W_r, const float *b, int32_t *topk_idx,
                       float *topk_w, int32_t *expert_counts, void *workspace,

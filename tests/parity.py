@@ -102,3 +102,32 @@ def frag16_reference(w):
     n = len(lead)
     perm = list(range(n)) + [n + 0, n + 2, n + 3, n + 1, n + 4]   # (i, j, c/8, r, c%8)
     return v.permute(*perm).reshape(w.shape)
+
+
+def effective_routing_grouped(ref, gpu_idx, gpu_w, K, scale):
+    """effective_routing for the group-limited choice.  A token is near a tie
+    when its K-th / (K+1)-th masked values or its last kept / first dropped
+    group scores (oracle, fp64) differ by less than TIE; only such tokens may
+    differ, and then the GPU set must be K distinct ascending ids whose
+    weights follow the definition on that set."""
+    gi = np.asarray(gpu_idx)
+    gw = np.asarray(gpu_w, np.float64)
+    E = ref["scores"].shape[1]
+    idx_eff = ref["idx"].copy()
+    w_eff = ref["w"].copy()
+    s = ref["scores"]
+    scale64 = float(np.float32(scale))
+    near = (ref["gap"] < TIE) | (ref["group_gap"] < TIE)
+    differ = np.any(gi != ref["idx"], axis=1)
+    assert not np.any(differ & ~near), (
+        f"{int(np.sum(differ & ~near))} tokens select a different set with margins >= {TIE}: "
+        f"first {np.nonzero(differ & ~near)[0][:5]}")
+    for t in np.nonzero(differ)[0]:
+        sel = gi[t]
+        assert np.all(np.diff(sel) > 0) and sel.min() >= 0 and sel.max() < E, f"token {t}: {sel}"
+        idx_eff[t] = sel
+        w_eff[t] = s[t, sel] / (s[t, sel].sum() + 1e-20) * scale64
+    err = np.abs(gw - w_eff) / np.abs(w_eff)
+    assert err.max() <= WTOL, f"gate weight rel err {err.max():.3g} > {WTOL}"
+    return idx_eff, w_eff, dict(near_tie=int(near.sum()), differ=int(differ.sum()),
+                                w_max_rel=float(err.max()))

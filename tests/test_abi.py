@@ -93,6 +93,14 @@ def test_router_rejects_bad_arguments():
     assert _router(_k2(E=2000)) == SHAPE
     assert _router(_k2(d=7000)) == SHAPE
     assert _router(_k2(act_dtype=3)) == UNSUP
+    # group-limited choice: groups must split E, hold >= 2 experts, <= 64 groups
+    assert _router(_k2(n_group=5, topk_group=2)) == SHAPE      # 384 % 5 != 0
+    assert _router(_k2(n_group=128, topk_group=2)) == SHAPE    # more than 64 groups
+    assert _router(_k2(n_group=8, topk_group=0)) == SHAPE
+    assert _router(_k2(n_group=8, topk_group=9)) == SHAPE
+    assert _router(_k2(n_group=-1)) == SHAPE
+    assert _router(_k2(E=8, K=2, n_group=8, topk_group=2)) == SHAPE  # one expert per group
+    assert moe.workspace_size(_k2(n_group=8, topk_group=4), True) == moe.workspace_size(_k2(), True)
     assert moe.lib().moe_router(None, None, None, None, None, None, None, None, 0, None) == NULL
 
 

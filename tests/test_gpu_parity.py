@@ -10,8 +10,8 @@ import torch
 import fine_grained_sparse_amd as moe
 import oracle
 from moe_inputs import Workload, get_workload, make_layer_inputs, make_router_inputs
-from parity import (TIE, check_dispatch, effective_routing, expert_weights, host, log,
-                    rel_l2, weights_to_device)
+from parity import (TIE, check_dispatch, effective_routing, effective_routing_grouped,
+                    expert_weights, host, log, rel_l2, weights_to_device)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -101,6 +101,57 @@ def test_router_all_tied_and_K1():
     dev = weights_to_device(inp, DEV)
     idx1, w1, _ = moe.router(dev["x"], dev["W_r"], dev["b"], 1)
     assert torch.all(w1.cpu() == torch.tensor(np.float32(2.827)))
+
+
+# ---------------------------------------------------------------- group-limited choice
+@pytest.mark.parametrize("name,T,n_group,topk_group,bias", [
+    ("tiny_fp32_t128", None, 4, 2, None),
+    ("mid_bf16_t300", None, 8, 3, None),
+    ("mid_bf16_t300", None, 6, 2, 0.6),        # biased scores below zero: the 0.0 fill matters
+    ("k2_router_t4096", 2048, 8, 4, None),
+    ("k2_router_t4096", 1024, 64, 13, None),
+    ("k3_latent_t4096", 512, 8, 4, None),
+])
+def test_router_grouped_parity(name, T, n_group, topk_group, bias):
+    wl = get_workload(name)
+    log(f"[gpu] grouped router {name} T={T or wl.T} groups {n_group}/{topk_group} bias={bias}")
+    r = make_router_inputs(wl, "cpu", seed=13, T=T)
+    if bias is not None:
+        g = torch.Generator().manual_seed(17)
+        r["b"] = (torch.rand(wl.E, generator=g) * 2 - 1) * bias - 0.45
+    ref = oracle.router_grouped(r["x"], r["W_r"], r["b"], wl.K, wl.scale, n_group, topk_group,
+                                want_scores=True)
+    dev = weights_to_device(r, DEV)
+    idx, w, counts = moe.router(dev["x"], dev["W_r"], dev["b"], wl.K, wl.scale,
+                                n_group=n_group, topk_group=topk_group)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    _, _, st = effective_routing_grouped(ref, gi, w.cpu().numpy(), wl.K, wl.scale)
+    assert np.array_equal(np.bincount(gi.ravel(), minlength=wl.E), counts.cpu().numpy())
+    if bias is not None:  # the case is exercised: many biased scores are below the 0.0 fill
+        v = ref["scores"] + r["b"].double().numpy()[None, :]
+        assert (v < 0).mean() > 0.2
+    log(f"  near_tie={st['near_tie']} differ={st['differ']} w_max_rel={st['w_max_rel']:.2e}")
+    assert st["near_tie"] <= max(3, (T or wl.T) // 100)
+
+
+def test_forward_with_grouped_routing():
+    wl = get_workload("mid_bf16_t300")
+    log("[gpu] forward mid_bf16_t300 with 8 groups / 3 kept")
+    inp = make_layer_inputs(wl, "cpu", seed=42)
+    dev = weights_to_device(inp, DEV)
+    out, r = moe.forward(dev["x"], dev["W_r"], dev["b"], expert_weights(dev), wl.K, wl.scale,
+                         n_shared=wl.n_shared, return_routing=True, n_group=8, topk_group=3)
+    torch.cuda.synchronize()
+    ref = oracle.router_grouped(inp["x"], inp["W_r"], inp["b"], wl.K, wl.scale, 8, 3,
+                                want_scores=True)
+    idx_eff, w_eff, _ = effective_routing_grouped(ref, r["idx"].cpu().numpy(),
+                                                  r["w"].cpu().numpy(), wl.K, wl.scale)
+    check_dispatch(r, wl.E)
+    out_ref = oracle.forward_given_routing(oracle.layer_from_inputs(wl, inp), inp["x"], idx_eff, w_eff)
+    err = rel_l2(out.float().cpu().numpy(), out_ref)
+    log(f"  rel_l2={err:.3e}")
+    assert err <= out_tol(wl)
 
 
 # ---------------------------------------------------------------- whole layer, every token
