@@ -46,12 +46,17 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+GEMM_SOURCES = ("api.cpp", "common.hpp", "gemm.hip", "launch.hpp")  # define or launch the GEMMs
+
+
 def source_hash() -> str:
-    """Hash of the HIP library sources with comments and whitespace removed:
-    counters taken on other code do not describe the kernels that run now."""
+    """Hash of the sources that define and launch the grouped GEMMs, with
+    comments and whitespace removed: counters taken on other code do not
+    describe the kernels that run now."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "fine_grained_sparse_amd", "csrc", "*"))):
-        if p.endswith((".hip", ".hpp", ".cpp")):
+    for name in GEMM_SOURCES:
+        p = os.path.join(ROOT, "fine_grained_sparse_amd", "csrc", name)
+        if os.path.exists(p):
             with open(p) as f:
                 code = f.read()
             code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
@@ -174,6 +179,7 @@ def measure_layer(moe, torch, wl, weights, steps, warmup, seed, layout):
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
+    per_step = sorted(evs[i][0].elapsed_time(evs[i][nev - 1]) for i in range(steps))
     stages = {}
     for j in range(1, nev):
         stages[moe.STAGES[j]] = sum(evs[i][j - 1].elapsed_time(evs[i][j]) for i in range(steps)) / steps
@@ -206,38 +212,49 @@ def measure_layer(moe, torch, wl, weights, steps, warmup, seed, layout):
                  touched_experts=wm["touched"],
                  hist_min_mean_max=[min(counts), round(sum(counts) / len(counts), 2), max(counts)])
     return dict(value=wl.T / layer_s, ms=ms, stages={k: round(v, 4) for k, v in stages.items()},
-                roofline=roof, layer=layer, inputs=(x, W_r, b))
+                roofline=roof, layer=layer, inputs=(x, W_r, b),
+                median_ms=round(per_step[len(per_step) // 2], 4), min_ms=round(per_step[0], 4))
 
 
 def measure_router(moe, torch, wl, steps, warmup, seed):
     """moe_router alone: logits (fp32 accumulation of the exact bf16 x bf16
-    products of x with the three bf16 planes of W_r), top-K gate, counts."""
+    products of x with the three bf16 planes of W_r), top-K gate, counts.
+    Its 70 MB of inputs would stay in the 256 MB MALL between calls, so a
+    512 MB buffer is written between timed calls (outside their events)."""
     from moe_inputs import make_router_inputs
     dev = torch.device("cuda:0")
     r_in = make_router_inputs(wl, dev, seed=seed)
     x, W_r, b = r_in["x"], r_in["W_r"], r_in["b"]
     ws = moe.Workspace()
     stream = torch.cuda.current_stream()
+    grp = dict(n_group=wl.n_group, topk_group=wl.topk_group)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     for _ in range(warmup):
-        moe.router(x, W_r, b, wl.K, wl.scale, workspace=ws, stream=stream)
+        moe.router(x, W_r, b, wl.K, wl.scale, workspace=ws, stream=stream, **grp)
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(steps):
-        moe.router(x, W_r, b, wl.K, wl.scale, workspace=ws, stream=stream)
-    t1.record(stream)
+    evs = [_events(torch, 2, stream) for _ in range(steps)]
+    for i in range(steps):
+        flush.fill_(i & 255)
+        evs[i][0].record(stream)
+        moe.router(x, W_r, b, wl.K, wl.scale, workspace=ws, stream=stream, **grp)
+        evs[i][1].record(stream)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    per_call = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    ms = sum(per_call) / steps
+    del flush
     fl = 2.0 * wl.T * wl.d * wl.E
     ach = fl / (ms * 1e-3) / 1e12
     return dict(value=round(wl.T / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 4),
+                median_ms=round(per_call[steps // 2], 4), min_ms=round(per_call[0], 4),
+                mall="512 MB written between calls",
                 roofline=dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_F32_TFLOPS,
                               unit="TFLOP/s", frac=round(ach / PEAK_F32_TFLOPS, 4), traffic=None,
                               kernel="router logits + top-K gate (fp32-accurate, bf16x3 MFMA)",
                               note="fp32 flops 2*T*d*E against the fp32 matrix peak; executed "
                                    "as 3 bf16 MFMA passes",
                               executed_bf16_tflops=round(3 * ach, 2)),
-                config=dict(workload=wl.name, T=wl.T, d=wl.d, E=wl.E, K=wl.K))
+                config=dict(workload=wl.name, T=wl.T, d=wl.d, E=wl.E, K=wl.K, n_group=wl.n_group,
+                            topk_group=wl.topk_group))
 
 
 def cpu_baseline(torch, wl, weights, x, W_r, b, target_s, seed):
@@ -322,7 +339,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="k2_prefill_t16384")
-    ap.add_argument("--also", default="k2_decode_t256,k2_router_t4096,k3_latent_t4096",
+    ap.add_argument("--also", default="k2_decode_t256,k2_router_t4096,k2_router_g8_t4096,k3_latent_t4096",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="target seconds of oracle time (0 skips the CPU baseline)")
@@ -385,7 +402,7 @@ def main():
         awl = get_workload(name)
         log(f"[bench] timing {name}")
         if awl.router_only:
-            r = measure_router(moe, torch, awl, max(args.steps, 50), args.warmup, args.seed)
+            r = measure_router(moe, torch, awl, max(args.steps, 100), args.warmup, args.seed)
             log(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step")
             also[name] = r
             continue
@@ -398,9 +415,11 @@ def main():
             weights = prepare(moe, torch, awl, make_expert_weights(awl, "cuda:0", seed=args.seed),
                               args.layout)
             wl = awl
-        r = measure_layer(moe, torch, awl, weights, max(args.steps, 20), args.warmup, args.seed, args.layout)
+        n_steps = max(args.steps, 50 if awl.T <= 1024 else 20)   # decode-sized: more, shorter steps
+        r = measure_layer(moe, torch, awl, weights, n_steps, args.warmup, args.seed, args.layout)
         log(f"[bench] {name}: {r['ms']:.3f} ms/step, stages {r['stages']}")
         also[name] = dict(value=round(r["value"], 1), unit="tokens/s", ms_per_step=round(r["ms"], 4),
+                          median_ms=r["median_ms"], min_ms=r["min_ms"],
                           roofline=r["roofline"], layer=r["layer"], stages_ms=r["stages"],
                           config=dict(workload=name, T=awl.T, d=awl.d, E=awl.E, K=awl.K,
                                       F=awl.F, n_shared=awl.n_shared, F_shared=awl.F_shared,
@@ -410,6 +429,7 @@ def main():
     line = {
         "metric": METRIC, "value": round(main_r["value"], 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(main_r["ms"], 4),
+        "median_ms": main_r["median_ms"], "min_ms": main_r["min_ms"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": mw.act_dtype,
         "data": "synthetic (seeded N(0,1) x, N(0,1/fan_in) weights, Zipf(1.1) expert skew)",
         "config": dict(workload=mw.name, T=mw.T, d=mw.d, E=mw.E, K=mw.K, F=mw.F,

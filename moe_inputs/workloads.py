@@ -30,6 +30,8 @@ class Workload:
     bias_range: float  # b ~ U(-bias_range, bias_range)
     zipf_skew: bool   # add a Zipf(1.1)-ranked logit offset (max 0.5) per expert
     router_only: bool  # the workload measures the router alone
+    n_group: int = 1   # group-limited choice: expert groups (1: plain top-K)
+    topk_group: int = 1  # groups kept per token when n_group > 1
 
     @property
     def d_in(self) -> int:
@@ -58,6 +60,10 @@ WORKLOADS = {
     # K2 router alone at 4096 tokens.
     "k2_router_t4096": Workload(name="k2_router_t4096", T=4096,
                                 router_only=True, **_K2),
+    # The K2 router alone with the group-limited choice of the router card's
+    # excerpt at 8 groups of 48 experts, 4 kept (the page's K2 uses one group).
+    "k2_router_g8_t4096": Workload(name="k2_router_g8_t4096", T=4096,
+                                   router_only=True, n_group=8, topk_group=4, **_K2),
     # K2 layer, decode-sized batch: weight streaming.
     "k2_decode_t256": Workload(name="k2_decode_t256", T=256,
                                router_only=False, **_K2),
