@@ -27,7 +27,8 @@ MOE_LAYOUT_ROWS, MOE_LAYOUT_FRAG16 = 0, 1
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
            4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_UNSUPPORTED", 6: "MOE_ERR_HIP"}
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
-EXPORTS = ("moe_workspace_size", "moe_router", "moe_forward", "moe_pack_weights", "moe_status_str")
+EXPORTS = ("moe_workspace_size", "moe_router", "moe_forward", "moe_pack_weights", "moe_bias_update",
+           "moe_status_str")
 WEIGHT_NAMES = ("W_gate", "W_up", "W_down", "Ws_gate", "Ws_up", "Ws_down", "W_lat_down", "W_lat_up")
 STAGES = ("start", "router", "dispatch", "latent", "up", "down", "end")
 NUM_STAGE_EVENTS = len(STAGES)
@@ -77,6 +78,8 @@ def lib():
         L.moe_pack_weights.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(ExpertWeights),
                                        ctypes.POINTER(ExpertWeights), vp]
         L.moe_pack_weights.restype = ctypes.c_int
+        L.moe_bias_update.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.c_float, vp]
+        L.moe_bias_update.restype = ctypes.c_int
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -200,6 +203,20 @@ def _weights_desc(weights, T, d, E, K, scale, dt, dev, n_shared, n_group=1, topk
     return D, W
 
 
+def bias_update(counts, b, gamma=1e-3, *, stream=None):
+    """moe_bias_update: b (fp32 [E], in place) += gamma * sgn(mean - counts)
+    from the per-expert selection counts (int32 [E]) of one or more
+    batches.  Returns b."""
+    _need(counts, "counts", torch.int32)
+    E = counts.numel()
+    _need(b, "b", torch.float32, (E,), counts.device)
+    D = desc(T=0, d=64, E=E, K=1)
+    rc = lib().moe_bias_update(ctypes.byref(D), _ptr(counts), _ptr(b), float(gamma), _stream(stream))
+    if rc:
+        raise MoeError("moe_bias_update", rc)
+    return b
+
+
 def pack_weights(weights, *, n_shared=None, stream=None):
     """moe_pack_weights: bf16 row-major weights -> a new dict of tensors of
     the same shapes in MOE_LAYOUT_FRAG16, with "layout" set.  Run once, e.g.
@@ -273,6 +290,6 @@ def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
     return (out, routing) if return_routing else out
 
 
-__all__ = ["router", "forward", "pack_weights", "workspace_size", "desc", "lib", "MoeError",
+__all__ = ["router", "forward", "pack_weights", "bias_update", "workspace_size", "desc", "lib", "MoeError",
            "LayerDesc", "ExpertWeights", "Workspace", "MOE_F32", "MOE_BF16", "MOE_LAYOUT_ROWS",
            "MOE_LAYOUT_FRAG16", "EXPORTS", "WEIGHT_NAMES"]

@@ -395,6 +395,16 @@ moe_status moe_forward(const moe_layer_desc* desc, const void* x, const float* W
                        workspace, s, stage_events);
 }
 
+moe_status moe_bias_update(const moe_layer_desc* desc, const int32_t* expert_counts, float* b, float gamma,
+                           void* stream) {
+    if (!desc) return MOE_ERR_NULL;
+    if (desc->E < 1 || desc->E > 1024) return MOE_ERR_SHAPE;
+    if (!expert_counts || !b) return MOE_ERR_NULL;
+    if (!aligned16(expert_counts) || !aligned16(b)) return MOE_ERR_ALIGN;
+    MOE_HIP(launch_bias_update(expert_counts, desc->E, gamma, b, static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
 moe_status moe_pack_weights(const moe_layer_desc* desc, const moe_expert_weights* src,
                             const moe_expert_weights* dst, void* stream) {
     if (!desc || !src || !dst) return MOE_ERR_NULL;

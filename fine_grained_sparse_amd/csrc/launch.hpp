@@ -77,6 +77,9 @@ hipError_t launch_gemm(const GemmArgs& args, DType dt, bool out_f32, Epi epi,
 hipError_t launch_pack_frag16(const uint16_t* src, uint16_t* dst, int64_t count, int rows, int cols,
                               hipStream_t stream);
 
+// b[e] += gamma * sgn(mean(counts) - counts[e]) for e < E (E <= 1024).
+hipError_t launch_bias_update(const int32_t* counts, int E, float gamma, float* b, hipStream_t stream);
+
 // W_r (fp32) -> three bf16 planes with hi + mid + lo == W_r exactly.
 hipError_t launch_split3(const float* W, int64_t n, uint16_t* hi,
                          uint16_t* mid, uint16_t* lo, hipStream_t stream);

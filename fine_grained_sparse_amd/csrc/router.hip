@@ -179,7 +179,37 @@ __global__ __launch_bounds__(256) void k_topk_gate(const float* __restrict__ z, 
     }
 }
 
+// Aux-loss-free bias update after a batch (llm-arch-kb "Kimi K2 MoE": the
+// selection bias follows DeepSeek V3's schedule, gamma = 1e-3, sign only):
+// b_e += gamma * sgn(mean count - c_e), the comparison taken exactly as
+// sum(c) - E c_e.  One block; thread e owns expert e (E <= 1024).
+__global__ __launch_bounds__(1024) void k_bias_update(const int32_t* __restrict__ counts, int E, float gamma,
+                                                      float* __restrict__ b) {
+    __shared__ long long part[16];
+    const int e = threadIdx.x, lane = e & 63, w = e >> 6;
+    long long c = e < E ? counts[e] : 0;
+    long long sum = c;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane == 0) part[w] = sum;
+    __syncthreads();
+    long long total = 0;
+    for (int i = 0; i < 16; ++i) total += part[i];
+    if (e < E) {
+        const long long diff = total - static_cast<long long>(E) * c;
+        const float sg = diff > 0 ? 1.0f : (diff < 0 ? -1.0f : 0.0f);
+        b[e] = b[e] + gamma * sg;  // gamma * sg is exact: one rounding
+    }
+}
+
 }  // namespace
+
+hipError_t launch_bias_update(const int32_t* counts, int E, float gamma, float* b, hipStream_t stream) {
+    if (E <= 0) return hipSuccess;
+    if (E > 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_bias_update, dim3(1), dim3(1024), 0, stream, counts, E, gamma, b);
+    return hipGetLastError();
+}
 
 hipError_t launch_split3(const float* W, int64_t n, uint16_t* hi, uint16_t* mid, uint16_t* lo, hipStream_t stream) {
     if (n <= 0) return hipSuccess;

@@ -164,6 +164,20 @@ moe_status moe_forward(const moe_layer_desc *desc, const void *x,
                        size_t workspace_bytes, void *stream,
                        void *const *stage_events);
 
+/* Aux-loss-free bias update after a batch [llm-arch-kb "Kimi K2 MoE"
+ * section 2: the selection bias follows DeepSeek V3's schedule, sign only,
+ * gamma = 1e-3; lilting.ch K3 essay: a per-expert load-adjustment bias].
+ * expert_counts [E] int32 are the batch's selections per expert (as
+ * moe_router / moe_forward return them, or summed over several batches);
+ * b [E] fp32 is updated in place:
+ *   b[e] += gamma * sgn(mean(expert_counts) - expert_counts[e])
+ * with sgn(0) = 0 and the comparison taken exactly (sum(c) - E c_e), so an
+ * expert above the mean load becomes less likely to be chosen.  Only E of
+ * the descriptor is used.                                                    */
+moe_status moe_bias_update(const moe_layer_desc *desc,
+                           const int32_t *expert_counts, float *b,
+                           float gamma, void *stream);
+
 /* Rewrite row-major bf16 weights into MOE_LAYOUT_FRAG16 (a pure
  * permutation of each matrix; done once, e.g. when a model is loaded).
  * Every non-NULL matrix of `src` (row-major, shapes from `desc`, whose

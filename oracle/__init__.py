@@ -52,9 +52,10 @@ def lib():
         L.oracle_router_grouped.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp,
                                             ctypes.c_float, vp, vp, vp, vp, vp, i32]
         L.oracle_dispatch.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+        L.oracle_bias_update.argtypes = [i32, vp, vp, ctypes.c_float, vp]
         L.oracle_forward_given_routing.argtypes = [vp, i32, vp, vp, vp, vp, i32]
         L.oracle_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32]
-        for f in (L.oracle_router, L.oracle_router_grouped, L.oracle_dispatch,
+        for f in (L.oracle_router, L.oracle_router_grouped, L.oracle_dispatch, L.oracle_bias_update,
                   L.oracle_forward_given_routing, L.oracle_forward):
             f.restype = ctypes.c_int
         _lib = L
@@ -146,6 +147,17 @@ def router_grouped(x, W_r, b, K, scale, n_group, topk_group, nthreads=None, want
                                      _ptr(ggap), _ptr(scores), nthreads or default_threads())
     _check(rc, "oracle_router_grouped")
     return dict(idx=idx, w=w, gap=gap, group_gap=ggap, scores=scores)
+
+
+def bias_update(counts, b, gamma=1e-3):
+    """Aux-loss-free sign update of the selection bias from per-expert counts;
+    returns the new fp32 bias (numpy)."""
+    c = np.ascontiguousarray(np.asarray(counts, np.int32))
+    bb = np.ascontiguousarray(np.asarray(b.numpy() if hasattr(b, "numpy") else b, np.float32))
+    out = np.zeros_like(bb)
+    _check(lib().oracle_bias_update(c.size, _ptr(c), _ptr(bb), float(gamma), _ptr(out)),
+           "oracle_bias_update")
+    return out
 
 
 def dispatch(idx, E):

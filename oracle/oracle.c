@@ -454,3 +454,29 @@ int oracle_forward(const oracle_layer *L, int32_t T, const void *x,
         free(w);
     return rc;
 }
+
+/* Aux-loss-free bias update [P1: the bias follows DeepSeek V3's schedule,
+ * gamma = 1e-3, sign-only; P4: the bias is a load-adjustment term].  With
+ * the batch's per-expert selection counts c_e and their mean
+ * cbar = sum(c) / E, an expert above the mean is made less attractive and
+ * one below it more: b_e <- b_e + gamma * sgn(cbar - c_e), sgn(0) = 0.  The
+ * comparison is taken exactly as sum(c) - E c_e in integers; the new bias is
+ * the fp32 rounding of the exact sum (the bias is an fp32 tensor). */
+int oracle_bias_update(int32_t E, const int32_t *counts, const float *b_in,
+                       float gamma, float *b_out)
+{
+    if (E <= 0)
+        return ORACLE_ERR_SHAPE;
+    if (!counts || !b_in || !b_out)
+        return ORACLE_ERR_NULL;
+    int64_t total = 0;
+    for (int32_t e = 0; e < E; ++e)
+        total += counts[e];
+    for (int32_t e = 0; e < E; ++e) {
+        int64_t diff = total - (int64_t)E * counts[e];
+        double sg = diff > 0 ? 1.0 : (diff < 0 ? -1.0 : 0.0);
+        b_out[e] = (float)((double)b_in[e] + (double)gamma * sg);
+    }
+    return ORACLE_OK;
+}
+

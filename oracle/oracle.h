@@ -103,6 +103,13 @@ int oracle_router_grouped(int32_t T, int32_t d, int32_t E, int32_t K,
                           double *gap, double *group_gap, double *scores,
                           int32_t nthreads);
 
+/* Aux-loss-free bias update after a batch [P1 sign-only, gamma = 1e-3;
+ * P4 load-adjustment bias]: b_out[e] = fp32(b_in[e] + gamma * sgn(cbar - c_e))
+ * with c the per-expert selection counts and cbar their mean (sgn(0) = 0,
+ * compared exactly as sum(c) - E c_e).  b_out may equal b_in.              */
+int oracle_bias_update(int32_t E, const int32_t *counts, const float *b_in,
+                       float gamma, float *b_out);
+
 int oracle_dispatch(int32_t T, int32_t E, int32_t K, const int32_t *topk_idx,
                     int32_t *counts, int32_t *offsets, int32_t *sorted_token,
                     int32_t *pos);

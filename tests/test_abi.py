@@ -30,8 +30,8 @@ def _declared():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == sorted(["moe_forward", "moe_pack_weights", "moe_router", "moe_status_str",
-                                  "moe_workspace_size"])
+    assert _declared() == sorted(["moe_bias_update", "moe_forward", "moe_pack_weights", "moe_router",
+                                  "moe_status_str", "moe_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -165,3 +165,14 @@ def test_zero_tokens_accepts_null_data_pointers():
     assert _router(D, x=None, W_r=None, b=None, idx=None, w=None, ws=None) == OK
     assert _forward(D, x=None, W_r=None, b=None, out=None, ws=None) == OK
     assert _forward(D, x=None, out=None, counts=FAKE_ODD) == ALIGN
+
+
+def test_bias_update_rejects_bad_arguments():
+    vp = ctypes.c_void_p
+    L = moe.lib()
+    assert L.moe_bias_update(None, vp(FAKE), vp(FAKE), 1e-3, None) == NULL
+    assert L.moe_bias_update(ctypes.byref(_k2()), None, vp(FAKE), 1e-3, None) == NULL
+    assert L.moe_bias_update(ctypes.byref(_k2()), vp(FAKE), None, 1e-3, None) == NULL
+    assert L.moe_bias_update(ctypes.byref(_k2()), vp(FAKE_ODD), vp(FAKE), 1e-3, None) == ALIGN
+    assert L.moe_bias_update(ctypes.byref(_k2(E=2000)), vp(FAKE), vp(FAKE), 1e-3, None) == SHAPE
+

@@ -154,6 +154,36 @@ def test_forward_with_grouped_routing():
     assert err <= out_tol(wl)
 
 
+# ---------------------------------------------------------------- bias update
+@pytest.mark.parametrize("E", [1, 7, 384, 896, 1024])
+def test_bias_update_parity(E):
+    log(f"[gpu] bias update E={E}")
+    g = torch.Generator().manual_seed(E)
+    counts = torch.randint(0, 50, (E,), generator=g, dtype=torch.int32)
+    if E >= 7:
+        counts[:3] = int(counts.float().mean().round())   # some near the mean
+        counts[3] = 0
+    b = (torch.rand(E, generator=g) - 0.5) * 0.1
+    ref = oracle.bias_update(counts.numpy(), b.numpy(), gamma=1e-3)
+    bd = b.to(DEV)
+    moe.bias_update(counts.to(DEV), bd, 1e-3)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bd.cpu().numpy(), ref)   # bit for bit
+
+
+def test_bias_update_from_the_layers_own_counts():
+    # the counts moe_forward returns feed the update directly
+    wl = get_workload("mid_bf16_t300")
+    log("[gpu] bias update from moe_forward counts")
+    dev = weights_to_device(make_layer_inputs(wl, "cpu", seed=42), DEV)
+    _, r = _run_forward(wl, dev)
+    b0 = dev["b"].clone()
+    moe.bias_update(r["counts"], dev["b"], 1e-3)
+    torch.cuda.synchronize()
+    ref = oracle.bias_update(r["counts"].cpu().numpy(), b0.cpu().numpy())
+    np.testing.assert_array_equal(dev["b"].cpu().numpy(), ref)
+
+
 # ---------------------------------------------------------------- whole layer, every token
 @pytest.mark.parametrize("name,packed", [("tiny_fp32_t128", False), ("mid_fp32_t77", False),
                                          ("mid_bf16_t300", False), ("mid_latent_t200", False),

@@ -492,3 +492,52 @@ def test_grouped_selection_matches_bruteforce_over_all_subsets():
         assert g["idx"][t].tolist() == list(best), t
         np.testing.assert_allclose(g["w"][t], s[t, list(best)] / s[t, list(best)].sum() * SCALE32,
                                    rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Aux-loss-free bias update (llm-arch-kb K2 entry: DeepSeek V3 schedule,
+# sign only, gamma = 1e-3; K3 essay: a per-expert load-adjustment bias)
+# --------------------------------------------------------------------------
+def test_bias_update_closed_forms():
+    g = np.float32(1e-3)
+    # one overloaded expert: it loses gamma, the others gain gamma
+    np.testing.assert_array_equal(oracle.bias_update([5, 1, 1, 1], np.zeros(4, np.float32)),
+                                  np.array([-g, g, g, g], np.float32))
+    # balanced load: nothing moves
+    b = np.array([0.3, -0.2, 0.0, 1.0], np.float32)
+    np.testing.assert_array_equal(oracle.bias_update([2, 2, 2, 2], b), b)
+    # a fractional mean (4/3): the comparison is exact, 2 > 4/3 > 1
+    np.testing.assert_array_equal(oracle.bias_update([2, 1, 1], np.zeros(3, np.float32)),
+                                  np.array([-g, g, g], np.float32))
+    # the new bias is the fp32 rounding of the exact sum (numpy's fp32 add is
+    # correctly rounded too)
+    b = np.array([1.0, 3.1e-4, -7.77], np.float32)
+    np.testing.assert_array_equal(oracle.bias_update([0, 9, 0], b),
+                                  np.array([b[0] + g, b[1] - g, b[2] + g], np.float32))
+
+
+def test_bias_updates_balance_a_skewed_router():
+    # What the update is for: repeated sign steps on a skewed router pull the
+    # per-expert loads toward the mean (a flipped sign would widen the skew).
+    wl = get_workload("tiny_fp32_t128")
+    r = make_router_inputs(wl, "cpu", seed=3)
+    W = r["W_r"].clone()
+    W[:, 0] += torch.linspace(-0.6, 0.6, wl.E)   # skew: higher-numbered experts win
+    x = r["x"].clone()
+    x[:, 0] = 1.0
+    b = np.zeros(wl.E, np.float32)
+
+    def load_spread(bias):
+        idx = oracle.router(x, W, torch.from_numpy(bias), wl.K, wl.scale)["idx"]
+        c = np.bincount(idx.ravel(), minlength=wl.E)
+        return c.max() / c.mean(), c
+
+    start, _ = load_spread(b)
+    for _ in range(60):
+        _, c = load_spread(b)
+        b = oracle.bias_update(c, b, gamma=0.02)
+    end, _ = load_spread(b)
+    assert start > 2.0 and end < 0.6 * start, (start, end)
+    # the bias went down for the experts the skew favoured
+    assert b[-4:].mean() < 0 < b[:4].mean()
+
