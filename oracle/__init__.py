@@ -53,9 +53,11 @@ def lib():
                                             ctypes.c_float, vp, vp, vp, vp, vp, i32]
         L.oracle_dispatch.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_bias_update.argtypes = [i32, vp, vp, ctypes.c_float, vp]
+        L.oracle_bias_quantile.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, i32]
         L.oracle_forward_given_routing.argtypes = [vp, i32, vp, vp, vp, vp, i32]
         L.oracle_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32]
         for f in (L.oracle_router, L.oracle_router_grouped, L.oracle_dispatch, L.oracle_bias_update,
+                  L.oracle_bias_quantile,
                   L.oracle_forward_given_routing, L.oracle_forward):
             f.restype = ctypes.c_int
         _lib = L
@@ -158,6 +160,22 @@ def bias_update(counts, b, gamma=1e-3):
     _check(lib().oracle_bias_update(c.size, _ptr(c), _ptr(bb), float(gamma), _ptr(out)),
            "oracle_bias_update")
     return out
+
+
+def bias_quantile(x, W_r, K, nthreads=None):
+    """Quantile Balancing bias (see oracle.h): returns (b [E] float64,
+    theta [E] float64)."""
+    xa, xdt = _host(x, "x")
+    Wa, _ = _host(W_r, "W_r")
+    if Wa.dtype != np.float32:
+        raise OracleError("W_r is fp32")
+    T, d = xa.shape
+    E = Wa.shape[0]
+    b = np.zeros((E,), np.float64)
+    theta = np.zeros((E,), np.float64)
+    _check(lib().oracle_bias_quantile(T, d, E, K, xdt, _ptr(xa), _ptr(Wa), _ptr(b), _ptr(theta),
+                                      nthreads or default_threads()), "oracle_bias_quantile")
+    return b, theta
 
 
 def dispatch(idx, E):

@@ -480,3 +480,62 @@ int oracle_bias_update(int32_t E, const int32_t *counts, const float *b_in,
     return ORACLE_OK;
 }
 
+static int cmp_desc(const void *a, const void *b)
+{
+    double x = *(const double *)a, y = *(const double *)b;
+    return (x < y) - (x > y);
+}
+
+/* Quantile Balancing [P4, the load-balancing paragraph: each expert's
+ * threshold for receiving its target number of tokens is read off a
+ * quantile of the router scores and sets the selection bias].  Reading:
+ * over the batch, s[t, e] = sigmoid(x_t . W_r[e]) (the unbiased router
+ * scores, as in oracle_router); every expert's target is the mean load
+ * n = max(1, floor(T K / E)) tokens; its threshold theta_e is the n-th
+ * largest of s[., e] (the expert would take exactly n tokens if it took
+ * those scoring at least theta_e); the bias puts every threshold on a common
+ * level: b_e = mean(theta) - theta_e, so the test s + b >= mean(theta) is
+ * s >= theta_e for each expert.  A common shift of b leaves every top-K
+ * unchanged, the mean keeps sum(b) = 0.  theta [E] (nullable) returns the
+ * thresholds.  Requires T >= 1. */
+int oracle_bias_quantile(int32_t T, int32_t d, int32_t E, int32_t K,
+                         int32_t x_dtype, const void *x, const float *W_r,
+                         double *b_out, double *theta, int32_t nthreads)
+{
+    if (T < 1 || d <= 0 || E <= 0 || K < 1 || K > E)
+        return ORACLE_ERR_SHAPE;
+    if (x_dtype != ORACLE_F32 && x_dtype != ORACLE_BF16)
+        return ORACLE_ERR_SHAPE;
+    if (!x || !W_r || !b_out)
+        return ORACLE_ERR_NULL;
+    int64_t n = ((int64_t)T * K) / E;
+    if (n < 1)
+        n = 1;
+    double *th = (double *)malloc(sizeof(double) * (size_t)E);
+    int nt = nthreads > 0 ? nthreads : 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int32_t e = 0; e < E; ++e) {
+        double *col = (double *)malloc(sizeof(double) * (size_t)T);
+        for (int32_t t = 0; t < T; ++t) {
+            double z = 0.0;
+            for (int32_t j = 0; j < d; ++j)
+                z += elem(x, x_dtype, (size_t)t * d + (size_t)j) * (double)W_r[(size_t)e * d + j];
+            col[t] = sigmoid(z);
+        }
+        qsort(col, (size_t)T, sizeof(double), cmp_desc);
+        th[e] = col[n - 1];
+        free(col);
+    }
+    double mean = 0.0;
+    for (int32_t e = 0; e < E; ++e)
+        mean += th[e];
+    mean /= (double)E;
+    for (int32_t e = 0; e < E; ++e) {
+        b_out[e] = mean - th[e];
+        if (theta)
+            theta[e] = th[e];
+    }
+    free(th);
+    return ORACLE_OK;
+}
+

@@ -110,6 +110,14 @@ int oracle_router_grouped(int32_t T, int32_t d, int32_t E, int32_t K,
 int oracle_bias_update(int32_t E, const int32_t *counts, const float *b_in,
                        float gamma, float *b_out);
 
+/* Quantile Balancing [P4 load-balancing paragraph], this reading: with
+ * s = sigmoid(x W_r^T) over the batch and the mean load
+ * n = max(1, floor(T K / E)), theta_e = the n-th largest s[., e] and
+ * b_out[e] = mean(theta) - theta_e (sum zero).  theta [E] nullable.        */
+int oracle_bias_quantile(int32_t T, int32_t d, int32_t E, int32_t K,
+                         int32_t x_dtype, const void *x, const float *W_r,
+                         double *b_out, double *theta, int32_t nthreads);
+
 int oracle_dispatch(int32_t T, int32_t E, int32_t K, const int32_t *topk_idx,
                     int32_t *counts, int32_t *offsets, int32_t *sorted_token,
                     int32_t *pos);

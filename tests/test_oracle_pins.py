@@ -541,3 +541,59 @@ def test_bias_updates_balance_a_skewed_router():
     # the bias went down for the experts the skew favoured
     assert b[-4:].mean() < 0 < b[:4].mean()
 
+
+
+# --------------------------------------------------------------------------
+# Quantile Balancing (K3 essay, load-balancing paragraph), this reading:
+# theta_e = the n-th largest router score of expert e over the batch with
+# n = max(1, floor(T K / E)); b_e = mean(theta) - theta_e
+# --------------------------------------------------------------------------
+def _logit(p):
+    return math.log(p / (1.0 - p))
+
+
+def test_quantile_bias_closed_form():
+    # E = 2, T = 4, K = 1: n = 2.  x_t = (logit s0_t, logit s1_t), W_r = I.
+    #   s[:, 0] = (.9, .8, .3, .1) -> theta_0 = .8
+    #   s[:, 1] = (.6, .5, .4, .2) -> theta_1 = .5;  mean .65 -> b = (-.15, .15)
+    s0, s1 = [0.9, 0.8, 0.3, 0.1], [0.6, 0.5, 0.4, 0.2]
+    x = _f32([[_logit(a), _logit(c)] for a, c in zip(s0, s1)])
+    b, th = oracle.bias_quantile(x, _f32([[1.0, 0.0], [0.0, 1.0]]), 1)
+    np.testing.assert_allclose(th, [0.8, 0.5], rtol=1e-6)
+    np.testing.assert_allclose(b, [-0.15, 0.15], atol=1e-6)
+
+
+def test_quantile_thresholds_are_the_order_statistics():
+    # the defining property: at least n tokens score >= theta_e and fewer
+    # than n score above it; and the bias sums to zero
+    wl = get_workload("tiny_fp32_t128")
+    r = make_router_inputs(wl, "cpu", seed=8)
+    b, th = oracle.bias_quantile(r["x"], r["W_r"], wl.K)
+    s = oracle.router(r["x"], r["W_r"], r["b"], wl.K, wl.scale, want_scores=True)["scores"]
+    n = max(1, wl.T * wl.K // wl.E)
+    assert np.all((s >= th[None, :]).sum(0) >= n)
+    assert np.all((s > th[None, :]).sum(0) < n)
+    assert abs(b.sum()) < 1e-12
+    # a batch of every token twice keeps each threshold when T K / E is whole
+    assert (wl.T * wl.K) % wl.E == 0
+    x2 = torch.cat([r["x"], r["x"]])
+    _, th2 = oracle.bias_quantile(x2, r["W_r"], wl.K)
+    np.testing.assert_array_equal(th2, th)
+
+
+def test_quantile_bias_balances_a_skewed_router():
+    wl = get_workload("tiny_fp32_t128")
+    r = make_router_inputs(wl, "cpu", seed=3)
+    W = r["W_r"].clone()
+    W[:, 0] += torch.linspace(-0.6, 0.6, wl.E)
+    x = r["x"].clone()
+    x[:, 0] = 1.0
+
+    def spread(bias):
+        idx = oracle.router(x, W, torch.from_numpy(np.asarray(bias, np.float32)), wl.K, wl.scale)["idx"]
+        c = np.bincount(idx.ravel(), minlength=wl.E)
+        return c.max() / c.mean()
+
+    b, _ = oracle.bias_quantile(x, W, wl.K)
+    before, after = spread(np.zeros(wl.E)), spread(b)
+    assert before > 2.0 and after < 0.6 * before, (before, after)
