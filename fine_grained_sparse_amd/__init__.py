@@ -28,7 +28,7 @@ _STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN
            4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_UNSUPPORTED", 6: "MOE_ERR_HIP"}
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 EXPORTS = ("moe_workspace_size", "moe_router", "moe_forward", "moe_pack_weights", "moe_bias_update",
-           "moe_status_str")
+           "moe_bias_quantile", "moe_status_str")
 WEIGHT_NAMES = ("W_gate", "W_up", "W_down", "Ws_gate", "Ws_up", "Ws_down", "W_lat_down", "W_lat_up")
 STAGES = ("start", "router", "dispatch", "latent", "up", "down", "end")
 NUM_STAGE_EVENTS = len(STAGES)
@@ -80,6 +80,8 @@ def lib():
         L.moe_pack_weights.restype = ctypes.c_int
         L.moe_bias_update.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, ctypes.c_float, vp]
         L.moe_bias_update.restype = ctypes.c_int
+        L.moe_bias_quantile.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.moe_bias_quantile.restype = ctypes.c_int
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -217,6 +219,32 @@ def bias_update(counts, b, gamma=1e-3, *, stream=None):
     return b
 
 
+def bias_quantile(x, W_r, K, *, out=None, workspace=None, stream=None):
+    """moe_bias_quantile: the Quantile Balancing bias of a batch (fp32 [E]):
+    b_e = mean(theta) - theta_e with theta_e the n-th largest router score of
+    expert e, n = max(1, T K // E)."""
+    _need(x, "x")
+    if x.dim() != 2 or x.dtype not in _DT:
+        raise ValueError("x must be [T, d] fp32 or bf16")
+    T, d = x.shape
+    dev = x.device
+    _need(W_r, "W_r", torch.float32, device=dev)
+    E = W_r.shape[0]
+    _need(W_r, "W_r", torch.float32, (E, d))
+    D = desc(T=T, d=d, E=E, K=K, act_dtype=_DT[x.dtype])
+    nbytes = workspace_size(D, False)
+    if nbytes == 0:
+        raise MoeError("moe_workspace_size", 2)
+    b = torch.empty((E,), dtype=torch.float32, device=dev) if out is None else out
+    _need(b, "out", torch.float32, (E,), dev)
+    ws = (workspace or _default_ws).get(dev, nbytes)
+    rc = lib().moe_bias_quantile(ctypes.byref(D), _ptr(x), _ptr(W_r), _ptr(b), _ptr(ws), nbytes,
+                                 _stream(stream))
+    if rc:
+        raise MoeError("moe_bias_quantile", rc)
+    return b
+
+
 def pack_weights(weights, *, n_shared=None, stream=None):
     """moe_pack_weights: bf16 row-major weights -> a new dict of tensors of
     the same shapes in MOE_LAYOUT_FRAG16, with "layout" set.  Run once, e.g.
@@ -290,6 +318,6 @@ def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
     return (out, routing) if return_routing else out
 
 
-__all__ = ["router", "forward", "pack_weights", "bias_update", "workspace_size", "desc", "lib", "MoeError",
+__all__ = ["router", "forward", "pack_weights", "bias_update", "bias_quantile", "workspace_size", "desc", "lib", "MoeError",
            "LayerDesc", "ExpertWeights", "Workspace", "MOE_F32", "MOE_BF16", "MOE_LAYOUT_ROWS",
            "MOE_LAYOUT_FRAG16", "EXPORTS", "WEIGHT_NAMES"]

@@ -47,7 +47,7 @@ struct Plan {
     TileCfg dcfg;                             // dense GEMMs (latent maps)
     // workspace offsets (bytes); -1 = absent
     int64_t o_planes, o_z, o_idx, o_w, o_counts, o_offsets, o_masks, o_cbase, o_sorted, o_pos, o_tiles,
-        o_ntiles, o_xlat, o_H, o_Hs, o_Y, o_R, total;
+        o_ntiles, o_xlat, o_H, o_Hs, o_Y, o_R, o_theta, total;
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -132,6 +132,7 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
     p.o_idx = take(p.A * 4);
     p.o_w = take(p.A * 4);
     p.o_counts = take(E * 4);
+    p.o_theta = take(E * 4);
     p.o_offsets = p.o_masks = p.o_cbase = p.o_sorted = p.o_pos = p.o_tiles = p.o_ntiles = -1;
     p.o_xlat = p.o_H = p.o_Hs = p.o_Y = p.o_R = -1;
     if (forward) {
@@ -169,9 +170,8 @@ GemmArgs gemm_args() {
     return a;
 }
 
-// Router: logits (split-K partial planes) then the top-K gate.
-moe_status run_router(const Plan& p, const void* x, const float* W_r, const float* b, int32_t* idx, float* w,
-                      int32_t* counts_atomic, void* ws, hipStream_t s) {
+// Router logits into the split-K partial planes of the workspace.
+moe_status run_logits(const Plan& p, const void* x, const float* W_r, void* ws, hipStream_t s) {
     float* z = at<float>(ws, p.o_z);
     GemmArgs g = gemm_args();
     GemmGroup& G = g.g[0];
@@ -194,9 +194,19 @@ moe_status run_router(const Plan& p, const void* x, const float* W_r, const floa
     g.nsplit = p.nsplit;
     g.split_stride = static_cast<int64_t>(p.T) * p.ldz;
     MOE_HIP(launch_gemm(g, p.dt, true, EPI_STORE, p.rcfg, p.rtiles, p.E, false, s));
+    return MOE_OK;
+}
+
+int64_t split_stride(const Plan& p) { return static_cast<int64_t>(p.T) * p.ldz; }
+
+// Router: logits, then the top-K gate.
+moe_status run_router(const Plan& p, const void* x, const float* W_r, const float* b, int32_t* idx, float* w,
+                      int32_t* counts_atomic, void* ws, hipStream_t s) {
+    moe_status st = run_logits(p, x, W_r, ws, s);
+    if (st != MOE_OK) return st;
     if (counts_atomic) MOE_HIP(launch_fill_i32(counts_atomic, 0, p.E, s));
-    MOE_HIP(launch_topk_gate(z, p.nsplit, g.split_stride, p.ldz, b, p.T, p.E, p.K, p.ng, p.tg, p.scale, idx, w,
-                             counts_atomic, s));
+    MOE_HIP(launch_topk_gate(at<float>(ws, p.o_z), p.nsplit, split_stride(p), p.ldz, b, p.T, p.E, p.K, p.ng, p.tg,
+                             p.scale, idx, w, counts_atomic, s));
     return MOE_OK;
 }
 
@@ -393,6 +403,24 @@ moe_status moe_forward(const moe_layer_desc* desc, const void* x, const float* W
     if (workspace_bytes < static_cast<size_t>(p.total)) return MOE_ERR_WORKSPACE;
     return run_forward(p, x, W_r, b, W, out, topk_idx, topk_w, expert_counts, expert_offsets, sorted_token,
                        workspace, s, stage_events);
+}
+
+moe_status moe_bias_quantile(const moe_layer_desc* desc, const void* x, const float* W_r, float* b,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    moe_status st = check_desc(desc, false);
+    if (st != MOE_OK) return st;
+    if (desc->T < 1 || desc->T > kQuantileMaxT) return MOE_ERR_SHAPE;
+    if (!x || !W_r || !b || !workspace) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(W_r) || !aligned16(b) || !aligned16(workspace)) return MOE_ERR_ALIGN;
+    const Plan p = make_plan(desc, false);
+    if (workspace_bytes < static_cast<size_t>(p.total)) return MOE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_logits(p, x, W_r, workspace, s);
+    if (st != MOE_OK) return st;
+    const int64_t n = std::max<int64_t>(1, static_cast<int64_t>(p.T) * p.K / p.E);
+    MOE_HIP(launch_quantile_bias(at<float>(workspace, p.o_z), p.nsplit, split_stride(p), p.ldz, p.T, p.E,
+                                 static_cast<int>(n), at<float>(workspace, p.o_theta), b, s));
+    return MOE_OK;
 }
 
 moe_status moe_bias_update(const moe_layer_desc* desc, const int32_t* expert_counts, float* b, float gamma,

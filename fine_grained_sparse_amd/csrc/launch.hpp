@@ -77,6 +77,13 @@ hipError_t launch_gemm(const GemmArgs& args, DType dt, bool out_f32, Epi epi,
 hipError_t launch_pack_frag16(const uint16_t* src, uint16_t* dst, int64_t count, int rows, int cols,
                               hipStream_t stream);
 
+// Quantile Balancing bias from the router logits (nsplit partial planes of
+// [T, ldz]): theta_e = n-th largest sigmoid(z[., e]), b_e = mean(theta) -
+// theta_e.  theta: E floats of scratch.  T <= kQuantileMaxT (LDS).
+constexpr int kQuantileMaxT = 32768;
+hipError_t launch_quantile_bias(const float* z, int nsplit, int64_t split_stride, int ldz, int T, int E, int n,
+                                float* theta, float* b, hipStream_t stream);
+
 // b[e] += gamma * sgn(mean(counts) - counts[e]) for e < E (E <= 1024).
 hipError_t launch_bias_update(const int32_t* counts, int E, float gamma, float* b, hipStream_t stream);
 

@@ -202,7 +202,89 @@ __global__ __launch_bounds__(1024) void k_bias_update(const int32_t* __restrict_
     }
 }
 
+// Quantile Balancing (lilting.ch K3 essay, load-balancing paragraph; read
+// as: theta_e = the n-th largest router score of expert e over the batch,
+// b_e = mean(theta) - theta_e).  Block e gathers sigmoid(z[., e]) into LDS
+// (summing the split-K partial planes) and selects the n-th largest by a
+// most-significant-digit radix select over the fp32 bit patterns, 8 bits a
+// pass: scores are >= 0, so bit order is value order and the result is the
+// exact order statistic.
+__global__ __launch_bounds__(256) void k_quantile_theta(const float* __restrict__ z, int nsplit,
+                                                        int64_t split_stride, int ldz, int T, int n,
+                                                        float* __restrict__ theta) {
+    extern __shared__ uint32_t vals[];  // T fp32 bit patterns
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t pick_prefix;
+    __shared__ int pick_rem;
+    const int e = blockIdx.x, tid = threadIdx.x;
+    for (int t = tid; t < T; t += 256) {
+        float zz = 0.f;
+        for (int p = 0; p < nsplit; ++p) zz += z[p * split_stride + static_cast<int64_t>(t) * ldz + e];
+        float sc = 1.0f / (1.0f + expf(-zz));
+        if (!(sc == sc)) sc = 0.0f;
+        vals[t] = __float_as_uint(sc);
+    }
+    uint32_t prefix = 0, mask = 0;
+    int rem = n;  // rank (1-based, from the top) still to find among the matching values
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        hist[tid] = 0;
+        __syncthreads();
+        for (int t = tid; t < T; t += 256) {
+            const uint32_t u = vals[t];
+            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int acc = 0, dgt = 255;
+            for (; dgt > 0; --dgt) {
+                if (acc + static_cast<int>(hist[dgt]) >= rem) break;
+                acc += static_cast<int>(hist[dgt]);
+            }
+            pick_prefix = prefix | (static_cast<uint32_t>(dgt) << shift);
+            pick_rem = rem - acc;
+        }
+        __syncthreads();
+        prefix = pick_prefix;
+        rem = pick_rem;
+        mask |= 255u << shift;
+    }
+    if (tid == 0) theta[e] = __uint_as_float(prefix);
+}
+
+// b_e = mean(theta) - theta_e; one block, thread e owns expert e.
+__global__ __launch_bounds__(1024) void k_bias_center(const float* __restrict__ theta, int E, float* __restrict__ b) {
+    __shared__ float part[16];
+    const int e = threadIdx.x, lane = e & 63, w = e >> 6;
+    const float th = e < E ? theta[e] : 0.f;
+    float sum = th;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane == 0) part[w] = sum;
+    __syncthreads();
+    float total = 0.f;
+    for (int i = 0; i < 16; ++i) total += part[i];
+    if (e < E) b[e] = total / static_cast<float>(E) - th;
+}
+
 }  // namespace
+
+hipError_t launch_quantile_bias(const float* z, int nsplit, int64_t split_stride, int ldz, int T, int E, int n,
+                                float* theta, float* b, hipStream_t stream) {
+    if (T <= 0 || E <= 0 || E > 1024 || n < 1 || n > T || T > kQuantileMaxT) return hipErrorInvalidValue;
+    const size_t lds = static_cast<size_t>(T) * 4;
+    if (lds > 48 * 1024) {  // more dynamic LDS than the default allowance (gfx950 has 160 KiB)
+        const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_quantile_theta),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(k_quantile_theta, dim3(E), dim3(256), lds, stream, z, nsplit, split_stride, ldz, T, n,
+                       theta);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_bias_center, dim3(1), dim3(1024), 0, stream, theta, E, b);
+    return hipGetLastError();
+}
 
 hipError_t launch_bias_update(const int32_t* counts, int E, float gamma, float* b, hipStream_t stream) {
     if (E <= 0) return hipSuccess;

@@ -178,6 +178,22 @@ moe_status moe_bias_update(const moe_layer_desc *desc,
                            const int32_t *expert_counts, float *b,
                            float gamma, void *stream);
 
+/* Quantile Balancing [lilting.ch K3 essay, the load-balancing paragraph:
+ * the threshold at which each expert receives its target number of tokens
+ * is read off a quantile of the router scores and sets the selection bias].
+ * This library's reading: over the batch x [T, d], s = sigmoid(x W_r^T)
+ * (the unbiased scores, computed as in moe_router); every expert's target
+ * is the mean load n = max(1, floor(T K / E)); theta_e = the n-th largest
+ * s[., e]; the bias is written as
+ *   b[e] = mean(theta) - theta_e        (b [E] fp32, output only)
+ * so that s + b >= mean(theta) is s >= theta_e for every expert.  Uses
+ * T, d, E, K and act_dtype of the descriptor; 1 <= T <= 32768; workspace of
+ * at least moe_workspace_size(desc, 0) bytes.  Training-time work: the
+ * pages fix the bias at inference.                                           */
+moe_status moe_bias_quantile(const moe_layer_desc *desc, const void *x,
+                             const float *W_r, float *b, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 /* Rewrite row-major bf16 weights into MOE_LAYOUT_FRAG16 (a pure
  * permutation of each matrix; done once, e.g. when a model is loaded).
  * Every non-NULL matrix of `src` (row-major, shapes from `desc`, whose

@@ -30,8 +30,9 @@ def _declared():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == sorted(["moe_bias_update", "moe_forward", "moe_pack_weights", "moe_router",
-                                  "moe_status_str", "moe_workspace_size"])
+    assert _declared() == sorted(["moe_bias_quantile", "moe_bias_update", "moe_forward",
+                                  "moe_pack_weights", "moe_router", "moe_status_str",
+                                  "moe_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -175,4 +176,22 @@ def test_bias_update_rejects_bad_arguments():
     assert L.moe_bias_update(ctypes.byref(_k2()), vp(FAKE), None, 1e-3, None) == NULL
     assert L.moe_bias_update(ctypes.byref(_k2()), vp(FAKE_ODD), vp(FAKE), 1e-3, None) == ALIGN
     assert L.moe_bias_update(ctypes.byref(_k2(E=2000)), vp(FAKE), vp(FAKE), 1e-3, None) == SHAPE
+
+
+def test_bias_quantile_rejects_bad_arguments():
+    vp = ctypes.c_void_p
+    L = moe.lib()
+    D = _k2(T=4096)
+    n = moe.workspace_size(D, False)
+
+    def q(D, x=FAKE, W=FAKE, b=FAKE, ws=FAKE, nbytes=n):
+        return L.moe_bias_quantile(ctypes.byref(D), vp(x), vp(W), vp(b), vp(ws), nbytes, None)
+    assert q(D, x=None) == NULL
+    assert q(D, b=None) == NULL
+    assert q(D, ws=None) == NULL
+    assert q(D, b=FAKE_ODD) == ALIGN
+    assert q(D, nbytes=n - 1) == WS
+    assert q(_k2(T=0)) == SHAPE
+    assert q(_k2(T=40000)) == SHAPE          # more tokens than the selection holds
+    assert q(_k2(K=17)) == SHAPE
 

@@ -184,6 +184,24 @@ def test_bias_update_from_the_layers_own_counts():
     np.testing.assert_array_equal(dev["b"].cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("name,T", [("tiny_fp32_t128", None), ("mid_bf16_t300", None),
+                                    ("k3_latent_t4096", None), ("k2_router_t4096", 16384)])
+def test_bias_quantile_parity(name, T):
+    wl = get_workload(name)
+    T = T or wl.T
+    log(f"[gpu] quantile bias {name} T={T}")
+    r = make_router_inputs(wl, "cpu", seed=29, T=T)
+    b_ref, th_ref = oracle.bias_quantile(r["x"], r["W_r"], wl.K)
+    dev = weights_to_device(r, DEV)
+    b = moe.bias_quantile(dev["x"], dev["W_r"], wl.K)
+    torch.cuda.synchronize()
+    # fp32 scores against fp64 ones: each threshold is an order statistic of
+    # scores within ~1e-6 of the oracle's, the mean adds no more
+    err = np.abs(b.cpu().numpy().astype(np.float64) - b_ref).max()
+    log(f"  max |b - b_ref| = {err:.2e}")
+    assert err <= 1e-5
+
+
 # ---------------------------------------------------------------- whole layer, every token
 @pytest.mark.parametrize("name,packed", [("tiny_fp32_t128", False), ("mid_fp32_t77", False),
                                          ("mid_bf16_t300", False), ("mid_latent_t200", False),
