@@ -257,6 +257,49 @@ def measure_router(moe, torch, wl, steps, warmup, seed):
                             topk_group=wl.topk_group))
 
 
+def measure_bias_steps(moe, torch, seed):
+    """The two bias updates after a batch: the sign step from the K2 prefill
+    batch's expert histogram (E = 384, O(E)), and Quantile Balancing over the
+    K3 router at 4096 tokens (router logits + a per-expert order statistic)."""
+    from moe_inputs import get_workload, make_router_inputs
+    dev = torch.device("cuda:0")
+    out = {}
+    wl = get_workload("k2_prefill_t16384")
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    counts = torch.randint(0, 2 * wl.T * wl.K // wl.E, (wl.E,), generator=g, dtype=torch.int32).to(dev)
+    b = torch.zeros(wl.E, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(10):
+        moe.bias_update(counts, b, 1e-3)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(200):
+        moe.bias_update(counts, b, 1e-3)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    out["bias_update_e384"] = dict(us_per_call=round(t0.elapsed_time(t1) / 200 * 1e3, 2),
+                                   config=dict(E=wl.E, gamma=1e-3))
+    wl = get_workload("k3_latent_t4096")
+    r = make_router_inputs(wl, dev, seed=seed)
+    ws = moe.Workspace()
+    for _ in range(3):
+        moe.bias_quantile(r["x"], r["W_r"], wl.K, workspace=ws)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(20):
+        moe.bias_quantile(r["x"], r["W_r"], wl.K, workspace=ws)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / 20
+    fl = 2.0 * wl.T * wl.d * wl.E
+    out["bias_quantile_k3_t4096"] = dict(
+        ms_per_call=round(ms, 4), fp32_tflops=round(fl / (ms * 1e-3) / 1e12, 2),
+        frac_of_fp32_peak=round(fl / (ms * 1e-3) / 1e12 / PEAK_F32_TFLOPS, 4),
+        config=dict(T=wl.T, d=wl.d, E=wl.E, K=wl.K))
+    return out
+
+
 def cpu_baseline(torch, wl, weights, x, W_r, b, target_s, seed):
     """The oracle as it stands, on a bounded token sample of the same
     workload (router + K routed experts + shared experts per token, fp64,
@@ -344,6 +387,8 @@ def main():
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="target seconds of oracle time (0 skips the CPU baseline)")
     ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--bias-steps", type=int, default=1,
+                    help="also time the bias updates (moe_bias_update, moe_bias_quantile); 0 = skip")
     ap.add_argument("--layout", choices=("frag16", "rows"), default="frag16",
                     help="weight layout the layer reads: packed once at load (frag16, "
                          "moe_pack_weights, outside the timed steps) or row-major")
@@ -425,6 +470,13 @@ def main():
                                       F=awl.F, n_shared=awl.n_shared, F_shared=awl.F_shared,
                                       d_latent=awl.d_latent, scale=awl.scale,
                                       weights=WEIGHTS_NOTE[args.layout]))
+    if args.bias_steps:
+        log("[bench] bias updates")
+        del weights
+        torch.cuda.empty_cache()
+        also.update(measure_bias_steps(moe, torch, args.seed))
+        log(f"[bench] bias: {also['bias_update_e384']['us_per_call']} us (sign), "
+            f"{also['bias_quantile_k3_t4096']['ms_per_call']} ms (quantile)")
     mw = get_workload(args.workload)
     line = {
         "metric": METRIC, "value": round(main_r["value"], 1), "unit": "tokens/s", "n_gpus": 1,
