@@ -9,6 +9,12 @@ Recipe (values only; nothing here computes any part of the layer):
   Ws_gate, Ws_up ~ N(0, 1/d), [n_shared*F_shared, d] (shared experts stacked)
   Ws_down  ~ N(0, 1/F_shared), [d, n_shared*F_shared]
   W_lat_down ~ N(0, 1/d), [d_latent, d];  W_lat_up ~ N(0, 1/d_latent), [d, d_latent]
+FP8 routed experts (w_dtype "fp8"; shared experts and latent maps bf16):
+  each routed matrix of target std sigma = fan_in**-0.5 is drawn as
+  E8M0 block exponents s = 127 + round(log2(sigma / 16)) + j, j uniform in
+  {-1, 0, 1} per 128 x 128 block, and codes = float8_e4m3fn(16 * N(0, 1))
+  (torch's round-to-nearest cast is only the sampler: the layer takes the
+  codes as given), so code * 2^(s - 127) has std about sigma.
 Zipf skew: a seeded permutation gives each expert a rank r in 1..E and an
 offset o = 0.5 * r**-1.1 (fp32).  The offset is placed inside the inputs:
 the last feature of every token is set to 1.0 and the last column of W_r to
@@ -18,12 +24,21 @@ Each tensor draws from its own torch.Generator seeded from (seed, stream).
 The same seed gives the same values on the same device type; values made
 on a GPU are copied to the host whenever the oracle needs them.
 """
+import math
+
 import torch
 
 STREAM = dict(x=1, W_r=2, b=3, zipf=4, W_gate=5, W_up=6, W_down=7,
-              Ws_gate=8, Ws_up=9, Ws_down=10, W_lat_down=11, W_lat_up=12)
+              Ws_gate=8, Ws_up=9, Ws_down=10, W_lat_down=11, W_lat_up=12,
+              W_gate_scale=13, W_up_scale=14, W_down_scale=15)
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+FP8_CODE_STD = 16.0
+
+
+def _dense_dtype(wl):
+    """dtype of the shared experts and latent maps."""
+    return torch.bfloat16 if wl.w_dtype == "fp8" else _DT[wl.w_dtype]
 
 
 def _gen(seed: int, stream: int, device) -> torch.Generator:
@@ -65,18 +80,37 @@ def _expert_stack(shape_one, n, std, dtype, g, dev):
     return out
 
 
+def _fp8_stack(shape_one, n, std, g, gs, dev):
+    """n block-scaled FP8 matrices: (codes float8_e4m3fn [n, r, c],
+    E8M0 exponents uint8 [n, r/128, c/128])."""
+    r, c = shape_one
+    base = 127 + int(round(math.log2(std / FP8_CODE_STD)))
+    codes = torch.empty((n, r, c), dtype=torch.float8_e4m3fn, device=dev)
+    for e in range(n):
+        codes[e] = _normal((r, c), FP8_CODE_STD, torch.float32, g, dev).to(torch.float8_e4m3fn)
+    jit = torch.randint(-1, 2, (n, r // 128, c // 128), generator=gs, device=dev, dtype=torch.int32)
+    return codes, (jit + base).to(torch.uint8)
+
+
 def make_expert_weights(wl, device="cpu", seed=42):
     """Routed, shared and latent weights in the layouts listed above."""
     dev = torch.device(device)
-    dt = _DT[wl.w_dtype]
+    dt = _dense_dtype(wl)
     din, F = wl.d_in, wl.F
     w = {}
-    w["W_gate"] = _expert_stack((F, din), wl.E, din ** -0.5, dt,
-                                _gen(seed, STREAM["W_gate"], dev), dev)
-    w["W_up"] = _expert_stack((F, din), wl.E, din ** -0.5, dt,
-                              _gen(seed, STREAM["W_up"], dev), dev)
-    w["W_down"] = _expert_stack((din, F), wl.E, F ** -0.5, dt,
-                                _gen(seed, STREAM["W_down"], dev), dev)
+    if wl.w_dtype == "fp8":
+        for name, shp, fan in (("W_gate", (F, din), din), ("W_up", (F, din), din),
+                               ("W_down", (din, F), F)):
+            w[name], w[name + "_scale"] = _fp8_stack(
+                shp, wl.E, fan ** -0.5, _gen(seed, STREAM[name], dev),
+                _gen(seed, STREAM[name + "_scale"], dev), dev)
+    else:
+        w["W_gate"] = _expert_stack((F, din), wl.E, din ** -0.5, dt,
+                                    _gen(seed, STREAM["W_gate"], dev), dev)
+        w["W_up"] = _expert_stack((F, din), wl.E, din ** -0.5, dt,
+                                  _gen(seed, STREAM["W_up"], dev), dev)
+        w["W_down"] = _expert_stack((din, F), wl.E, F ** -0.5, dt,
+                                    _gen(seed, STREAM["W_down"], dev), dev)
     Fs = wl.n_shared * wl.F_shared
     if Fs:
         w["Ws_gate"] = _normal((Fs, wl.d), wl.d ** -0.5, dt,

@@ -26,7 +26,8 @@ class Workload:
     d_latent: int     # 0: experts act on x; >0: experts act on a d_latent projection of x
     scale: float      # routed scaling factor applied after renormalisation
     act_dtype: str    # "f32" or "bf16": x and the layer output
-    w_dtype: str      # "f32" or "bf16": expert, shared and latent weights
+    w_dtype: str      # "f32" or "bf16": expert, shared and latent weights;
+                      # "fp8": routed experts block-scaled FP8, the rest bf16
     bias_range: float  # b ~ U(-bias_range, bias_range)
     zipf_skew: bool   # add a Zipf(1.1)-ranked logit offset (max 0.5) per expert
     router_only: bool  # the workload measures the router alone
@@ -70,6 +71,12 @@ WORKLOADS = {
     # K2 layer, prefill-sized batch: grouped GEMMs.
     "k2_prefill_t16384": Workload(name="k2_prefill_t16384", T=16384,
                                   router_only=False, **_K2),
+    # The same two K2 layers with the routed experts stored in FP8 with
+    # 128 x 128 block scales (the router card's checkpoint note).
+    "k2_decode_fp8_t256": Workload(name="k2_decode_fp8_t256", T=256, router_only=False,
+                                   **dict(_K2, w_dtype="fp8")),
+    "k2_prefill_fp8_t16384": Workload(name="k2_prefill_fp8_t16384", T=16384, router_only=False,
+                                      **dict(_K2, w_dtype="fp8")),
     # K3-shaped latent layer.
     "k3_latent_t4096": Workload(
         name="k3_latent_t4096", T=4096, d=7168, E=896, K=16, F=3072,
@@ -87,6 +94,16 @@ WORKLOADS = {
         name="mid_latent_t200", T=200, d=768, E=40, K=5, F=192, n_shared=2,
         F_shared=128, d_latent=384, scale=1.0, act_dtype="bf16",
         w_dtype="bf16", bias_range=0.02, zipf_skew=False, router_only=False),
+    # FP8 routed experts (128 x 128 scale blocks): d_in and F in whole
+    # blocks, several blocks per matrix in both directions.
+    "mid_fp8_t300": Workload(
+        name="mid_fp8_t300", T=300, d=1024, E=48, K=6, F=384, n_shared=1,
+        F_shared=192, d_latent=0, scale=2.827, act_dtype="bf16",
+        w_dtype="fp8", bias_range=0.02, zipf_skew=True, router_only=False),
+    "mid_fp8_latent_t200": Workload(
+        name="mid_fp8_latent_t200", T=200, d=768, E=40, K=5, F=256, n_shared=2,
+        F_shared=128, d_latent=384, scale=1.0, act_dtype="bf16",
+        w_dtype="fp8", bias_range=0.02, zipf_skew=False, router_only=False),
     "mid_fp32_t77": Workload(
         name="mid_fp32_t77", T=77, d=320, E=20, K=3, F=192, n_shared=0,
         F_shared=0, d_latent=0, scale=2.827, act_dtype="f32", w_dtype="f32",

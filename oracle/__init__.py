@@ -15,7 +15,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "liboracle.so")
-F32, BF16 = 0, 1
+F32, BF16, FP8 = 0, 1, 2
 _lib = None
 
 
@@ -36,6 +36,9 @@ class _Layer(ctypes.Structure):
         ("Ws_gate", ctypes.c_void_p), ("Ws_up", ctypes.c_void_p),
         ("Ws_down", ctypes.c_void_p),
         ("W_lat_down", ctypes.c_void_p), ("W_lat_up", ctypes.c_void_p),
+        ("sw_dtype", ctypes.c_int32),
+        ("W_gate_scale", ctypes.c_void_p), ("W_up_scale", ctypes.c_void_p),
+        ("W_down_scale", ctypes.c_void_p),
     ]
 
 
@@ -54,10 +57,11 @@ def lib():
         L.oracle_dispatch.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_bias_update.argtypes = [i32, vp, vp, ctypes.c_float, vp]
         L.oracle_bias_quantile.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, i32]
+        L.oracle_fp8_dequant.argtypes = [i32, i32, vp, vp, vp]
         L.oracle_forward_given_routing.argtypes = [vp, i32, vp, vp, vp, vp, i32]
         L.oracle_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32]
         for f in (L.oracle_router, L.oracle_router_grouped, L.oracle_dispatch, L.oracle_bias_update,
-                  L.oracle_bias_quantile,
+                  L.oracle_bias_quantile, L.oracle_fp8_dequant,
                   L.oracle_forward_given_routing, L.oracle_forward):
             f.restype = ctypes.c_int
         _lib = L
@@ -82,6 +86,10 @@ def _host(a, what):
             a = a.contiguous()
             if a.dtype == torch.bfloat16:
                 return a.view(torch.int16).numpy().view(np.uint16), BF16
+            if a.dtype == torch.float8_e4m3fn:
+                return a.view(torch.uint8).numpy(), FP8
+            if a.dtype == torch.uint8:
+                return a.numpy(), None
             if a.dtype == torch.float32:
                 return a.numpy(), F32
             if a.dtype == torch.int32:
@@ -193,19 +201,40 @@ def dispatch(idx, E):
                 pos=pos)
 
 
+def fp8_dequant(codes, scales):
+    """Block-scaled FP8 matrix (float8_e4m3fn or uint8 codes [rows, cols],
+    uint8 E8M0 scales [rows/128, cols/128]) -> float64 [rows, cols]."""
+    ca, _ = _host(codes, "codes")
+    sa, _ = _host(scales, "scales")
+    ca = np.ascontiguousarray(ca.view(np.uint8))
+    sa = np.ascontiguousarray(np.asarray(sa, dtype=np.uint8))
+    rows, cols = ca.shape
+    if sa.shape != (rows // 128, cols // 128):
+        raise OracleError("fp8_dequant: scales must be [rows/128, cols/128]")
+    out = np.zeros((rows, cols), np.float64)
+    _check(lib().oracle_fp8_dequant(rows, cols, _ptr(ca), _ptr(sa), _ptr(out)),
+           "oracle_fp8_dequant")
+    return out
+
+
 class Layer:
     """Host-side description of one layer for the oracle.
 
     Routed expert weights are given either stacked ([E, F, d_in] etc.) or
     as per-expert sequences whose entries may be None for experts that no
     token of the call selects (so that only the needed experts have to be
-    on the host).
+    on the host).  They are fp32, bf16, or float8_e4m3fn codes; in the FP8
+    case W_gate_scale / W_up_scale / W_down_scale give, per expert, the
+    uint8 E8M0 exponents of its 128 x 128 blocks ([rows/128, cols/128]).
+    The shared experts and latent maps are fp32 or bf16, one dtype for all
+    of them.
     """
 
     def __init__(self, *, d, E, K, F, scale, W_r, b, W_gate, W_up, W_down,
                  n_shared=0, F_shared=0, Ws_gate=None, Ws_up=None,
                  Ws_down=None, d_latent=0, W_lat_down=None, W_lat_up=None,
-                 act_dtype=None, w_dtype=None):
+                 act_dtype=None, w_dtype=None, W_gate_scale=None,
+                 W_up_scale=None, W_down_scale=None):
         self._keep = []
         self.d, self.E, self.K, self.F = d, E, K, F
         self.scale = float(scale)
@@ -213,18 +242,25 @@ class Layer:
         self.W_r, _ = _host(W_r, "W_r")
         self.b, _ = _host(b, "b")
         self._keep += [self.W_r, self.b]
-        wdt = [w_dtype]
+        rdt, sdt = [w_dtype], [w_dtype if w_dtype != FP8 else None]
 
-        def one(a, what):
+        def one(a, what, slot, allowed):
             if a is None:
                 return None
             arr, dt = _host(a, what)
-            if dt is None:
-                raise OracleError(f"{what}: weights must be fp32 or bf16")
-            if wdt[0] is None:
-                wdt[0] = dt
-            elif wdt[0] != dt:
+            if dt not in allowed:
+                raise OracleError(f"{what}: unsupported weight dtype")
+            if slot[0] is None:
+                slot[0] = dt
+            elif slot[0] != dt:
                 raise OracleError(f"{what}: mixed weight dtypes")
+            self._keep.append(arr)
+            return arr
+
+        def raw(a, what):
+            arr, _ = _host(a, what)
+            if arr.dtype != np.uint8:
+                raise OracleError(f"{what}: block scales must be uint8 E8M0")
             self._keep.append(arr)
             return arr
 
@@ -232,16 +268,38 @@ class Layer:
             arr = (ctypes.c_void_p * E)()
             for e in range(E):
                 a = seq[e] if seq is not None else None
-                arr[e] = one(a, f"{what}[{e}]").ctypes.data if a is not None else None
+                if a is not None:
+                    arr[e] = one(a, f"{what}[{e}]", rdt, (F32, BF16, FP8)).ctypes.data
+            self._keep.append(arr)
+            return arr
+
+        def scale_table(seq, what):
+            arr = (ctypes.c_void_p * E)()
+            for e in range(E):
+                a = seq[e] if seq is not None else None
+                if a is not None:
+                    arr[e] = raw(a, f"{what}[{e}]").ctypes.data
             self._keep.append(arr)
             return arr
 
         self._tables = [table(W_gate, "W_gate"), table(W_up, "W_up"),
                         table(W_down, "W_down")]
-        self._shared = [one(Ws_gate, "Ws_gate"), one(Ws_up, "Ws_up"),
-                        one(Ws_down, "Ws_down")]
-        self._latent = [one(W_lat_down, "W_lat_down"), one(W_lat_up, "W_lat_up")]
-        self.w_dtype = wdt[0] if wdt[0] is not None else F32
+        self._scales = [scale_table(W_gate_scale, "W_gate_scale"),
+                        scale_table(W_up_scale, "W_up_scale"),
+                        scale_table(W_down_scale, "W_down_scale")]
+        self._shared = [one(Ws_gate, "Ws_gate", sdt, (F32, BF16)),
+                        one(Ws_up, "Ws_up", sdt, (F32, BF16)),
+                        one(Ws_down, "Ws_down", sdt, (F32, BF16))]
+        self._latent = [one(W_lat_down, "W_lat_down", sdt, (F32, BF16)),
+                        one(W_lat_up, "W_lat_up", sdt, (F32, BF16))]
+        self.w_dtype = rdt[0] if rdt[0] is not None else F32
+        self.sw_dtype = sdt[0] if sdt[0] is not None else F32
+        if self.w_dtype != FP8:
+            if sdt[0] is not None and rdt[0] is not None and sdt[0] != rdt[0]:
+                raise OracleError("mixed weight dtypes")
+            self.sw_dtype = self.w_dtype = rdt[0] if rdt[0] is not None else self.sw_dtype
+        elif W_gate_scale is None or W_up_scale is None or W_down_scale is None:
+            raise OracleError("FP8 routed weights need their block scales")
         self.act_dtype = act_dtype
 
     def struct(self, act_dtype):
@@ -255,6 +313,10 @@ class Layer:
         s.W_down = ctypes.cast(self._tables[2], ctypes.c_void_p)
         s.Ws_gate, s.Ws_up, s.Ws_down = [_ptr(a) for a in self._shared]
         s.W_lat_down, s.W_lat_up = [_ptr(a) for a in self._latent]
+        s.sw_dtype = self.sw_dtype
+        s.W_gate_scale = ctypes.cast(self._scales[0], ctypes.c_void_p)
+        s.W_up_scale = ctypes.cast(self._scales[1], ctypes.c_void_p)
+        s.W_down_scale = ctypes.cast(self._scales[2], ctypes.c_void_p)
         return s
 
 
@@ -270,6 +332,9 @@ def layer_from_inputs(wl, inp, experts=None):
     return Layer(d=wl.d, E=wl.E, K=wl.K, F=wl.F, scale=wl.scale,
                  W_r=inp["W_r"], b=inp["b"], W_gate=pick(inp["W_gate"]),
                  W_up=pick(inp["W_up"]), W_down=pick(inp["W_down"]),
+                 W_gate_scale=pick(inp.get("W_gate_scale")),
+                 W_up_scale=pick(inp.get("W_up_scale")),
+                 W_down_scale=pick(inp.get("W_down_scale")),
                  n_shared=wl.n_shared, F_shared=wl.F_shared,
                  Ws_gate=inp.get("Ws_gate"), Ws_up=inp.get("Ws_up"),
                  Ws_down=inp.get("Ws_down"), d_latent=wl.d_latent,

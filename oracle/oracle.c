@@ -29,6 +29,51 @@ static double elem(const void *p, int32_t dtype, size_t i)
 
 static double sigmoid(double a) { return 1.0 / (1.0 + exp(-a)); }
 
+/* OCP FP8 E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+ * 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no infinities. */
+static double fp8_e4m3(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double v = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* E8M0 block scale: 2^(s - 127) (255 is NaN). */
+static double e8m0(uint8_t s) { return s == 255 ? NAN : ldexp(1.0, (int)s - 127); }
+
+/* Element (r, c) of a block-scaled FP8 matrix with `cols` columns. */
+static double fp8_elem(const uint8_t *W, const uint8_t *S, int32_t cols,
+                       int32_t r, int32_t c)
+{
+    return fp8_e4m3(W[(size_t)r * cols + c]) *
+           e8m0(S[(size_t)(r / 128) * (cols / 128) + c / 128]);
+}
+
+/* A routed expert with block-scaled FP8 weights: the same SwiGLU as
+ * swiglu() on the dequantised values. */
+static void swiglu_fp8(int32_t din, int32_t F, const double *vin,
+                       const uint8_t *Wg, const uint8_t *Sg, const uint8_t *Wu,
+                       const uint8_t *Su, const uint8_t *Wd, const uint8_t *Sd,
+                       double *h, double *y)
+{
+    for (int32_t f = 0; f < F; ++f) {
+        double g = 0.0, u = 0.0;
+        for (int32_t j = 0; j < din; ++j) {
+            g += fp8_elem(Wg, Sg, din, f, j) * vin[j];
+            u += fp8_elem(Wu, Su, din, f, j) * vin[j];
+        }
+        h[f] = g * sigmoid(g) * u;
+    }
+    for (int32_t o = 0; o < din; ++o) {
+        double acc = 0.0;
+        for (int32_t f = 0; f < F; ++f)
+            acc += fp8_elem(Wd, Sd, F, o, f) * h[f];
+        y[o] = acc;
+    }
+}
+
 /* One token of the router [P3 four steps and MoEGate forward].
  * s_out (length E) receives sigmoid(z); sel (length K) the selected set in
  * ascending expert id; w (length K) the renormalised, scaled weights. */
@@ -341,8 +386,15 @@ static int check_layer(const oracle_layer *L)
         (L->n_shared > 0 && L->F_shared <= 0))
         return ORACLE_ERR_SHAPE;
     if ((L->act_dtype != ORACLE_F32 && L->act_dtype != ORACLE_BF16) ||
-        (L->w_dtype != ORACLE_F32 && L->w_dtype != ORACLE_BF16))
+        (L->w_dtype != ORACLE_F32 && L->w_dtype != ORACLE_BF16 && L->w_dtype != ORACLE_FP8))
         return ORACLE_ERR_SHAPE;
+    if (L->w_dtype == ORACLE_FP8) {
+        int32_t din = L->d_latent ? L->d_latent : L->d;
+        if ((L->sw_dtype != ORACLE_F32 && L->sw_dtype != ORACLE_BF16) || L->F % 128 || din % 128)
+            return ORACLE_ERR_SHAPE;
+        if (!L->W_gate_scale || !L->W_up_scale || !L->W_down_scale)
+            return ORACLE_ERR_NULL;
+    }
     if (!L->W_gate || !L->W_up || !L->W_down)
         return ORACLE_ERR_NULL;
     if (L->n_shared > 0 && (!L->Ws_gate || !L->Ws_up || !L->Ws_down))
@@ -375,7 +427,12 @@ int oracle_forward_given_routing(const oracle_layer *L, int32_t T,
             return ORACLE_ERR_SHAPE;
         if (!L->W_gate[e] || !L->W_up[e] || !L->W_down[e])
             return ORACLE_ERR_NULL;
+        if (L->w_dtype == ORACLE_FP8 &&
+            (!L->W_gate_scale[e] || !L->W_up_scale[e] || !L->W_down_scale[e]))
+            return ORACLE_ERR_NULL;
     }
+    /* dtype of the shared experts and latent maps */
+    const int32_t sdt = L->w_dtype == ORACLE_FP8 ? L->sw_dtype : L->w_dtype;
     const int32_t Fs_all = L->n_shared * L->F_shared;
     const int32_t hmax = F > L->F_shared ? F : L->F_shared;
     int nt = nthreads > 0 ? nthreads : 1;
@@ -391,7 +448,7 @@ int oracle_forward_given_routing(const oracle_layer *L, int32_t T,
             xd[j] = elem(x, L->act_dtype, (size_t)t * d + j);
         /* routed experts' input: x, or its latent compression [P4] */
         if (L->d_latent)
-            matvec(din, d, L->W_lat_down, L->w_dtype, xd, xin);
+            matvec(din, d, L->W_lat_down, sdt, xd, xin);
         else
             memcpy(xin, xd, sizeof(double) * (size_t)d);
         /* weighted sum of the selected experts, in slot order [P1 sec. 3] */
@@ -399,20 +456,25 @@ int oracle_forward_given_routing(const oracle_layer *L, int32_t T,
             routed_in[j] = 0.0;
         for (int32_t k = 0; k < K; ++k) {
             int32_t e = topk_idx[(size_t)t * K + k];
-            swiglu(din, F, din, xin, L->w_dtype, L->W_gate[e], L->W_up[e], 0,
-                   L->W_down[e], (size_t)F, 0, h, y);
+            if (L->w_dtype == ORACLE_FP8)
+                swiglu_fp8(din, F, xin, (const uint8_t *)L->W_gate[e], L->W_gate_scale[e],
+                           (const uint8_t *)L->W_up[e], L->W_up_scale[e],
+                           (const uint8_t *)L->W_down[e], L->W_down_scale[e], h, y);
+            else
+                swiglu(din, F, din, xin, L->w_dtype, L->W_gate[e], L->W_up[e], 0,
+                       L->W_down[e], (size_t)F, 0, h, y);
             double wk = topk_w[(size_t)t * K + k];
             for (int32_t j = 0; j < din; ++j)
                 routed_in[j] += wk * y[j];
         }
         /* back to the model width [P4]; identity in the K2 form */
         if (L->d_latent)
-            matvec(d, din, L->W_lat_up, L->w_dtype, routed_in, o);
+            matvec(d, din, L->W_lat_up, sdt, routed_in, o);
         else
             memcpy(o, routed_in, sizeof(double) * (size_t)d);
         /* always-on shared experts, unweighted [P1 sec. 3; P4] */
         for (int32_t sidx = 0; sidx < L->n_shared; ++sidx) {
-            swiglu(d, L->F_shared, d, xd, L->w_dtype, L->Ws_gate, L->Ws_up,
+            swiglu(d, L->F_shared, d, xd, sdt, L->Ws_gate, L->Ws_up,
                    (size_t)sidx * L->F_shared, L->Ws_down, (size_t)Fs_all,
                    (size_t)sidx * L->F_shared, h, y);
             for (int32_t j = 0; j < d; ++j)
@@ -424,6 +486,19 @@ int oracle_forward_given_routing(const oracle_layer *L, int32_t T,
         free(y);
         free(h);
     }
+    return ORACLE_OK;
+}
+
+int oracle_fp8_dequant(int32_t rows, int32_t cols, const uint8_t *codes,
+                       const uint8_t *scales, double *out)
+{
+    if (rows <= 0 || cols <= 0 || rows % 128 || cols % 128)
+        return ORACLE_ERR_SHAPE;
+    if (!codes || !scales || !out)
+        return ORACLE_ERR_NULL;
+    for (int32_t r = 0; r < rows; ++r)
+        for (int32_t c = 0; c < cols; ++c)
+            out[(size_t)r * cols + c] = fp8_elem(codes, scales, cols, r, c);
     return ORACLE_OK;
 }
 

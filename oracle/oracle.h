@@ -21,8 +21,14 @@
  *        table and the Stable LatentMoE paragraph (routed experts act on a
  *        3584-wide compression of x, their combined output is projected
  *        back to 7168, two shared experts act on x itself).
+ *   [P3] also states that the released checkpoint stores its weights in
+ *        FP8 with block scales; it gives neither the element format nor the
+ *        block shape nor the scale encoding.  This oracle's reading: OCP
+ *        E4M3FN codes, one power-of-two scale (E8M0 exponent) per 128 x 128
+ *        block, applied to the routed experts only.
  * Readings where the pages are silent (slot order, tie-break, SwiGLU form,
- * latent maps, shared-expert stacking) are stated at each function.
+ * latent maps, shared-expert stacking, the FP8 format) are stated at each
+ * function.
  *
  * Error behaviour: every function returns ORACLE_OK (0) or an error code;
  * argument checks run before any output is written, except that
@@ -38,7 +44,7 @@
 extern "C" {
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8 = 2 };
 enum { ORACLE_OK = 0, ORACLE_ERR_NULL = 1, ORACLE_ERR_SHAPE = 2 };
 
 typedef struct {
@@ -68,6 +74,17 @@ typedef struct {
     const void *Ws_down;
     const void *W_lat_down;  /* [d_latent, d] */
     const void *W_lat_up;    /* [d, d_latent] */
+    /* w_dtype == ORACLE_FP8 (block-scaled routed experts): W_gate[e] etc.
+     * hold OCP FP8 E4M3FN codes (bias 7, max 448, 0x7F / 0xFF NaN), and
+     * W_*_scale[e] one E8M0 code per 128 x 128 block of that matrix
+     * (row-major over blocks: [rows/128, cols/128]); element (r, c) is
+     * code(r, c) * 2^(scale[r/128][c/128] - 127).  The shared experts and
+     * the latent maps then have dtype sw_dtype.  Otherwise these fields are
+     * unused and shared / latent weights have dtype w_dtype.              */
+    int32_t sw_dtype;
+    const uint8_t *const *W_gate_scale;
+    const uint8_t *const *W_up_scale;
+    const uint8_t *const *W_down_scale;
 } oracle_layer;
 
 /* Router [P3 four steps; P3 MoEGate forward; P1 section 2].
@@ -121,6 +138,13 @@ int oracle_bias_quantile(int32_t T, int32_t d, int32_t E, int32_t K,
 int oracle_dispatch(int32_t T, int32_t E, int32_t K, const int32_t *topk_idx,
                     int32_t *counts, int32_t *offsets, int32_t *sorted_token,
                     int32_t *pos);
+
+/* Block-scaled FP8 matrix -> doubles [P3 checkpoint note; the format is
+ * this oracle's reading]: out[r*cols + c] = e4m3fn(codes[r*cols + c]) *
+ * 2^(scales[(r/128)*(cols/128) + c/128] - 127).  rows and cols must be
+ * positive multiples of 128.  NaN codes (0x7F, 0xFF) and scale 255 give NaN. */
+int oracle_fp8_dequant(int32_t rows, int32_t cols, const uint8_t *codes,
+                       const uint8_t *scales, double *out);
 
 /* Expert part of the layer for a given routing [P1 sections 2 and 3; P4]:
  *   out[t] = sum_s f_s(x[t]) + U( sum_k topk_w[t,k] * f_{idx[t,k]}(L(x[t])) )

@@ -597,3 +597,78 @@ def test_quantile_bias_balances_a_skewed_router():
     b, _ = oracle.bias_quantile(x, W, wl.K)
     before, after = spread(np.zeros(wl.E)), spread(b)
     assert before > 2.0 and after < 0.6 * before, (before, after)
+
+
+# --------------------------------------------------------------------------
+# FP8 routed experts.  The router card says only that the released weights
+# are FP8 with block scales; the element format (OCP E4M3FN), the 128 x 128
+# blocks and the E8M0 (power-of-two) scales are the oracle's reading.
+# --------------------------------------------------------------------------
+def test_fp8_codes_decode_as_torch_float8_e4m3fn():
+    codes = torch.zeros((128, 128), dtype=torch.uint8)
+    codes.view(-1)[:256] = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    got = oracle.fp8_dequant(codes, torch.full((1, 1), 127, dtype=torch.uint8)).reshape(-1)[:256]
+    ref = codes.view(-1)[:256].view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert set(np.nonzero(nan)[0].tolist()) == {0x7F, 0xFF}
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    # closed forms of the format: largest 448, smallest subnormal 2^-9,
+    # smallest normal 2^-6, 1.0 and -1.0, both zeros
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+    assert got[0x38] == 1.0 and got[0xB8] == -1.0 and got[0x00] == 0.0 and got[0x80] == 0.0
+
+
+def test_fp8_block_scales_follow_the_128_blocks():
+    # every code 1.0 (0x38): element (r, c) is 2^(s[r/128][c/128] - 127); a
+    # 2 x 3 block grid catches a transposed or shifted scale index
+    codes = torch.full((256, 384), 0x38, dtype=torch.uint8)
+    s = torch.tensor([[120, 121, 122], [130, 131, 132]], dtype=torch.uint8)
+    got = oracle.fp8_dequant(codes, s)
+    expect = np.ldexp(1.0, s.numpy().astype(np.int64) - 127).repeat(128, 0).repeat(128, 1)
+    np.testing.assert_array_equal(got, expect)
+    # E8M0 ends: 2^-127 and 2^127; 255 is NaN
+    ends = oracle.fp8_dequant(torch.full((128, 384), 0x38, dtype=torch.uint8),
+                              torch.tensor([[0, 254, 255]], dtype=torch.uint8))
+    assert ends[0, 0] == 2.0 ** -127 and ends[0, 128] == 2.0 ** 127 and np.isnan(ends[0, 256])
+
+
+def _fp8_dequant_torch(codes, scales):
+    """torch's float8_e4m3fn decoding times each block's power of two, in
+    fp32 (exact for the generated exponents)."""
+    sc = torch.pow(2.0, scales.to(torch.float64) - 127.0)
+    sc = sc.repeat_interleave(128, -2).repeat_interleave(128, -1)
+    return (codes.to(torch.float64) * sc).float().contiguous()
+
+
+@pytest.mark.parametrize("latent", [False, True], ids=["k2", "latent"])
+def test_fp8_layer_equals_the_layer_on_dequantised_weights(latent):
+    wl = _small(E=5, K=2, T=9, d=256, F=128, n_shared=2, F_shared=64, act_dtype="bf16",
+                w_dtype="fp8", d_latent=128 if latent else 0)
+    inp = make_layer_inputs(wl, "cpu", seed=31)
+    assert inp["W_gate"].dtype == torch.float8_e4m3fn and inp["W_down_scale"].shape == (5, wl.d_in // 128, 1)
+    got = oracle.forward(oracle.layer_from_inputs(wl, inp), inp["x"])
+    deq = {k: v for k, v in inp.items() if not k.endswith("_scale")}
+    for k in ("W_gate", "W_up", "W_down"):
+        deq[k] = _fp8_dequant_torch(inp[k], inp[k + "_scale"])
+    for k in ("Ws_gate", "Ws_up", "Ws_down", "W_lat_down", "W_lat_up"):
+        if deq.get(k) is not None:
+            deq[k] = deq[k].float()          # bf16 -> fp32 is exact
+    wl32 = Workload(**dict(wl.__dict__, w_dtype="f32"))
+    ref = oracle.forward(oracle.layer_from_inputs(wl32, deq), inp["x"])
+    np.testing.assert_array_equal(got["idx"], ref["idx"])
+    np.testing.assert_array_equal(got["out"], ref["out"])
+
+
+def test_fp8_layer_needs_whole_blocks_and_scales():
+    wl = _small(E=3, K=1, T=2, d=256, F=128, act_dtype="bf16", w_dtype="fp8")
+    inp = make_layer_inputs(wl, "cpu", seed=3)
+    no_scales = {k: v for k, v in inp.items() if not k.endswith("_scale")}
+    with pytest.raises(oracle.OracleError):
+        oracle.layer_from_inputs(wl, no_scales)
+    # F = 64 is not a whole number of 128-blocks
+    cut = dict(inp, W_gate=inp["W_gate"][:, :64].contiguous(), W_up=inp["W_up"][:, :64].contiguous(),
+               W_down=inp["W_down"][:, :, :64].contiguous())
+    lay = oracle.layer_from_inputs(Workload(**dict(wl.__dict__, F=64)), cut)
+    with pytest.raises(oracle.OracleError):
+        oracle.forward(lay, inp["x"])
