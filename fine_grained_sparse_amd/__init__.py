@@ -22,7 +22,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_LAYOUT_ROWS, MOE_LAYOUT_FRAG16 = 0, 1
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
            4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_UNSUPPORTED", 6: "MOE_ERR_HIP"}
@@ -30,6 +30,7 @@ _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 EXPORTS = ("moe_workspace_size", "moe_router", "moe_forward", "moe_pack_weights", "moe_bias_update",
            "moe_bias_quantile", "moe_status_str")
 WEIGHT_NAMES = ("W_gate", "W_up", "W_down", "Ws_gate", "Ws_up", "Ws_down", "W_lat_down", "W_lat_up")
+SCALE_NAMES = ("W_gate_scale", "W_up_scale", "W_down_scale")  # FP8 routed experts only
 STAGES = ("start", "router", "dispatch", "latent", "up", "down", "end")
 NUM_STAGE_EVENTS = len(STAGES)
 
@@ -51,7 +52,7 @@ class LayerDesc(ctypes.Structure):
 
 
 class ExpertWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES + SCALE_NAMES]
 
 
 _lib = None
@@ -170,14 +171,27 @@ def router(x, W_r, b, K, scale=2.827, *, counts=True, workspace=None, stream=Non
 
 
 def _weights_desc(weights, T, d, E, K, scale, dt, dev, n_shared, n_group=1, topk_group=1):
-    """Validate the weight tensors; return (LayerDesc, ExpertWeights)."""
+    """Validate the weight tensors; return (LayerDesc, ExpertWeights).
+    Routed experts are of dtype dt, or float8_e4m3fn codes with uint8 E8M0
+    block scales (W_gate_scale, W_up_scale [E, F/128, d_in/128];
+    W_down_scale [E, d_in/128, F/128]) when dt is bf16."""
     Wg, Wu, Wd = weights["W_gate"], weights["W_up"], weights["W_down"]
-    _need(Wg, "W_gate", dt, device=dev)
+    f8 = isinstance(Wg, torch.Tensor) and Wg.dtype == torch.float8_e4m3fn and dt == torch.bfloat16
+    rdt = torch.float8_e4m3fn if f8 else dt
+    _need(Wg, "W_gate", rdt, device=dev)
     if Wg.dim() != 3 or Wg.shape[0] != E:
         raise ValueError("W_gate must be [E, F, d_in]")
     F, din = Wg.shape[1], Wg.shape[2]
-    _need(Wu, "W_up", dt, (E, F, din), dev)
-    _need(Wd, "W_down", dt, (E, din, F), dev)
+    _need(Wu, "W_up", rdt, (E, F, din), dev)
+    _need(Wd, "W_down", rdt, (E, din, F), dev)
+    scales = [None] * 3
+    if f8:
+        if F % 128 or din % 128:
+            raise ValueError("FP8 routed experts need F and d_in in whole 128-blocks")
+        shapes = ((E, F // 128, din // 128), (E, F // 128, din // 128), (E, din // 128, F // 128))
+        for i, (n, shp) in enumerate(zip(SCALE_NAMES, shapes)):
+            _need(weights.get(n), n, torch.uint8, shp, dev)
+            scales[i] = weights[n]
     Wl_d, Wl_u = weights.get("W_lat_down"), weights.get("W_lat_up")
     d_lat = 0
     if Wl_d is not None or Wl_u is not None:
@@ -198,10 +212,10 @@ def _weights_desc(weights, T, d, E, K, scale, dt, dev, n_shared, n_group=1, topk
         _need(Wsd, "Ws_down", dt, (d, ns * Fs), dev)
     layout = int(weights.get("layout", MOE_LAYOUT_ROWS))
     D = desc(T=T, d=d, E=E, K=K, F=F, n_shared=ns, F_shared=Fs, d_latent=d_lat,
-             scale=scale, act_dtype=_DT[dt], w_layout=layout, n_group=n_group,
-             topk_group=topk_group)
+             scale=scale, act_dtype=_DT[dt], w_dtype=MOE_FP8_E4M3 if f8 else None,
+             w_layout=layout, n_group=n_group, topk_group=topk_group)
     W = ExpertWeights(*[None if t is None else t.data_ptr() for t in
-                        (Wg, Wu, Wd, Wsg, Wsu, Wsd, Wl_d, Wl_u)])
+                        (Wg, Wu, Wd, Wsg, Wsu, Wsd, Wl_d, Wl_u, *scales)])
     return D, W
 
 
@@ -246,19 +260,24 @@ def bias_quantile(x, W_r, K, *, out=None, workspace=None, stream=None):
 
 
 def pack_weights(weights, *, n_shared=None, stream=None):
-    """moe_pack_weights: bf16 row-major weights -> a new dict of tensors of
-    the same shapes in MOE_LAYOUT_FRAG16, with "layout" set.  Run once, e.g.
-    at model load; the packed tensors are what forward() then reads."""
+    """moe_pack_weights: row-major weights (bf16, or FP8 routed experts with
+    bf16 shared / latent maps) -> a new dict of tensors of the same shapes
+    in MOE_LAYOUT_FRAG16, with "layout" set (FP8 block scales are carried
+    over as they are).  Run once, e.g. at model load; the packed tensors are
+    what forward() then reads."""
     if int(weights.get("layout", MOE_LAYOUT_ROWS)) != MOE_LAYOUT_ROWS:
         raise ValueError("weights are already packed")
     Wg = weights["W_gate"]
-    if Wg.dtype != torch.bfloat16:
-        raise TypeError("only bf16 weights have a packed layout")
+    if Wg.dtype not in (torch.bfloat16, torch.float8_e4m3fn):
+        raise TypeError("only bf16 and FP8 weights have a packed layout")
     E, F, din = Wg.shape
     d = weights["W_lat_down"].shape[1] if weights.get("W_lat_down") is not None else din
-    D, src = _weights_desc(weights, 1, d, E, 1, 1.0, Wg.dtype, Wg.device, n_shared)
+    D, src = _weights_desc(weights, 1, d, E, 1, 1.0, torch.bfloat16, Wg.device, n_shared)
     out = {k: (torch.empty_like(weights[k]) if weights.get(k) is not None else None) for k in WEIGHT_NAMES}
     dst = ExpertWeights(*[None if out[k] is None else out[k].data_ptr() for k in WEIGHT_NAMES])
+    for k in SCALE_NAMES:
+        if weights.get(k) is not None:
+            out[k] = weights[k]
     rc = lib().moe_pack_weights(ctypes.byref(D), ctypes.byref(src), ctypes.byref(dst), _stream(stream))
     if rc:
         raise MoeError("moe_pack_weights", rc)
@@ -273,7 +292,9 @@ def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
     W_up [E,F,d_in], W_down [E,d_in,F] and optionally Ws_gate/Ws_up
     [n_shared*F_shared, d], Ws_down [d, n_shared*F_shared], W_lat_down
     [d_latent, d], W_lat_up [d, d_latent], plus "layout" (MOE_LAYOUT_ROWS
-    when absent; pack_weights returns MOE_LAYOUT_FRAG16 weights).  Returns
+    when absent; pack_weights returns MOE_LAYOUT_FRAG16 weights).  With bf16
+    x the routed experts may be float8_e4m3fn codes (packed) with uint8 E8M0
+    block scales W_gate_scale, W_up_scale, W_down_scale.  Returns
     out [T, d], or (out, routing dict) with return_routing=True.
     `stage_events` (optional) is a sequence of NUM_STAGE_EVENTS
     already-created torch.cuda.Event objects recorded at the stage
@@ -319,5 +340,5 @@ def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
 
 
 __all__ = ["router", "forward", "pack_weights", "bias_update", "bias_quantile", "workspace_size", "desc", "lib", "MoeError",
-           "LayerDesc", "ExpertWeights", "Workspace", "MOE_F32", "MOE_BF16", "MOE_LAYOUT_ROWS",
-           "MOE_LAYOUT_FRAG16", "EXPORTS", "WEIGHT_NAMES"]
+           "LayerDesc", "ExpertWeights", "Workspace", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
+           "MOE_LAYOUT_ROWS", "MOE_LAYOUT_FRAG16", "EXPORTS", "WEIGHT_NAMES", "SCALE_NAMES"]

@@ -14,6 +14,10 @@
 // the worst case and tiles past the device-side tile count exit at once.
 // Weight GEMMs at prefill sizes use the register-fed WIDE tile when the
 // weights are packed (MOE_LAYOUT_FRAG16), the LDS tile otherwise.
+// FP8 routed experts (w_dtype MOE_FP8_E4M3): the routed up and down
+// projections are FP8-weight launches of their own (WIDE, or WIDE16 at
+// decode sizes) and the shared experts, bf16, run as dense launches beside
+// them; the tile table then holds routed tiles only.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -37,6 +41,7 @@ struct Plan {
     int64_t A;                                // assignments T*K
     DType dt;
     bool packed;                              // weights in MOE_LAYOUT_FRAG16
+    bool f8;                                  // routed experts in block-scaled FP8
     int64_t es;                               // element size
     // router
     TileCfg rcfg;
@@ -55,10 +60,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 moe_status check_desc(const moe_layer_desc* D, bool forward) {
     if (!D) return MOE_ERR_NULL;
     if (D->act_dtype != MOE_F32 && D->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-    if (forward && D->w_dtype != D->act_dtype) return MOE_ERR_UNSUPPORTED;
-    if (forward && D->w_layout != MOE_LAYOUT_ROWS &&
-        !(D->w_layout == MOE_LAYOUT_FRAG16 && D->w_dtype == MOE_BF16))
-        return MOE_ERR_UNSUPPORTED;
+    if (forward) {
+        if (D->w_dtype == MOE_FP8_E4M3) {  // bf16 activations, packed weights
+            if (D->act_dtype != MOE_BF16 || D->w_layout != MOE_LAYOUT_FRAG16) return MOE_ERR_UNSUPPORTED;
+        } else {
+            if (D->w_dtype != D->act_dtype) return MOE_ERR_UNSUPPORTED;
+            if (D->w_layout != MOE_LAYOUT_ROWS && !(D->w_layout == MOE_LAYOUT_FRAG16 && D->w_dtype == MOE_BF16))
+                return MOE_ERR_UNSUPPORTED;
+        }
+    }
     if (D->T < 0 || D->E < 1 || D->E > 1024 || D->K < 1 || D->K > 16 || D->K > D->E) return MOE_ERR_SHAPE;
     if (D->d <= 0 || D->d % 64) return MOE_ERR_SHAPE;
     if (static_cast<int64_t>(D->T) * D->K >= (int64_t{1} << 31)) return MOE_ERR_SHAPE;
@@ -74,6 +84,10 @@ moe_status check_desc(const moe_layer_desc* D, bool forward) {
         if (D->n_shared < 0 || D->n_shared > 8) return MOE_ERR_SHAPE;
         if (D->n_shared > 0 && (D->F_shared <= 0 || D->F_shared % 64)) return MOE_ERR_SHAPE;
         if (D->d_latent < 0 || D->d_latent % 64) return MOE_ERR_SHAPE;
+        if (D->w_dtype == MOE_FP8_E4M3) {  // whole 128 x 128 scale blocks; K <= 8192 per GEMM
+            const int64_t din = D->d_latent ? D->d_latent : D->d;
+            if (din % 128 || D->F % 128 || din > 8192 || D->F > 8192) return MOE_ERR_SHAPE;
+        }
     }
     return MOE_OK;
 }
@@ -113,12 +127,13 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
     // Experts: big M tiles once experts average 64 rows or more (the
     // register-fed WIDE tile on packed weights, the LDS tile otherwise).
     p.packed = forward && D->w_layout == MOE_LAYOUT_FRAG16;
+    p.f8 = forward && D->w_dtype == MOE_FP8_E4M3;
     const TileCfg big = p.packed ? TILE_WIDE : TILE_LARGE;
-    p.ecfg = (p.A >= 64ll * p.E && p.dt == DT_BF16) ? big : TILE_SMALL;
+    p.ecfg = (p.A >= 64ll * p.E && p.dt == DT_BF16) ? big : (p.f8 ? TILE_WIDE16 : TILE_SMALL);
     p.bm = tile_bm(p.ecfg);
     p.dcfg = (p.T >= 1024 && p.dt == DT_BF16) ? big : TILE_SMALL;
     p.nch = static_cast<int>(cdiv(p.T, 64));
-    p.max_tiles = static_cast<int>(cdiv(p.A, p.bm) + p.E + (p.ns ? cdiv(p.T, p.bm) : 0));
+    p.max_tiles = static_cast<int>(cdiv(p.A, p.bm) + p.E + (p.ns && !p.f8 ? cdiv(p.T, p.bm) : 0));
 
     int64_t off = 0;
     auto take = [&](int64_t bytes) {
@@ -210,6 +225,27 @@ moe_status run_router(const Plan& p, const void* x, const float* W_r, const floa
     return MOE_OK;
 }
 
+// FP8 form of a grouped projection: g.g[0] (routed, FP8 weights with block
+// scales bs / bsu) on the tile table, then g.g[1] (shared experts, bf16;
+// absent when its N is 0) as a dense launch over the T tokens.
+moe_status run_f8_pair(const Plan& p, const GemmArgs& g, const uint8_t* bs, const uint8_t* bsu, Epi epi, int n_routed,
+                       hipStream_t s) {
+    GemmArgs r = g;
+    r.g[1] = GemmGroup{};
+    r.g[0].bs = bs;
+    r.g[0].bsu = bsu;
+    r.g[0].s_estride = static_cast<int64_t>(r.g[0].N / 128) * (r.g[0].seg[0].K / 128);
+    MOE_HIP(launch_gemm_f8(r, epi, p.ecfg, p.max_tiles, n_routed, s));
+    if (g.g[1].N > 0) {
+        GemmArgs d = gemm_args();
+        d.g[0] = g.g[1];
+        d.M = p.T;
+        MOE_HIP(launch_gemm(d, p.dt, false, epi, p.dcfg, static_cast<int>(cdiv(p.T, tile_bm(p.dcfg))), d.g[0].N,
+                            p.packed, s));
+    }
+    return MOE_OK;
+}
+
 hipError_t record(void* const* ev, int i, hipStream_t s) {
     if (!ev || !ev[i]) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
@@ -237,8 +273,9 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
     moe_status st = run_router(p, x, W_r, b, idx, w, nullptr, ws, s);
     if (st != MOE_OK) return st;
     MOE_HIP(record(ev, MOE_EV_ROUTER, s));
-    // shared tiles ride in the routed launches (rows = tokens)
-    MOE_HIP(launch_dispatch(idx, p.T, p.E, p.K, p.bm, p.ns ? p.T : 0, at<uint64_t>(ws, p.o_masks),
+    // shared tiles ride in the routed launches (rows = tokens), except with
+    // FP8 routed weights, where they run as dense bf16 launches of their own
+    MOE_HIP(launch_dispatch(idx, p.T, p.E, p.K, p.bm, p.ns && !p.f8 ? p.T : 0, at<uint64_t>(ws, p.o_masks),
                             at<int32_t>(ws, p.o_cbase), counts, offsets, sorted, pos, tiles, ntiles, s));
     MOE_HIP(record(ev, MOE_EV_DISPATCH, s));
 
@@ -276,7 +313,12 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
         S1.ldc = p.Fsh;
         g.tiles = tiles;
         g.ntiles = ntiles;
-        MOE_HIP(launch_gemm(g, p.dt, false, EPI_SWIGLU, p.ecfg, p.max_tiles, std::max(p.F, p.Fsh), p.packed, s));
+        if (p.f8) {
+            st = run_f8_pair(p, g, W->W_gate_scale, W->W_up_scale, EPI_SWIGLU, p.F, s);
+            if (st != MOE_OK) return st;
+        } else {
+            MOE_HIP(launch_gemm(g, p.dt, false, EPI_SWIGLU, p.ecfg, p.max_tiles, std::max(p.F, p.Fsh), p.packed, s));
+        }
     }
     MOE_HIP(record(ev, MOE_EV_UP, s));
     // down projection: routed -> Y[sorted rows]; shared (K2 form) -> Y[A + t]
@@ -290,7 +332,19 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
         R0.C = Y;
         R0.ldc = p.din;
         GemmGroup& S1 = g.g[1];
-        if (p.ns && !latent) {
+        if (p.f8) {
+            if (p.ns && !latent) {
+                S1.seg[0] = GemmSeg{Hs, W->Ws_down, nullptr, p.Fsh, p.Fsh, p.Fsh, 0};
+                S1.nseg = 1;
+                S1.N = p.d;
+                S1.C = Y + p.A * p.d * p.es;
+                S1.ldc = p.d;
+            }
+            g.tiles = tiles;
+            g.ntiles = ntiles;
+            st = run_f8_pair(p, g, W->W_down_scale, nullptr, EPI_STORE, p.din, s);
+            if (st != MOE_OK) return st;
+        } else if (p.ns && !latent) {
             S1.seg[0] = GemmSeg{Hs, W->Ws_down, nullptr, p.Fsh, p.Fsh, p.Fsh, 0};
             S1.nseg = 1;
             S1.N = p.d;
@@ -300,9 +354,11 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
             S1.N = 0;  // shared tiles (latent form) do nothing here
             S1.nseg = 0;
         }
-        g.tiles = tiles;
-        g.ntiles = ntiles;
-        MOE_HIP(launch_gemm(g, p.dt, false, EPI_STORE, p.ecfg, p.max_tiles, p.din, p.packed, s));
+        if (!p.f8) {
+            g.tiles = tiles;
+            g.ntiles = ntiles;
+            MOE_HIP(launch_gemm(g, p.dt, false, EPI_STORE, p.ecfg, p.max_tiles, p.din, p.packed, s));
+        }
     }
     MOE_HIP(record(ev, MOE_EV_DOWN, s));
     if (!latent) {
@@ -388,6 +444,8 @@ moe_status moe_forward(const moe_layer_desc* desc, const void* x, const float* W
     if (!x || !W_r || !b || !weights || !out || !workspace) return MOE_ERR_NULL;
     const moe_expert_weights* W = weights;
     if (!W->W_gate || !W->W_up || !W->W_down) return MOE_ERR_NULL;
+    if (desc->w_dtype == MOE_FP8_E4M3 && (!W->W_gate_scale || !W->W_up_scale || !W->W_down_scale))
+        return MOE_ERR_NULL;
     if (desc->n_shared > 0 && (!W->Ws_gate || !W->Ws_up || !W->Ws_down)) return MOE_ERR_NULL;
     if (desc->d_latent > 0 && (!W->W_lat_down || !W->W_lat_up)) return MOE_ERR_NULL;
     const void* need[] = {x, W_r, b, out, workspace, W->W_gate, W->W_up, W->W_down};
@@ -437,38 +495,46 @@ moe_status moe_pack_weights(const moe_layer_desc* desc, const moe_expert_weights
                             const moe_expert_weights* dst, void* stream) {
     if (!desc || !src || !dst) return MOE_ERR_NULL;
     moe_layer_desc D = *desc;
-    D.w_layout = MOE_LAYOUT_ROWS;  // the layout of src; dst gets FRAG16
-    moe_status st = check_desc(&D, true);
+    if (D.w_dtype != MOE_BF16 && D.w_dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    // shapes as for the forward over the packed result (src is row-major)
+    D.w_layout = MOE_LAYOUT_FRAG16;
+    const moe_status st = check_desc(&D, true);
     if (st != MOE_OK) return st;
-    if (D.w_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     const int din = D.d_latent ? D.d_latent : D.d, Fsh = D.n_shared * D.F_shared;
+    const bool f8 = D.w_dtype == MOE_FP8_E4M3;  // routed matrices: one byte per element
     struct Mat {
         const void* s;
         const void* d;
         int64_t count;
         int rows, cols;
+        bool f8;
     };
     const Mat mats[] = {
-        {src->W_gate, dst->W_gate, D.E, D.F, din},     {src->W_up, dst->W_up, D.E, D.F, din},
-        {src->W_down, dst->W_down, D.E, din, D.F},     {src->Ws_gate, dst->Ws_gate, 1, Fsh, D.d},
-        {src->Ws_up, dst->Ws_up, 1, Fsh, D.d},         {src->Ws_down, dst->Ws_down, 1, D.d, Fsh},
-        {src->W_lat_down, dst->W_lat_down, 1, D.d_latent, D.d},
-        {src->W_lat_up, dst->W_lat_up, 1, D.d, D.d_latent},
+        {src->W_gate, dst->W_gate, D.E, D.F, din, f8},     {src->W_up, dst->W_up, D.E, D.F, din, f8},
+        {src->W_down, dst->W_down, D.E, din, D.F, f8},     {src->Ws_gate, dst->Ws_gate, 1, Fsh, D.d, false},
+        {src->Ws_up, dst->Ws_up, 1, Fsh, D.d, false},      {src->Ws_down, dst->Ws_down, 1, D.d, Fsh, false},
+        {src->W_lat_down, dst->W_lat_down, 1, D.d_latent, D.d, false},
+        {src->W_lat_up, dst->W_lat_up, 1, D.d, D.d_latent, false},
     };
     for (const Mat& m : mats) {  // validate everything before enqueueing
         if (!m.s) continue;
         if (!m.d) return MOE_ERR_NULL;
         if (!aligned16(m.s) || !aligned16(m.d)) return MOE_ERR_ALIGN;
         if (m.rows <= 0 || m.cols <= 0) return MOE_ERR_SHAPE;
-        const uintptr_t bytes = static_cast<uintptr_t>(m.count) * m.rows * m.cols * 2;
+        const uintptr_t bytes = static_cast<uintptr_t>(m.count) * m.rows * m.cols * (m.f8 ? 1 : 2);
         const uintptr_t a = reinterpret_cast<uintptr_t>(m.s), b = reinterpret_cast<uintptr_t>(m.d);
         if (a < b + bytes && b < a + bytes) return MOE_ERR_SHAPE;  // overlapping buffers
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    for (const Mat& m : mats)
-        if (m.s)
+    for (const Mat& m : mats) {
+        if (!m.s) continue;
+        if (m.f8)
+            MOE_HIP(launch_pack_frag16_fp8(static_cast<const uint8_t*>(m.s), static_cast<uint8_t*>(const_cast<void*>(m.d)),
+                                           m.count, m.rows, m.cols, s));
+        else
             MOE_HIP(launch_pack_frag16(static_cast<const uint16_t*>(m.s), static_cast<uint16_t*>(const_cast<void*>(m.d)),
                                        m.count, m.rows, m.cols, s));
+    }
     return MOE_OK;
 }
 

@@ -287,6 +287,15 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// 16 FP8 E4M3FN codes (two 8-code K chunks) -> two bf16 fragments of 8,
+// each code times `scale` (a power of two: the product is exact).
+__device__ __forceinline__ void fp8x16_to_bf16(uint4 q, float scale, uint4& lo, uint4& hi) {
+#define MOE_CVT(w, upper) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, upper))
+    lo = make_uint4(MOE_CVT(q.x, false), MOE_CVT(q.x, true), MOE_CVT(q.y, false), MOE_CVT(q.y, true));
+    hi = make_uint4(MOE_CVT(q.z, false), MOE_CVT(q.z, true), MOE_CVT(q.w, false), MOE_CVT(q.w, true));
+#undef MOE_CVT
+}
+
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(src) : "memory", "m0");
 }
@@ -597,46 +606,67 @@ __global__ __launch_bounds__(64 * WM * WN, (big_occupancy<BM, BN, NST, ROWB>()))
     store_tile<TC, EPI, BM, BNO, TM, TN, MB, NB, WP, NT>(acc, lds, wm, wn, G, C, row0, rows, n0);
 }
 
-// Prefill tile for packed weights: 128 A rows x 512 B rows per workgroup
-// of four waves; wave w owns B rows [128 w, 128 w + 128), a 128 x 128
-// output block held in 64 accumulators of 16x16.  Only A is shared between
-// the waves, so only A goes through LDS (DMA into a ring of four 64-K
-// slots).  Each wave loads its own B fragments from global memory straight
-// into registers one stage ahead, a fragment being reloaded with the next
-// stage as soon as its last MFMA of this stage has issued.  In the packed
-// layout a fragment (16 rows x 32 K) is one contiguous KiB in lane order, so
+// Register-fed tile for packed weights: BM A rows x 512 B rows per
+// workgroup of four waves; wave w owns B rows [128 w, 128 w + 128), a
+// BM x 128 output block held in 16x16 accumulators.  Only A is shared
+// between the waves, so only A goes through LDS (DMA into a ring of four
+// 64-K slots).  Each wave loads its own weight fragments from global memory
+// straight into registers one stage ahead, a fragment being reloaded with
+// the next stage as soon as its last use in this stage has issued.  In the
+// packed layouts a fragment block is one contiguous KiB in lane order, so
 // each of these loads reads eight whole 128-byte lines: the vector memory
 // path on gfx950 is limited by the lines an instruction touches, and a
 // row-major fragment (16 rows x 64 bytes) touches twice as many.
 //
-// NSEG K segments (1, or 2 for a sum of two products).  Per stage and lane
-// the memory operations are, in issue order: NB B loads of the next stage
-// among the first slab's MFMAs, NAB A DMA loads for stage it + NST (after the
-// barrier between the slabs), NB B loads among the second slab's MFMAs.
-// Every stage issues the same loads (past the last stage they re-read it),
-// so the loads younger than A(it + 1) at its wait are a compile-time count
-// (the first stages, after a prologue of A(0..NST-1) and B(0), have their own).
-template <typename TC, int EPI, int NSEG, int BM>
-__global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
+// bf16 weights (F8 false): a 1 KiB block is one 16 x 32 fragment, two loads
+// per 16-row block per stage.  FP8 weights (F8 true; OCP E4M3FN codes with
+// one E8M0 exponent per 128 x 128 block): a 1 KiB block is 16 rows x 64
+// columns, lane l holding columns 8 (l/16) .. + 7 of both 32-column halves
+// of row l % 16, so one load per 16-row block brings both slabs of a stage;
+// v_cvt_scalef32_pk_bf16_fp8 turns the codes into bf16 scaled by the
+// block's power of two (exact: 3 mantissa bits fit in bf16's 7), and the
+// MFMAs are the bf16 ones.  Lane l keeps the exponent of K block l of its
+// row block (K <= 8192) and a stage reads its own with readlane.
+//
+// NSEG K segments (1, or 2 for a sum of two products; FP8: 1).  Per stage
+// and lane the memory operations are, in issue order: the first slab's B
+// loads of the next stage among the first slab's MFMAs (bf16: NB; FP8: the
+// NB loads of both slabs), NAB A DMA loads for stage it + NST (after the
+// barrier between the slabs), the second slab's NB B loads among its MFMAs
+// (bf16 only).  Every stage issues the same loads (past the last stage they
+// re-read it), so the loads younger than A(it + 1) at its wait are a
+// compile-time count (the first stages, after a prologue of A(0..NST-1) and
+// B(0), have their own).
+template <typename TC, int EPI, int NSEG, int BM, bool F8>
+__global__ __launch_bounds__(256, BM >= 64 ? 1 : 2) void k_gemm_wide(const GemmArgs a) {
     using T = bf16_t;
-    static_assert(BM == 128 || BM == 64, "row tiles");
+    static_assert(BM == 128 || BM == 64 || BM == 32 || BM == 16, "row tiles");
+    static_assert(!F8 || NSEG == 1, "FP8 weights: one K segment");
     constexpr int ES = 2, BN = 512, NW = 4, TN = BN / NW;
+    constexpr int WES = F8 ? 1 : 2;            // bytes per weight element
     constexpr int MB = BM / 16, NB = TN / 16;
     constexpr int ROWB = 128, BKE = ROWB / ES;  // a stage is 64 K = two 32-K slabs
     constexpr int NST = 4;                     // A slots: stages it .. it+3 (it+4 after the barrier)
     constexpr int STAGE = BM * ROWB;
     constexpr int BNO = EPI == EPI_SWIGLU ? BN / 2 : BN;
-    constexpr int NAB = STAGE / 1024 / NW;  // 1 KiB A blocks per wave per stage
-    constexpr int LOADS = NAB + 2 * NB;     // vector loads per lane per stage
+    // A blocks of 1 KiB (8 rows) per stage, split across the waves; with
+    // fewer blocks than waves every wave loads all of them (identical bytes
+    // to identical LDS addresses)
+    constexpr int NBLK = STAGE / 1024;
+    constexpr bool A_ALL = NBLK < NW;
+    constexpr int NAB = A_ALL ? NBLK : NBLK / NW;  // A DMA loads per wave per stage
+    constexpr int NBL = F8 ? NB : 2 * NB;         // B loads per wave per stage
+    constexpr int LOADS = NAB + NBL;               // vector loads per lane per stage
+    constexpr int B2 = F8 ? 0 : NB;                // B loads after the A DMA of a stage
     // A(it + 1) is waited for between the slabs of stage it.  Loads younger
     // than it: once A(it + 1) came from stage it + 1 - NST, that stage's
-    // second-slab B loads, NST - 2 whole stages and the first-slab B loads
-    // of stage it; before that (A from the prologue: A(0..NST-1), B(0)),
-    // the later prologue loads, the stages so far and the first slab.
-    constexpr int kWaitA = 2 * NB + (NST - 2) * LOADS;
-    constexpr int kY0 = NAB * (NST - 2) + 3 * NB, kY1 = NAB * (NST - 3) + 3 * NB + LOADS;
+    // later B loads, NST - 2 whole stages and the first-slab B loads of
+    // stage it; before that (A from the prologue: A(0..NST-1), B(0)), the
+    // later prologue loads, the stages so far and the first slab.
+    constexpr int kWaitA = B2 + NB + (NST - 2) * LOADS;
+    constexpr int kY0 = NAB * (NST - 2) + NBL + NB, kY1 = NAB * (NST - 3) + NBL + NB + LOADS;
     constexpr int kWait0 = kY0 < kWaitA ? kY0 : kWaitA, kWait1 = kY1 < kWaitA ? kY1 : kWaitA;
-    static_assert(kWaitA < 64 && (NSEG == 1 || NSEG == 2) && (NST == 3 || NST == 4), "vmcnt range; shape");
+    static_assert(kWaitA < 64 && (NSEG == 1 || NSEG == 2) && NST == 4, "vmcnt range; shape");
     constexpr int WP = 256;
     constexpr int EP_BYTES = BM * (WP + 4) * 4;
     constexpr int LDS_BYTES = NST * STAGE > EP_BYTES ? NST * STAGE : EP_BYTES;
@@ -654,12 +684,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
 
     // A: block q of a stage holds tile rows 8q .. 8q+7 (128 bytes each, the
     // 16-byte chunk c of row r at position c ^ (r & 7)); lane i fills row
-    // 8q + i/8, position i%8.  This wave loads blocks wid + NW j.
+    // 8q + i/8, position i%8.  This wave loads blocks ablk(j).
     const int achunk = ((lane & 7) ^ (lane >> 3)) << 4;
     int arow[NAB];
+    auto ablk = [&](int j) { return A_ALL ? j : wid + NW * j; };
 #pragma unroll
     for (int j = 0; j < NAB; ++j) {
-        const int r = (wid + NW * j) * 8 + (lane >> 3);
+        const int r = ablk(j) * 8 + (lane >> 3);
         const int p = row0 + (r < rows ? r : 0);
         arow[j] = G.rowmap ? G.rowmap[p] : p;
     }
@@ -670,12 +701,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
     const char* const sA0 = static_cast<const char*>(G.seg[0].A);
     const char* const sA1 = static_cast<const char*>(G.seg[NSEG - 1].A);
     const int64_t lda0 = G.seg[0].lda * ES, lda1 = G.seg[NSEG - 1].lda * ES;
-    const int64_t eoff = static_cast<int64_t>(jb.expert) * G.b_estride * ES;  // segment 0 only
+    const int64_t eoff = static_cast<int64_t>(jb.expert) * G.b_estride * WES;  // segment 0 only
     const char* const sB0 = static_cast<const char*>(G.seg[0].B) + eoff;
     const char* const sU0 = EPI == EPI_SWIGLU ? static_cast<const char*>(G.seg[0].Bu) + eoff : sB0;
     const char* const sB1 = static_cast<const char*>(G.seg[NSEG - 1].B);
     const char* const sU1 = EPI == EPI_SWIGLU ? static_cast<const char*>(G.seg[NSEG - 1].Bu) : sB1;
-    const uint32_t kb0 = static_cast<uint32_t>(G.seg[0].K / 32), kb1 = static_cast<uint32_t>(G.seg[NSEG - 1].K / 32);
+    // fragment blocks per row block: K/32 (bf16) or K/64 (FP8)
+    const uint32_t kb0 = static_cast<uint32_t>(G.seg[0].K / (F8 ? 64 : 32));
+    const uint32_t kb1 = static_cast<uint32_t>(G.seg[NSEG - 1].K / 32);
 
     const char* asrc[NAB];  // segment 0 row addresses
 #pragma unroll
@@ -686,20 +719,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
         const uint32_t dst = lds_base + slot * STAGE;
         if (NSEG == 1) {
 #pragma unroll
-            for (int j = 0; j < NAB; ++j) lds_dma16(asrc[j] + kt * ROWB, dst + (wid + NW * j) * 1024);
+            for (int j = 0; j < NAB; ++j) lds_dma16(asrc[j] + kt * ROWB, dst + ablk(j) * 1024);
         } else {
             const bool s1 = kt >= nk0;
             const char* base = (s1 ? sA1 : sA0) + (kt - (s1 ? nk0 : 0)) * ROWB + achunk;
             const int64_t lda = s1 ? lda1 : lda0;
 #pragma unroll
-            for (int j = 0; j < NAB; ++j) lds_dma16(base + arow[j] * lda, dst + (wid + NW * j) * 1024);
+            for (int j = 0; j < NAB; ++j) lds_dma16(base + arow[j] * lda, dst + ablk(j) * 1024);
         }
     };
 
     // B: fragment j of this wave is row block rb[j] (16 rows); for SwiGLU,
     // j < NB/2 are gate row blocks and j + NB/2 the same blocks of the up
-    // matrix.  Fragment block (row block r, slab k) of a [rows, K] matrix
-    // sits at byte (r (K/32) + k) 1024; lane l reads its 16 bytes at 16 l.
+    // matrix.  Fragment block (row block r, column block k) of a [rows, K]
+    // matrix sits at byte (r kb + k) 1024; lane l reads its 16 bytes at 16 l.
     int rb[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -710,10 +743,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
         const bool s1 = NSEG == 2 && kt >= nk0;
         const bool up = EPI == EPI_SWIGLU && j >= NB / 2;
         const char* m = s1 ? (up ? sU1 : sB1) : (up ? sU0 : sB0);
-        const uint32_t blk = static_cast<uint32_t>(rb[j]) * (s1 ? kb1 : kb0) +
-                             static_cast<uint32_t>((kt - (s1 ? nk0 : 0)) * 2 + sl);
+        const uint32_t kblk = F8 ? static_cast<uint32_t>(kt) : static_cast<uint32_t>((kt - (s1 ? nk0 : 0)) * 2 + sl);
+        const uint32_t blk = static_cast<uint32_t>(rb[j]) * (s1 ? kb1 : kb0) + kblk;
         return *reinterpret_cast<const uint4*>(m + blk * 1024u + lane * 16);
     };
+    // FP8 block scales: lane l holds the exponent of K block l of this
+    // wave's 128-row block (gate and up), placed as the bits of the float
+    // 2^(s - 127); the wave's rows never straddle a 128-row block (n0 is a
+    // multiple of 256, the wave's B rows a 64- or 128-row aligned range).
+    uint32_t scg = 0, scu = 0;
+    if constexpr (F8) {
+        const int kbl = G.seg[0].K / 128;
+        const int r128 = min((EPI == EPI_SWIGLU ? n0 + wid * (TN / 2) : n0 + wid * TN) / 128, N / 128 - 1);
+        const int64_t so = static_cast<int64_t>(jb.expert) * G.s_estride + static_cast<int64_t>(r128) * kbl;
+        scg = lane < kbl ? static_cast<uint32_t>(G.bs[so + lane]) << 23 : 0u;
+        scu = EPI == EPI_SWIGLU ? (lane < kbl ? static_cast<uint32_t>(G.bsu[so + lane]) << 23 : 0u) : scg;
+    }
 
     f32x4 acc[MB][NB];
 #pragma unroll
@@ -726,8 +771,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
     const int fo0 = frow * ROWB + ((((lane >> 4) + 0) ^ (frow & 7)) << 4);
     const int fo1 = frow * ROWB + ((((lane >> 4) + 4) ^ (frow & 7)) << 4);
 
-    uint4 fb[2][NB];  // B fragments of the current stage, refilled with the next
-    uint4 fa0[MB];    // A fragments of the first slab of the current stage
+    // B fragments of the current stage, refilled with the next: bf16, both
+    // slabs; FP8, the raw codes of both slabs in fb[0]
+    uint4 fb[F8 ? 1 : 2][NB];
+    uint4 fa0[MB];  // A fragments of the first slab of the current stage
     auto read_a = [&](uint4 (&fa)[MB], int stage, int fo) {
         const char* As = lds + (stage % NST) * STAGE;
 #pragma unroll
@@ -736,32 +783,51 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
     // One K stage.  The order below is the schedule (the scheduler would
     // otherwise sink the B loads to their next use and expose their
     // latency): a B fragment is reloaded with the next stage right after its
-    // last MFMA here; the second slab's A fragments are read early in the
+    // last use here; the second slab's A fragments are read early in the
     // first slab; the barrier sits between the slabs, after which the slot
     // of this stage (read by every wave) takes A(it + NST) and the next
     // stage's first A fragments are read while the second slab computes.
     auto step = [&](int it, auto wait_next) {
         const int kb = min(it + 1, nkt - 1);
         uint4 fa1[MB];
+        uint4 f1[F8 ? NB : 1];  // FP8: the second slab's converted fragments
+        float sg = 0.f, su = 0.f;
+        if constexpr (F8) {
+            sg = __uint_as_float(__builtin_amdgcn_readlane(scg, it >> 1));
+            su = EPI == EPI_SWIGLU ? __uint_as_float(__builtin_amdgcn_readlane(scu, it >> 1)) : sg;
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
+            if constexpr (F8) {
+                uint4 f0;
+                fp8x16_to_bf16(fb[0][j], (EPI == EPI_SWIGLU && j >= NB / 2) ? su : sg, f0, f1[j]);
+                fb[0][j] = load_b(kb, 0, j);
 #pragma unroll
-            for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa0[i], fb[0][j], acc[i][j]);
-            fb[0][j] = load_b(kb, 0, j);
+                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa0[i], f0, acc[i][j]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa0[i], fb[0][j], acc[i][j]);
+                fb[0][j] = load_b(kb, 0, j);
+            }
             if (j == 1) read_a(fa1, it, fo1);
             __builtin_amdgcn_sched_barrier(0);
         }
         wait_next();      // this wave's A(it + 1) has landed
-        __syncthreads();  // ... every wave's; every wave is done reading slot it % 3
+        __syncthreads();  // ... every wave's; every wave is done reading slot it % NST
         issue_a(min(it + NST, nkt - 1), it % NST);
         read_a(fa0, it + 1, fo0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
+            if constexpr (F8) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa1[i], fb[1][j], acc[i][j]);
-            fb[1][j] = load_b(kb, 1, j);
+                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa1[i], f1[j], acc[i][j]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa1[i], fb[1][j], acc[i][j]);
+                fb[1][j] = load_b(kb, 1, j);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -769,10 +835,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_wide(const GemmArgs a) {
 #pragma unroll
     for (int p = 0; p < NST; ++p) issue_a(min(p, nkt - 1), p);
 #pragma unroll
-    for (int sl = 0; sl < 2; ++sl)
+    for (int sl = 0; sl < (F8 ? 1 : 2); ++sl)
 #pragma unroll
         for (int j = 0; j < NB; ++j) fb[sl][j] = load_b(0, sl, j);
-    wait_vmcnt<(NST - 1) * NAB + 2 * NB>();  // A(0): younger are A(1..NST-1) and B(0)
+    wait_vmcnt<(NST - 1) * NAB + NBL>();  // A(0): younger are A(1..NST-1) and B(0)
     __syncthreads();
     read_a(fa0, 0, fo0);
     for (int it = 0; it < nkt; ++it)
@@ -803,10 +869,10 @@ constexpr int kWideBM = 128, kWideBN = 512;
 
 static_assert(kSmBM == 16, "fp32 small tiles share the 16-row M tiling");
 static_assert(kBigBM == kWideBM, "prefill tiles share the tile table's 128-row M tiling");
-int tile_bm(TileCfg cfg) { return cfg == TILE_SMALL ? kSmBM : kBigBM; }
+int tile_bm(TileCfg cfg) { return (cfg == TILE_SMALL || cfg == TILE_WIDE16) ? kSmBM : kBigBM; }
 int tile_bn_out(TileCfg cfg, Epi epi) {  // bf16 kernels (sizing heuristics only)
     // B rows per N tile (gate + up rows for SwiGLU)
-    const int bn = cfg == TILE_SMALL ? kSmBN : (cfg == TILE_WIDE ? kWideBN : kBigBN);
+    const int bn = cfg == TILE_SMALL ? kSmBN : ((cfg == TILE_WIDE || cfg == TILE_WIDE16) ? kWideBN : kBigBN);
     return epi == EPI_SWIGLU ? bn / 2 : bn;
 }
 
@@ -838,6 +904,7 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
         if (packed || cfg != TILE_SMALL) return hipErrorInvalidValue;  // fp32 runs the small tiles only
     }
     if (cfg == TILE_WIDE && !(packed && wide_fits(args))) cfg = TILE_LARGE;
+    if (cfg == TILE_WIDE16) cfg = TILE_SMALL;  // bf16 decode: the LDS tile streams slightly faster
     const bool wide = cfg == TILE_WIDE;
     // output columns per N tile of the kernel actually launched
     const int bn = sizeof(T) == 4 ? kF32BN : (cfg == TILE_SMALL ? kSmBN : (wide ? kWideBN : kBigBN));
@@ -855,9 +922,9 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
     } else {
         if (cfg == TILE_WIDE) {
             if (max_nseg(a) == 1)
-                hipLaunchKernelGGL((k_gemm_wide<TC, EPI, 1, kWideBM>), grid, dim3(256), 0, stream, a);
+                hipLaunchKernelGGL((k_gemm_wide<TC, EPI, 1, kWideBM, false>), grid, dim3(256), 0, stream, a);
             else
-                hipLaunchKernelGGL((k_gemm_wide<TC, EPI, 2, kWideBM>), grid, dim3(256), 0, stream, a);
+                hipLaunchKernelGGL((k_gemm_wide<TC, EPI, 2, kWideBM, false>), grid, dim3(256), 0, stream, a);
         } else if (cfg == TILE_SMALL) {
             if (packed)
                 hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, kSmNST, kSmROWB, EPI, true>), grid,
@@ -877,7 +944,47 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
     return hipGetLastError();
 }
 
+// What the FP8 form of the wide kernel handles: one K segment per group,
+// block scales present, rows and K in whole 128 x 128 scale blocks, the
+// scale row of a 128-row block in one wave (K <= 8192), byte offsets in 31
+// bits.
+bool wide_f8_fits(const GemmArgs& a, Epi epi) {
+    if (a.nsplit != 1) return false;
+    for (int g = 0; g < 2; ++g) {
+        const GemmGroup& G = a.g[g];
+        if (G.N == 0) continue;
+        const int K = G.seg[0].K;
+        if (G.nseg != 1 || !G.bs || (epi == EPI_SWIGLU && !G.bsu)) return false;
+        if (G.N % 128 || K < 128 || K % 128 || K > 64 * 128) return false;
+        if (static_cast<int64_t>(G.N) * K >= (int64_t{1} << 31)) return false;
+    }
+    return true;
+}
+
+template <int EPI>
+hipError_t launch_f8_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n, hipStream_t stream) {
+    if ((cfg != TILE_WIDE && cfg != TILE_WIDE16) || !wide_f8_fits(args, static_cast<Epi>(EPI)))
+        return hipErrorInvalidValue;
+    constexpr int bno = EPI == EPI_SWIGLU ? kWideBN / 2 : kWideBN;
+    GemmArgs a = args;
+    a.ntn = (max_n + bno - 1) / bno;
+    const unsigned blocks = static_cast<unsigned>(max_tiles) * a.ntn;
+    dim3 grid((blocks + 7u) & ~7u, 1, 1);  // a multiple of 8: see launch_t
+    if (cfg == TILE_WIDE)
+        hipLaunchKernelGGL((k_gemm_wide<bf16_t, EPI, 1, kWideBM, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_gemm_wide<bf16_t, EPI, 1, kSmBM, true>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_gemm_f8(const GemmArgs& args, Epi epi, TileCfg cfg, int max_tiles, int max_n,
+                          hipStream_t stream) {
+    if (max_tiles <= 0 || max_n <= 0) return hipSuccess;
+    if (epi == EPI_SWIGLU) return launch_f8_t<EPI_SWIGLU>(args, cfg, max_tiles, max_n, stream);
+    return launch_f8_t<EPI_STORE>(args, cfg, max_tiles, max_n, stream);
+}
 
 hipError_t launch_gemm(const GemmArgs& args, DType dt, bool out_f32, Epi epi, TileCfg cfg, int max_tiles,
                        int max_n, bool packed, hipStream_t stream) {

@@ -13,7 +13,9 @@ enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1 };
 // per expert (decode-sized batches); LARGE (128 x 256, both operands through
 // LDS) and WIDE (128 x 512, weights fed to registers) are the prefill tiles.
 // All bf16 prefill tiles are 128 rows, so one tile table serves both.
-enum TileCfg { TILE_SMALL = 0, TILE_LARGE = 1, TILE_WIDE = 2 };
+// WIDE16 is the register-fed tile at 16 rows (FP8 decode; bf16 decode runs
+// SMALL).
+enum TileCfg { TILE_SMALL = 0, TILE_LARGE = 1, TILE_WIDE = 2, TILE_WIDE16 = 3 };
 
 int tile_bm(TileCfg cfg);         // rows per M tile
 int tile_bn_out(TileCfg cfg, Epi epi);  // output columns per N tile
@@ -34,6 +36,9 @@ struct GemmSeg {
 // expert * b_estride) or one dense matrix (the shared experts, a latent
 // map, the router).  Row p of the group reads A row rowmap ? rowmap[p] : p
 // and writes C row p.
+// FP8 weights (launch_gemm_f8): bs / bsu hold the E8M0 exponents of B / Bu
+// per 128 x 128 block, [N/128, K/128] per matrix, s_estride bytes apart per
+// expert; b_estride is then in bytes (one per element).
 struct GemmGroup {
     GemmSeg seg[3];
     int32_t nseg;
@@ -42,6 +47,9 @@ struct GemmGroup {
     const int32_t* rowmap;
     void* C;
     int64_t ldc;
+    const uint8_t* bs;
+    const uint8_t* bsu;
+    int64_t s_estride;
 };
 
 // One M tile of a grouped GEMM.  `first` and `count` describe the run of
@@ -71,6 +79,19 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs& args, DType dt, bool out_f32, Epi epi,
                        TileCfg cfg, int max_tiles, int max_n, bool packed,
                        hipStream_t stream);
+
+// C = epi(A * B^T) with bf16 A and C and block-scaled FP8 B (16 x 64
+// fragment blocks of MOE_LAYOUT_FRAG16 for FP8): one K segment per group,
+// N and K multiples of 128, K <= 8192.  cfg: TILE_WIDE (128-row tiles) or
+// TILE_WIDE16 (16-row tiles).
+hipError_t launch_gemm_f8(const GemmArgs& args, Epi epi, TileCfg cfg, int max_tiles, int max_n,
+                          hipStream_t stream);
+
+// Row-major [rows, cols] uint8 FP8 matrices -> 16 x 64 blocks of 1 KiB:
+// lane l of a block holds columns 8 (l/16) .. + 7 and 32 + 8 (l/16) .. + 7
+// of row l % 16.
+hipError_t launch_pack_frag16_fp8(const uint8_t* src, uint8_t* dst, int64_t count, int rows, int cols,
+                                  hipStream_t stream);
 
 // Row-major [rows, cols] bf16 matrices (count of them, consecutive) -> the
 // fragment-block layout: block (rows/16) x (cols/32) of 1 KiB each.

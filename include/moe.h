@@ -50,7 +50,11 @@
 extern "C" {
 #endif
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* MOE_FP8_E4M3 is a weight dtype only: OCP FP8 E4M3FN codes (sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; 0x7F and 0xFF are NaN, no
+ * infinities) with one E8M0 scale per 128 x 128 block (see
+ * moe_expert_weights).                                                      */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 
 typedef enum {
     MOE_OK = 0,
@@ -74,24 +78,36 @@ typedef struct {
     float scale;       /* routed scaling factor (2.827 for K2)                */
     int32_t act_dtype; /* moe_dtype of x, out and the intermediates           */
     int32_t w_dtype;   /* moe_dtype of expert, shared and latent weights;     */
-                       /* must equal act_dtype (W_r and b are always fp32)    */
-    int32_t w_layout;  /* moe_weight_layout of those weights (bf16 may be     */
-                       /* MOE_LAYOUT_FRAG16; fp32 must be MOE_LAYOUT_ROWS)    */
+                       /* equal to act_dtype (W_r and b are always fp32), or  */
+                       /* MOE_FP8_E4M3: routed experts in block-scaled FP8,   */
+                       /* shared and latent weights bf16 (act_dtype bf16,     */
+                       /* MOE_LAYOUT_FRAG16; d_in and F multiples of 128 and  */
+                       /* at most 8192)                                       */
+    int32_t w_layout;  /* moe_weight_layout of those weights (bf16 and FP8    */
+                       /* may be, and FP8 must be, MOE_LAYOUT_FRAG16; fp32    */
+                       /* must be MOE_LAYOUT_ROWS)                            */
     int32_t n_group;   /* group-limited choice: expert groups (0 or 1: none)  */
     int32_t topk_group;/* groups kept per token when n_group > 1              */
 } moe_layer_desc;
 
 /* Storage of the expert, shared and latent weight matrices.
  *   MOE_LAYOUT_ROWS: row-major [rows, cols] (nn.Linear [out, in]).
- *   MOE_LAYOUT_FRAG16 (bf16 only): each [rows, cols] matrix as
+ *   MOE_LAYOUT_FRAG16, bf16 matrices: each [rows, cols] matrix as
  *     (rows/16) x (cols/32) blocks of 16 rows x 32 columns, block (i, j) at
  *     element offset (i * (cols/32) + j) * 512; inside a block, element
  *     (r, c) at ((c / 8) * 16 + r) * 8 + c % 8.  A block is then exactly
  *     the B operand of one v_mfma_f32_16x16x32_bf16 in lane order (lane l
  *     holds row l % 16, columns 8 (l / 16) .. 8 (l / 16) + 7), so the GEMMs
- *     read weights as whole 1 KiB blocks.  Stacked matrices (W_gate etc.)
- *     keep their per-expert stride rows * cols; the sizes of all buffers
- *     are those of the row-major layout.  moe_pack_weights converts.       */
+ *     read weights as whole 1 KiB blocks.
+ *   MOE_LAYOUT_FRAG16, FP8 matrices (the routed experts under
+ *     MOE_FP8_E4M3): (rows/16) x (cols/64) blocks of 16 rows x 64 columns,
+ *     block (i, j) at byte (i * (cols/64) + j) * 1024; inside a block,
+ *     element (r, c) at byte (((c % 32) / 8) * 16 + r) * 16 + (c / 32) * 8
+ *     + c % 8, so lane l's 16 bytes hold the codes of the two bf16 operands
+ *     (columns 0-31 and 32-63) that lane feeds.
+ *   Stacked matrices (W_gate etc.) keep their per-expert stride rows * cols
+ *   elements; the sizes of all buffers are those of the row-major layout.
+ *   moe_pack_weights converts.                                              */
 typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_FRAG16 = 1 } moe_weight_layout;
 
 /* Expert weights, nn.Linear layout [out, in]; d_in = d_latent ? d_latent : d.
@@ -99,11 +115,22 @@ typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_FRAG16 = 1 } moe_weight_layout;
  *   Ws_gate, Ws_up [n_shared*F_shared, d];  Ws_down [d, n_shared*F_shared]
  *     (shared expert s owns rows/columns [s*F_shared, (s+1)*F_shared))
  *   W_lat_down [d_latent, d];  W_lat_up [d, d_latent]  (NULL if d_latent == 0)
- * Shared pointers may be NULL when n_shared == 0.                            */
+ * Shared pointers may be NULL when n_shared == 0.
+ * Block scales of FP8 routed experts (OpenModelAtlas "Kimi K2 · Router": the
+ * released weights are FP8 with block scales; the block shape and scale
+ * encoding are this library's reading), used only when w_dtype is
+ * MOE_FP8_E4M3:
+ *   W_gate_scale, W_up_scale [E, F/128, d_in/128];  W_down_scale
+ *   [E, d_in/128, F/128], uint8 E8M0 exponents s (row-major over blocks,
+ *   not repacked), so that element (r, c) of a matrix is
+ *   code(r, c) * 2^(s[r/128][c/128] - 127).  The product is rounded to
+ *   bf16 before the MFMA; it is exact (3 mantissa bits) while it lies in
+ *   bf16's normal range.  s = 255 (NaN in E8M0) is not supported.           */
 typedef struct {
     const void *W_gate, *W_up, *W_down;
     const void *Ws_gate, *Ws_up, *Ws_down;
     const void *W_lat_down, *W_lat_up;
+    const uint8_t *W_gate_scale, *W_up_scale, *W_down_scale;
 } moe_expert_weights;
 
 /* Bytes of device workspace moe_router (for_forward = 0) or moe_forward
@@ -194,12 +221,15 @@ moe_status moe_bias_quantile(const moe_layer_desc *desc, const void *x,
                              const float *W_r, float *b, void *workspace,
                              size_t workspace_bytes, void *stream);
 
-/* Rewrite row-major bf16 weights into MOE_LAYOUT_FRAG16 (a pure
- * permutation of each matrix; done once, e.g. when a model is loaded).
- * Every non-NULL matrix of `src` (row-major, shapes from `desc`, whose
- * w_layout is ignored) is written to the same member of `dst`, which must
- * then be non-NULL, 16-byte aligned, of the same size and not overlap it.
- * Requires w_dtype == MOE_BF16.  Enqueued on `stream` like the other calls. */
+/* Rewrite row-major weights into MOE_LAYOUT_FRAG16 (a pure permutation of
+ * each matrix; done once, e.g. when a model is loaded).  Every non-NULL
+ * matrix of `src` (row-major, shapes from `desc`, whose w_layout is
+ * ignored) is written to the same member of `dst`, which must then be
+ * non-NULL, 16-byte aligned, of the same size and not overlap it.
+ * Requires w_dtype MOE_BF16, or MOE_FP8_E4M3 (routed matrices as FP8 codes,
+ * shared and latent ones bf16; the block scales are not touched and keep
+ * their layout).  Shapes are checked as for moe_forward on the packed
+ * result.  Enqueued on `stream` like the other calls.                       */
 moe_status moe_pack_weights(const moe_layer_desc *desc,
                             const moe_expert_weights *src,
                             const moe_expert_weights *dst, void *stream);

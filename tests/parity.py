@@ -89,8 +89,12 @@ def weights_to_device(inp, device):
 
 
 def expert_weights(inp):
-    return {k: inp.get(k) for k in ("W_gate", "W_up", "W_down", "Ws_gate", "Ws_up",
-                                    "Ws_down", "W_lat_down", "W_lat_up")}
+    w = {k: inp.get(k) for k in ("W_gate", "W_up", "W_down", "Ws_gate", "Ws_up",
+                                 "Ws_down", "W_lat_down", "W_lat_up")}
+    for k in ("W_gate_scale", "W_up_scale", "W_down_scale"):   # FP8 routed experts
+        if inp.get(k) is not None:
+            w[k] = inp[k]
+    return w
 
 
 def frag16_reference(w):
@@ -101,6 +105,18 @@ def frag16_reference(w):
     v = w.reshape(*lead, R // 16, 16, C // 32, 4, 8)
     n = len(lead)
     perm = list(range(n)) + [n + 0, n + 2, n + 3, n + 1, n + 4]   # (i, j, c/8, r, c%8)
+    return v.permute(*perm).reshape(w.shape)
+
+
+def frag16_fp8_reference(w):
+    """include/moe.h MOE_LAYOUT_FRAG16 of an FP8 [..., R, C] as a reshape /
+    permute: block (i, j) of 16 rows x 64 columns at byte (i * C/64 + j) *
+    1024, element (r, c) of a block at byte (((c % 32) / 8) * 16 + r) * 16 +
+    (c / 32) * 8 + c % 8."""
+    *lead, R, C = w.shape
+    v = w.reshape(*lead, R // 16, 16, C // 64, 2, 4, 8)   # (i, r, j, c/32, (c%32)/8, c%8)
+    n = len(lead)
+    perm = list(range(n)) + [n + 0, n + 2, n + 4, n + 1, n + 3, n + 5]
     return v.permute(*perm).reshape(w.shape)
 
 

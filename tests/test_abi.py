@@ -138,6 +138,24 @@ def test_forward_rejects_bad_arguments():
     assert _forward(_k2(w_layout=moe.MOE_LAYOUT_FRAG16), out=None) == NULL
 
 
+def test_forward_rejects_bad_fp8_arguments():
+    f8 = dict(w_dtype=moe.MOE_FP8_E4M3, w_layout=moe.MOE_LAYOUT_FRAG16)
+    S = (FAKE, FAKE, FAKE)
+    W = lambda *scales: moe.ExpertWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, *scales)  # noqa: E731
+    assert moe.workspace_size(_k2(**f8), True) > 0
+    # FP8 weights need bf16 activations and the packed layout
+    assert _forward(_k2(w_dtype=moe.MOE_FP8_E4M3), W=W(*S)) == UNSUP
+    assert _forward(_k2(act_dtype=moe.MOE_F32, **f8), W=W(*S)) == UNSUP
+    # whole 128 x 128 scale blocks, K <= 8192 per projection
+    assert _forward(_k2(F=2112, **f8), W=W(*S)) == SHAPE
+    assert _forward(_k2(d_latent=3520, **f8), W=W(*S)) == SHAPE
+    assert _forward(_k2(F=8320, **f8), W=W(*S)) == SHAPE
+    assert _forward(_k2(d=8320, **f8), W=W(*S)) == SHAPE
+    # the block scales are required
+    assert _forward(_k2(**f8), W=W()) == NULL
+    assert _forward(_k2(**f8), W=W(FAKE, FAKE, None)) == NULL
+
+
 def _pack(D, src, dst):
     return moe.lib().moe_pack_weights(None if D is None else ctypes.byref(D),
                                       None if src is None else ctypes.byref(src),
@@ -158,6 +176,10 @@ def test_pack_weights_rejects_bad_arguments():
     assert _pack(D, src, W(FAKE + 4096, None, None, None, None, None, None, None)) == SHAPE
     assert _pack(_k2(act_dtype=moe.MOE_F32), src, W(far, None, None, None, None, None, None, None)) == UNSUP
     assert _pack(_k2(F=100), src, W(far, None, None, None, None, None, None, None)) == SHAPE
+    # FP8 routed experts pack in whole 128 x 128 blocks (act bf16)
+    assert _pack(_k2(F=2112, w_dtype=moe.MOE_FP8_E4M3), src, W(far, None, None, None, None, None, None, None)) == SHAPE
+    assert _pack(_k2(w_dtype=moe.MOE_FP8_E4M3, act_dtype=moe.MOE_F32), src,
+                 W(far, None, None, None, None, None, None, None)) == UNSUP
 
 
 def test_zero_tokens_accepts_null_data_pointers():

@@ -205,7 +205,8 @@ def test_bias_quantile_parity(name, T):
 # ---------------------------------------------------------------- whole layer, every token
 @pytest.mark.parametrize("name,packed", [("tiny_fp32_t128", False), ("mid_fp32_t77", False),
                                          ("mid_bf16_t300", False), ("mid_latent_t200", False),
-                                         ("mid_bf16_t300", True), ("mid_latent_t200", True)])
+                                         ("mid_bf16_t300", True), ("mid_latent_t200", True),
+                                         ("mid_fp8_t300", True), ("mid_fp8_latent_t200", True)])
 def test_forward_parity_every_token(name, packed):
     wl = get_workload(name)
     _full_parity(wl, make_layer_inputs(wl, "cpu", seed=42), packed=packed)
@@ -250,6 +251,35 @@ def test_forward_edge_cases(case, packed):
         assert c[0] == 520 and 0 < c[1:].max() <= 64
 
 
+@pytest.mark.parametrize("case", ["one_token", "K_equals_E", "no_shared", "latent_no_shared",
+                                  "large_tiles", "large_tiles_latent", "half_tiles"])
+def test_forward_fp8_edge_cases(case):
+    # FP8 routed experts (packed): 16-row tiles below 64 rows per expert on
+    # average, 128-row tiles above; the shared experts and latent maps run
+    # as bf16 launches of their own.  Block-scale rows past N (down
+    # projections narrower than the 512-row tile) are clamped.
+    fp8 = dict(w_dtype="fp8")
+    if case == "one_token":
+        wl = _custom(T=1, **fp8)
+    elif case == "K_equals_E":
+        wl = _custom(E=16, K=16, T=33, **fp8)
+    elif case == "no_shared":
+        wl = _custom(n_shared=0, F_shared=0, T=130, **fp8)
+    elif case == "latent_no_shared":
+        wl = _custom(d=320, d_latent=128, n_shared=0, F_shared=0, T=90, scale=1.0, **fp8)
+    elif case == "large_tiles":
+        wl = _custom(E=6, K=2, T=700, d=384, F=256, n_shared=2, F_shared=64, **fp8)
+    elif case == "large_tiles_latent":  # 128-row expert tiles; bf16 128-row dense tiles
+        wl = _custom(E=5, K=2, T=1100, d=320, F=256, n_shared=1, F_shared=128, d_latent=256,
+                     scale=1.0, **fp8)
+    else:  # half_tiles: expert 0 takes every token, the others ~35 rows each
+        wl = _custom(E=16, K=2, T=520, **fp8)
+    inp = make_layer_inputs(wl, "cpu", seed=6)
+    if case == "half_tiles":
+        inp["b"][0] = 10.0
+    _full_parity(wl, inp, "fp8 " + case, packed=True)
+
+
 def test_forward_zero_tokens():
     wl = _custom(T=0)
     log("[gpu] forward T=0")
@@ -290,8 +320,9 @@ def _sampled_tokens(T, ref, counts, idx_eff, n_random=6):
     return sorted(toks)
 
 
-@pytest.mark.parametrize("packed", [False, True], ids=["rows", "packed"])
-@pytest.mark.parametrize("name", ["k2_decode_t256", "k2_prefill_t16384", "k3_latent_t4096"])
+@pytest.mark.parametrize("name,packed", [(n, p) for n in ("k2_decode_t256", "k2_prefill_t16384",
+                                                            "k3_latent_t4096") for p in (False, True)]
+                         + [("k2_decode_fp8_t256", True), ("k2_prefill_fp8_t16384", True)])
 def test_forward_parity_full_size_sampled(name, packed):
     wl = get_workload(name)
     log(f"[gpu] full-size {name}: generating inputs on the GPU")
@@ -313,10 +344,13 @@ def test_forward_parity_full_size_sampled(name, packed):
     toks = _sampled_tokens(wl.T, ref, counts, idx_eff)
     experts = set(idx_eff[toks].ravel().tolist())
     log(f"[cpu] oracle experts for {len(toks)} tokens ({len(experts)} experts)")
-    per = {k: [host(inp[k][e]) if e in experts else None for e in range(wl.E)]
-           for k in ("W_gate", "W_up", "W_down")}
+    names = ("W_gate", "W_up", "W_down") + (("W_gate_scale", "W_up_scale", "W_down_scale")
+                                              if wl.w_dtype == "fp8" else ())
+    per = {k: [host(inp[k][e]) if e in experts else None for e in range(wl.E)] for k in names}
     lay = oracle.Layer(d=wl.d, E=wl.E, K=wl.K, F=wl.F, scale=wl.scale, W_r=Wr_h, b=b_h,
                        W_gate=per["W_gate"], W_up=per["W_up"], W_down=per["W_down"],
+                       W_gate_scale=per.get("W_gate_scale"), W_up_scale=per.get("W_up_scale"),
+                       W_down_scale=per.get("W_down_scale"),
                        n_shared=wl.n_shared, F_shared=wl.F_shared,
                        Ws_gate=host(inp["Ws_gate"]), Ws_up=host(inp["Ws_up"]),
                        Ws_down=host(inp["Ws_down"]), d_latent=wl.d_latent,
