@@ -40,6 +40,12 @@ TRAFFIC_MD = os.path.join(ROOT, "profiles", "traffic.md")
 CAL_REPS = 3                # streaming copies of --calibrate-copy-gib each
 WEIGHTS_NOTE = {"frag16": "bf16, fragment-block layout (moe_pack_weights once at load, untimed)",
                 "rows": "bf16, row-major"}
+FP8_NOTE = ("routed experts FP8 E4M3FN with one E8M0 scale per 128x128 block, shared experts "
+            "bf16; fragment-block layout (moe_pack_weights once at load, untimed)")
+
+
+def weights_note(wl, layout):
+    return FP8_NOTE if wl.w_dtype == "fp8" else WEIGHTS_NOTE[layout]
 
 
 def log(msg):
@@ -86,6 +92,10 @@ def load_traffic(workload: str, layout: str):
 def up_kernel(wl, layout):
     """The kernel the library runs for the up projection of this workload."""
     big_rows = wl.T * wl.K >= 64 * wl.E and wl.act_dtype == "bf16"
+    if wl.w_dtype == "fp8":
+        return ("k_gemm_wide FP8 (" + ("128x512" if big_rows else "16x512") +
+                ", register-fed, codes converted to bf16 in registers) + the shared expert's "
+                "dense bf16 launch")
     if big_rows and layout == "frag16":
         return "k_gemm_wide (128x512, register-fed packed weights)"
     return "k_gemm_big (" + ("128x256" if big_rows else "16x512") + ", weights through LDS)"
@@ -93,13 +103,13 @@ def up_kernel(wl, layout):
 
 def is_up_kernel(name):
     """Kernel name (untruncated) of an up-projection dispatch: the SwiGLU
-    instantiation of k_gemm_wide<TC, EPI, NSEG, BM> or of
+    instantiation of k_gemm_wide<TC, EPI, NSEG, BM, F8> or of
     k_gemm_big<TC, BM, BN, WM, WN, NST, ROWB, EPI, PK>."""
     m = re.search(r"k_gemm_(wide|big)<([^>]*)>", name)
     if not m:
         return False
     args = m.group(2).replace(" ", "").split(",")
-    if m.group(1) == "wide":          # k_gemm_wide<TC, EPI, NSEG, BM>
+    if m.group(1) == "wide":          # k_gemm_wide<TC, EPI, NSEG, BM, F8>
         return args[1] == "1"
     return args[7] == "1"
 
@@ -122,7 +132,12 @@ def work_model(wl, counts):
     Fsh = wl.n_shared * wl.F_shared
     A = wl.T * wl.K
     touched = int(sum(1 for c in counts if c > 0))
-    w_expert = 3 * din * F * es
+    # routed weights: es bytes per element, or one FP8 byte plus one scale
+    # byte per 128 x 128 block
+    f8 = wl.w_dtype == "fp8"
+    wes = 1 if f8 else es
+    sblk = (F // 128) * (din // 128) if f8 else 0
+    w_expert = 3 * din * F * wes + 3 * sblk
     flops_routed = 2.0 * A * 3 * din * F
     flops_shared = 2.0 * T * 3 * d * Fsh
     flops_latent = 2.0 * T * d * wl.d_latent * 2
@@ -132,7 +147,7 @@ def work_model(wl, counts):
 
     up = dict(
         flops=2.0 * A * din * 2 * F + 2.0 * T * d * 2 * Fsh,
-        bytes=(touched * 2 * F * din * es + 2 * Fsh * d * es + T * din * es
+        bytes=(touched * (2 * F * din * wes + 2 * sblk) + 2 * Fsh * d * es + T * din * es
                + A * F * es + T * Fsh * es))
     return dict(touched=touched, flops_bf16=flops_routed + flops_shared + flops_latent,
                 flops_router=flops_router, bytes=bytes_step, up=up)
@@ -148,7 +163,7 @@ def _events(torch, n, stream):
 def prepare(moe, torch, wl, rows, layout):
     """The weights the layer reads: row-major as generated, or packed once
     (a one-time load step, not part of the timed forward)."""
-    if layout == "rows":
+    if layout == "rows" and wl.w_dtype != "fp8":   # FP8 experts are read packed only
         return rows
     packed = moe.pack_weights(rows, n_shared=wl.n_shared)
     torch.cuda.synchronize()
@@ -382,7 +397,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="k2_prefill_t16384")
-    ap.add_argument("--also", default="k2_decode_t256,k2_router_t4096,k2_router_g8_t4096,k3_latent_t4096",
+    ap.add_argument("--also", default="k2_decode_t256,k2_router_t4096,k2_router_g8_t4096,k3_latent_t4096,"
+                                      "k2_decode_fp8_t256,k2_prefill_fp8_t16384",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="target seconds of oracle time (0 skips the CPU baseline)")
@@ -451,8 +467,8 @@ def main():
             log(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step")
             also[name] = r
             continue
-        same = (awl.d, awl.E, awl.F, awl.n_shared, awl.F_shared, awl.d_latent, awl.act_dtype) == \
-               (wl.d, wl.E, wl.F, wl.n_shared, wl.F_shared, wl.d_latent, wl.act_dtype)
+        same = (awl.d, awl.E, awl.F, awl.n_shared, awl.F_shared, awl.d_latent, awl.act_dtype, awl.w_dtype) == \
+               (wl.d, wl.E, wl.F, wl.n_shared, wl.F_shared, wl.d_latent, wl.act_dtype, wl.w_dtype)
         if not same:
             del weights
             torch.cuda.empty_cache()
@@ -469,7 +485,7 @@ def main():
                           config=dict(workload=name, T=awl.T, d=awl.d, E=awl.E, K=awl.K,
                                       F=awl.F, n_shared=awl.n_shared, F_shared=awl.F_shared,
                                       d_latent=awl.d_latent, scale=awl.scale,
-                                      weights=WEIGHTS_NOTE[args.layout]))
+                                      weights=weights_note(awl, args.layout)))
     if args.bias_steps:
         log("[bench] bias updates")
         del weights
@@ -486,7 +502,7 @@ def main():
         "data": "synthetic (seeded N(0,1) x, N(0,1/fan_in) weights, Zipf(1.1) expert skew)",
         "config": dict(workload=mw.name, T=mw.T, d=mw.d, E=mw.E, K=mw.K, F=mw.F,
                        n_shared=mw.n_shared, F_shared=mw.F_shared, d_latent=mw.d_latent,
-                       scale=mw.scale, weights=WEIGHTS_NOTE[args.layout],
+                       scale=mw.scale, weights=weights_note(mw, args.layout),
                        parallelism="single-gpu"),
         "roofline": main_r["roofline"], "cpu_baseline": cpu, "layer": main_r["layer"],
         "stages_ms": main_r["stages"], "kernel_source": source_hash(), "also": also,

@@ -14,10 +14,9 @@
 // the worst case and tiles past the device-side tile count exit at once.
 // Weight GEMMs at prefill sizes use the register-fed WIDE tile when the
 // weights are packed (MOE_LAYOUT_FRAG16), the LDS tile otherwise.
-// FP8 routed experts (w_dtype MOE_FP8_E4M3): the routed up and down
-// projections are FP8-weight launches of their own (WIDE, or WIDE16 at
-// decode sizes) and the shared experts, bf16, run as dense launches beside
-// them; the tile table then holds routed tiles only.
+// FP8 routed experts (w_dtype MOE_FP8_E4M3): the up and down projections
+// run the FP8 form of the WIDE tile (WIDE16 at decode sizes), whose shared
+// (bf16) tiles take the bf16 path inside the same launch.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -133,7 +132,7 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
     p.bm = tile_bm(p.ecfg);
     p.dcfg = (p.T >= 1024 && p.dt == DT_BF16) ? big : TILE_SMALL;
     p.nch = static_cast<int>(cdiv(p.T, 64));
-    p.max_tiles = static_cast<int>(cdiv(p.A, p.bm) + p.E + (p.ns && !p.f8 ? cdiv(p.T, p.bm) : 0));
+    p.max_tiles = static_cast<int>(cdiv(p.A, p.bm) + p.E + (p.ns ? cdiv(p.T, p.bm) : 0));
 
     int64_t off = 0;
     auto take = [&](int64_t bytes) {
@@ -157,7 +156,7 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
         p.o_sorted = take(p.A * 4);
         p.o_pos = take(p.A * 4);
         p.o_tiles = take(static_cast<int64_t>(p.max_tiles) * sizeof(TileInfo));
-        p.o_ntiles = take(4);
+        p.o_ntiles = take(8);
         if (p.dl) p.o_xlat = take(T * p.dl * p.es);
         p.o_H = take(p.A * p.F * p.es);
         if (p.ns) p.o_Hs = take(T * p.Fsh * p.es);
@@ -225,25 +224,14 @@ moe_status run_router(const Plan& p, const void* x, const float* W_r, const floa
     return MOE_OK;
 }
 
-// FP8 form of a grouped projection: g.g[0] (routed, FP8 weights with block
-// scales bs / bsu) on the tile table, then g.g[1] (shared experts, bf16;
-// absent when its N is 0) as a dense launch over the T tokens.
-moe_status run_f8_pair(const Plan& p, const GemmArgs& g, const uint8_t* bs, const uint8_t* bsu, Epi epi, int n_routed,
-                       hipStream_t s) {
-    GemmArgs r = g;
-    r.g[1] = GemmGroup{};
-    r.g[0].bs = bs;
-    r.g[0].bsu = bsu;
-    r.g[0].s_estride = static_cast<int64_t>(r.g[0].N / 128) * (r.g[0].seg[0].K / 128);
-    MOE_HIP(launch_gemm_f8(r, epi, p.ecfg, p.max_tiles, n_routed, s));
-    if (g.g[1].N > 0) {
-        GemmArgs d = gemm_args();
-        d.g[0] = g.g[1];
-        d.M = p.T;
-        MOE_HIP(launch_gemm(d, p.dt, false, epi, p.dcfg, static_cast<int>(cdiv(p.T, tile_bm(p.dcfg))), d.g[0].N,
-                            p.packed, s));
-    }
-    return MOE_OK;
+// FP8 form of a grouped projection: g.g[0] the routed experts (FP8 weights
+// with block scales bs / bsu), g.g[1] the shared experts (bf16), one launch.
+hipError_t launch_f8(const Plan& p, GemmArgs g, const uint8_t* bs, const uint8_t* bsu, Epi epi, int max_n,
+                     hipStream_t s) {
+    g.g[0].bs = bs;
+    g.g[0].bsu = bsu;
+    g.g[0].s_estride = static_cast<int64_t>(g.g[0].N / 128) * (g.g[0].seg[0].K / 128);
+    return launch_gemm_f8(g, epi, p.ecfg, p.max_tiles, max_n, s);
 }
 
 hipError_t record(void* const* ev, int i, hipStream_t s) {
@@ -273,9 +261,8 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
     moe_status st = run_router(p, x, W_r, b, idx, w, nullptr, ws, s);
     if (st != MOE_OK) return st;
     MOE_HIP(record(ev, MOE_EV_ROUTER, s));
-    // shared tiles ride in the routed launches (rows = tokens), except with
-    // FP8 routed weights, where they run as dense bf16 launches of their own
-    MOE_HIP(launch_dispatch(idx, p.T, p.E, p.K, p.bm, p.ns && !p.f8 ? p.T : 0, at<uint64_t>(ws, p.o_masks),
+    // shared tiles ride in the routed launches (rows = tokens)
+    MOE_HIP(launch_dispatch(idx, p.T, p.E, p.K, p.bm, p.ns ? p.T : 0, at<uint64_t>(ws, p.o_masks),
                             at<int32_t>(ws, p.o_cbase), counts, offsets, sorted, pos, tiles, ntiles, s));
     MOE_HIP(record(ev, MOE_EV_DISPATCH, s));
 
@@ -313,12 +300,10 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
         S1.ldc = p.Fsh;
         g.tiles = tiles;
         g.ntiles = ntiles;
-        if (p.f8) {
-            st = run_f8_pair(p, g, W->W_gate_scale, W->W_up_scale, EPI_SWIGLU, p.F, s);
-            if (st != MOE_OK) return st;
-        } else {
+        if (p.f8)
+            MOE_HIP(launch_f8(p, g, W->W_gate_scale, W->W_up_scale, EPI_SWIGLU, std::max(p.F, p.Fsh), s));
+        else
             MOE_HIP(launch_gemm(g, p.dt, false, EPI_SWIGLU, p.ecfg, p.max_tiles, std::max(p.F, p.Fsh), p.packed, s));
-        }
     }
     MOE_HIP(record(ev, MOE_EV_UP, s));
     // down projection: routed -> Y[sorted rows]; shared (K2 form) -> Y[A + t]
@@ -332,19 +317,7 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
         R0.C = Y;
         R0.ldc = p.din;
         GemmGroup& S1 = g.g[1];
-        if (p.f8) {
-            if (p.ns && !latent) {
-                S1.seg[0] = GemmSeg{Hs, W->Ws_down, nullptr, p.Fsh, p.Fsh, p.Fsh, 0};
-                S1.nseg = 1;
-                S1.N = p.d;
-                S1.C = Y + p.A * p.d * p.es;
-                S1.ldc = p.d;
-            }
-            g.tiles = tiles;
-            g.ntiles = ntiles;
-            st = run_f8_pair(p, g, W->W_down_scale, nullptr, EPI_STORE, p.din, s);
-            if (st != MOE_OK) return st;
-        } else if (p.ns && !latent) {
+        if (p.ns && !latent) {
             S1.seg[0] = GemmSeg{Hs, W->Ws_down, nullptr, p.Fsh, p.Fsh, p.Fsh, 0};
             S1.nseg = 1;
             S1.N = p.d;
@@ -354,11 +327,12 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
             S1.N = 0;  // shared tiles (latent form) do nothing here
             S1.nseg = 0;
         }
-        if (!p.f8) {
-            g.tiles = tiles;
-            g.ntiles = ntiles;
+        g.tiles = tiles;
+        g.ntiles = ntiles;
+        if (p.f8)
+            MOE_HIP(launch_f8(p, g, W->W_down_scale, nullptr, EPI_STORE, p.din, s));
+        else
             MOE_HIP(launch_gemm(g, p.dt, false, EPI_STORE, p.ecfg, p.max_tiles, p.din, p.packed, s));
-        }
     }
     MOE_HIP(record(ev, MOE_EV_DOWN, s));
     if (!latent) {

@@ -109,7 +109,10 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(const uint64_t* __restri
         ti.pad0_ = ti.pad1_ = 0;
         tiles[ttotal + j] = ti;
     }
-    if (threadIdx.x == 0) *ntiles = ttotal + nsh;
+    if (threadIdx.x == 0) {
+        ntiles[0] = ttotal + nsh;
+        ntiles[1] = ttotal;
+    }
 }
 
 __global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t* __restrict__ idx, int T, int E, int K, int nch,

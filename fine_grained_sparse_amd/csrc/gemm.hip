@@ -317,18 +317,31 @@ __device__ __forceinline__ int swz(int row) {
 // expert, or up to 8 dense row tiles), inside a run N tile by N tile with
 // the M tile fastest.  A run of `cnt` tiles starting at tile `first`
 // occupies slots [first*ntn, (first+cnt)*ntn), so slot / ntn names a tile of
-// the run that owns the slot.  Returns false for blocks without work.
+// the run that owns the slot.  With a tile table the routed slots and the
+// shared-expert slots (the table's tail) are split across the XCDs
+// separately, each XCD walking a stretch of either: the shared tiles re-read
+// one weight matrix per run and would otherwise all land on the last XCD.
+// The grid holds 8 * (per_routed + per_shared) blocks or more (launch
+// grids carry 16 spare blocks).  Returns false for blocks without work.
 struct Job {
     int gi, expert, row0, rows, n0;
 };
 
 template <int BM, int BNO>
 __device__ __forceinline__ bool pick_job(const GemmArgs& a, Job& jb) {
-    const int total = (a.tiles ? *a.ntiles : (a.M + BM - 1) / BM) * a.ntn;  // active (M, N) tile pairs
-    const int per = (total + 7) >> 3;
-    const int slot = static_cast<int>(blockIdx.x) >> 3;
-    const int lin = (static_cast<int>(blockIdx.x) & 7) * per + slot;
-    if (slot >= per || lin >= total) return false;
+    const int total = (a.tiles ? a.ntiles[0] : (a.M + BM - 1) / BM) * a.ntn;  // active (M, N) tile pairs
+    const int total_r = a.tiles ? a.ntiles[1] * a.ntn : total;                // ... of them routed
+    const int per = (total_r + 7) >> 3, per_s = (total - total_r + 7) >> 3;
+    const int slot = static_cast<int>(blockIdx.x) >> 3, xcd = static_cast<int>(blockIdx.x) & 7;
+    int lin;
+    if (slot < per) {
+        lin = xcd * per + slot;
+        if (lin >= total_r) return false;
+    } else {
+        const int k = slot - per;
+        lin = total_r + xcd * per_s + k;
+        if (k >= per_s || lin >= total) return false;
+    }
     int first, cnt;
     if (a.tiles) {
         const TileInfo t0 = a.tiles[lin / a.ntn];
@@ -637,8 +650,13 @@ __global__ __launch_bounds__(64 * WM * WN, (big_occupancy<BM, BN, NST, ROWB>()))
 // re-read it), so the loads younger than A(it + 1) at its wait are a
 // compile-time count (the first stages, after a prologue of A(0..NST-1) and
 // B(0), have their own).
+template <int BM>
+constexpr int wide_lds_bytes() {  // the A ring, or the epilogue's fp32 staging
+    return 4 * BM * 128 > BM * (256 + 4) * 4 ? 4 * BM * 128 : BM * (256 + 4) * 4;
+}
+
 template <typename TC, int EPI, int NSEG, int BM, bool F8>
-__global__ __launch_bounds__(256, BM >= 64 ? 1 : 2) void k_gemm_wide(const GemmArgs a) {
+__device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char* lds) {
     using T = bf16_t;
     static_assert(BM == 128 || BM == 64 || BM == 32 || BM == 16, "row tiles");
     static_assert(!F8 || NSEG == 1, "FP8 weights: one K segment");
@@ -668,12 +686,8 @@ __global__ __launch_bounds__(256, BM >= 64 ? 1 : 2) void k_gemm_wide(const GemmA
     constexpr int kWait0 = kY0 < kWaitA ? kY0 : kWaitA, kWait1 = kY1 < kWaitA ? kY1 : kWaitA;
     static_assert(kWaitA < 64 && (NSEG == 1 || NSEG == 2) && NST == 4, "vmcnt range; shape");
     constexpr int WP = 256;
-    constexpr int EP_BYTES = BM * (WP + 4) * 4;
-    constexpr int LDS_BYTES = NST * STAGE > EP_BYTES ? NST * STAGE : EP_BYTES;
-    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+    static_assert(NST * STAGE <= wide_lds_bytes<BM>() && BM * (WP + 4) * 4 <= wide_lds_bytes<BM>(), "LDS");
 
-    Job jb;
-    if (!pick_job<BM, BNO>(a, jb)) return;
     const GemmGroup& G = jb.gi ? a.g[1] : a.g[0];
     const int N = G.N, row0 = jb.row0, rows = jb.rows, n0 = jb.n0;
     const int nk0 = G.seg[0].K / BKE;
@@ -856,6 +870,24 @@ __global__ __launch_bounds__(256, BM >= 64 ? 1 : 2) void k_gemm_wide(const GemmA
                                                           n0);
 }
 
+// F8: group 0 (routed experts) has FP8 weights, group 1 (the shared
+// experts, riding in the same launch) bf16 ones; a tile takes its group's
+// path.
+template <typename TC, int EPI, int NSEG, int BM, bool F8>
+__global__ __launch_bounds__(256, BM >= 64 ? 1 : 2) void k_gemm_wide(const GemmArgs a) {
+    __shared__ __attribute__((aligned(1024))) char lds[wide_lds_bytes<BM>()];
+    constexpr int BNO = EPI == EPI_SWIGLU ? 256 : 512;
+    Job jb;
+    if (!pick_job<BM, BNO>(a, jb)) return;
+    if constexpr (F8) {
+        if (jb.gi) {
+            wide_tile<TC, EPI, 1, BM, false>(a, jb, lds);
+            return;
+        }
+    }
+    wide_tile<TC, EPI, NSEG, BM, F8>(a, jb, lds);
+}
+
 // fp32 operands: register-staged 16 x 256 tiles
 constexpr int kF32BN = 256;
 // decode tile (few rows per expert): 16 x 512, two stages of 128-byte row pieces
@@ -877,6 +909,17 @@ int tile_bn_out(TileCfg cfg, Epi epi) {  // bf16 kernels (sizing heuristics only
 }
 
 namespace {
+
+// Grid of a pick_job launch.  The XCD-aware remap sends block b to a
+// logical slot in the stretch of XCD b % 8; the routed and shared stretches
+// (ceil(routed / 8) + ceil(shared / 8) blocks per XCD) cover every active
+// slot only when the grid holds 8 times that, at most the active pairs plus
+// 14: round the grid up to a multiple of 8 and add 16 (blocks past the
+// active slots return at once).
+unsigned job_blocks(int max_tiles, int ntn) {
+    const unsigned blocks = static_cast<unsigned>(max_tiles) * static_cast<unsigned>(ntn);
+    return ((blocks + 7u) & ~7u) + 16u;
+}
 
 // What the wide kernel handles: packed weights, one or two K segments per
 // group (multiples of 64), no split K, fragment-block byte offsets in 31 bits.
@@ -911,12 +954,7 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
     const int bno = EPI == EPI_SWIGLU ? bn / 2 : bn;
     GemmArgs a = args;
     a.ntn = (max_n + bno - 1) / bno;
-    // The XCD-aware remap sends block b to logical slot (b % 8) * per + b / 8
-    // with per = ceil(active / 8); it covers every active slot only when the
-    // grid holds 8 * per blocks, so round the grid up to a multiple of 8
-    // (blocks past the active slots return at once).
-    const unsigned blocks = static_cast<unsigned>(max_tiles) * a.ntn;
-    dim3 grid((blocks + 7u) & ~7u, 1, a.nsplit);
+    const dim3 grid(job_blocks(max_tiles, a.ntn), 1, a.nsplit);
     if constexpr (sizeof(T) == 4) {
         hipLaunchKernelGGL((k_gemm<T, TC, 16, kF32BN, 1, 4, EPI>), grid, dim3(256), 0, stream, a);
     } else {
@@ -944,21 +982,18 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
     return hipGetLastError();
 }
 
-// What the FP8 form of the wide kernel handles: one K segment per group,
-// block scales present, rows and K in whole 128 x 128 scale blocks, the
-// scale row of a 128-row block in one wave (K <= 8192), byte offsets in 31
-// bits.
+// What the FP8 form of the wide kernel handles: one K segment per group;
+// group 0 with block scales, rows and K in whole 128 x 128 scale blocks,
+// the scale row of a 128-row block in one wave (K <= 8192), byte offsets
+// in 31 bits; group 1 (bf16) as wide_fits.
 bool wide_f8_fits(const GemmArgs& a, Epi epi) {
-    if (a.nsplit != 1) return false;
-    for (int g = 0; g < 2; ++g) {
-        const GemmGroup& G = a.g[g];
-        if (G.N == 0) continue;
-        const int K = G.seg[0].K;
-        if (G.nseg != 1 || !G.bs || (epi == EPI_SWIGLU && !G.bsu)) return false;
-        if (G.N % 128 || K < 128 || K % 128 || K > 64 * 128) return false;
-        if (static_cast<int64_t>(G.N) * K >= (int64_t{1} << 31)) return false;
-    }
-    return true;
+    if (a.nsplit != 1 || !wide_fits(a)) return false;
+    const GemmGroup& G = a.g[0];
+    const int K = G.seg[0].K;
+    if (G.N == 0 || G.nseg != 1 || (a.g[1].N != 0 && a.g[1].nseg != 1)) return false;
+    if (!G.bs || (epi == EPI_SWIGLU && !G.bsu)) return false;
+    if (G.N % 128 || K < 128 || K % 128 || K > 64 * 128) return false;
+    return static_cast<int64_t>(G.N) * K < (int64_t{1} << 31);
 }
 
 template <int EPI>
@@ -968,8 +1003,7 @@ hipError_t launch_f8_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max
     constexpr int bno = EPI == EPI_SWIGLU ? kWideBN / 2 : kWideBN;
     GemmArgs a = args;
     a.ntn = (max_n + bno - 1) / bno;
-    const unsigned blocks = static_cast<unsigned>(max_tiles) * a.ntn;
-    dim3 grid((blocks + 7u) & ~7u, 1, 1);  // a multiple of 8: see launch_t
+    const dim3 grid(job_blocks(max_tiles, a.ntn), 1, 1);
     if (cfg == TILE_WIDE)
         hipLaunchKernelGGL((k_gemm_wide<bf16_t, EPI, 1, kWideBM, true>), grid, dim3(256), 0, stream, a);
     else

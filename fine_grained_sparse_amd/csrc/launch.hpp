@@ -64,7 +64,7 @@ struct TileInfo {
 struct GemmArgs {
     GemmGroup g[2];
     const TileInfo* tiles;   // device tile table (grouped) or NULL (dense)
-    const int32_t* ntiles;   // device count of valid tiles (grouped)
+    const int32_t* ntiles;   // device counts (grouped): [0] valid tiles, [1] of them routed (group 0)
     int32_t M;               // dense: rows of group 0
     int32_t nsplit;          // split-K ways; output split s at C + s*split_stride
     int64_t split_stride;
@@ -80,10 +80,10 @@ hipError_t launch_gemm(const GemmArgs& args, DType dt, bool out_f32, Epi epi,
                        TileCfg cfg, int max_tiles, int max_n, bool packed,
                        hipStream_t stream);
 
-// C = epi(A * B^T) with bf16 A and C and block-scaled FP8 B (16 x 64
-// fragment blocks of MOE_LAYOUT_FRAG16 for FP8): one K segment per group,
-// N and K multiples of 128, K <= 8192.  cfg: TILE_WIDE (128-row tiles) or
-// TILE_WIDE16 (16-row tiles).
+// C = epi(A * B^T) with bf16 A and C; group 0 with block-scaled FP8 B
+// (16 x 64 fragment blocks of MOE_LAYOUT_FRAG16 for FP8; N and K multiples
+// of 128, K <= 8192), group 1 with packed bf16 B; one K segment per group.
+// cfg: TILE_WIDE (128-row tiles) or TILE_WIDE16 (16-row tiles).
 hipError_t launch_gemm_f8(const GemmArgs& args, Epi epi, TileCfg cfg, int max_tiles, int max_n,
                           hipStream_t stream);
 
@@ -126,7 +126,7 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n,
 
 // Histogram, scan and stable permutation; also the tile table for the
 // grouped GEMMs (routed tiles of bm rows, then shared tiles if
-// shared_rows > 0).
+// shared_rows > 0) and ntiles[0..1] = (all tiles, routed tiles).
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int K, int bm,
                            int shared_rows, uint64_t* masks,
                            int32_t* chunk_base, int32_t* counts,
