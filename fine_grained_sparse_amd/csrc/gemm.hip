@@ -658,7 +658,7 @@ constexpr int wide_lds_bytes() {  // the A ring, or the epilogue's fp32 staging
 template <typename TC, int EPI, int NSEG, int BM, bool F8>
 __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char* lds) {
     using T = bf16_t;
-    static_assert(BM == 128 || BM == 64 || BM == 32 || BM == 16, "row tiles");
+    static_assert(BM % 16 == 0 && BM <= 128 && (BM * 128 / 1024 < 4 || BM * 128 / 1024 % 4 == 0), "row tiles");
     static_assert(!F8 || NSEG == 1, "FP8 weights: one K segment");
     constexpr int ES = 2, BN = 512, NW = 4, TN = BN / NW;
     constexpr int WES = F8 ? 1 : 2;            // bytes per weight element
@@ -874,11 +874,7 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
 // experts, riding in the same launch) bf16 ones; a tile takes its group's
 // path.
 template <typename TC, int EPI, int NSEG, int BM, bool F8>
-__global__ __launch_bounds__(256, BM >= 64 ? 1 : 2) void k_gemm_wide(const GemmArgs a) {
-    __shared__ __attribute__((aligned(1024))) char lds[wide_lds_bytes<BM>()];
-    constexpr int BNO = EPI == EPI_SWIGLU ? 256 : 512;
-    Job jb;
-    if (!pick_job<BM, BNO>(a, jb)) return;
+__device__ __forceinline__ void wide_group(const GemmArgs& a, const Job& jb, char* lds) {
     if constexpr (F8) {
         if (jb.gi) {
             wide_tile<TC, EPI, 1, BM, false>(a, jb, lds);
@@ -886,6 +882,32 @@ __global__ __launch_bounds__(256, BM >= 64 ? 1 : 2) void k_gemm_wide(const GemmA
         }
     }
     wide_tile<TC, EPI, NSEG, BM, F8>(a, jb, lds);
+}
+
+// A 128-row tile holding fewer rows (the ragged last tile of an expert)
+// runs the body of the next multiple of 32 rows: fewer MFMAs and less A
+// traffic, the same weight traffic.
+template <typename TC, int EPI, int NSEG, int BM, bool F8>
+__global__ __launch_bounds__(256, BM >= 64 ? 1 : 2) void k_gemm_wide(const GemmArgs a) {
+    __shared__ __attribute__((aligned(1024))) char lds[wide_lds_bytes<BM>()];
+    constexpr int BNO = EPI == EPI_SWIGLU ? 256 : 512;
+    Job jb;
+    if (!pick_job<BM, BNO>(a, jb)) return;
+    if constexpr (BM == 128) {
+        if (jb.rows <= 32) {
+            wide_group<TC, EPI, NSEG, 32, F8>(a, jb, lds);
+            return;
+        }
+        if (jb.rows <= 64) {
+            wide_group<TC, EPI, NSEG, 64, F8>(a, jb, lds);
+            return;
+        }
+        if (jb.rows <= 96) {
+            wide_group<TC, EPI, NSEG, 96, F8>(a, jb, lds);
+            return;
+        }
+    }
+    wide_group<TC, EPI, NSEG, BM, F8>(a, jb, lds);
 }
 
 // fp32 operands: register-staged 16 x 256 tiles

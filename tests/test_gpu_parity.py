@@ -280,6 +280,29 @@ def test_forward_fp8_edge_cases(case):
     _full_parity(wl, inp, "fp8 " + case, packed=True)
 
 
+@pytest.mark.parametrize("w_dtype", ["bf16", "fp8"])
+def test_forward_tile_row_buckets(w_dtype):
+    # Experts with 1, 31, 32, 33, ... 129, 200 rows: the ragged last 128-row
+    # tile of each expert runs the 32-, 64-, 96- or 128-row body; every
+    # bucket edge appears.  Token t is steered to expert f(t) by a one-hot
+    # feature that only W_r[f(t)] weights heavily (K = 1, wide margins).
+    sizes = [1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 200]
+    E, T, d = len(sizes), sum(sizes), 256
+    wl = _custom(E=E, K=1, T=T, d=d, F=128, w_dtype=w_dtype)
+    inp = make_layer_inputs(wl, "cpu", seed=8)
+    g = torch.Generator().manual_seed(8)
+    owner = torch.cat([torch.full((c,), e, dtype=torch.int64) for e, c in enumerate(sizes)])
+    owner = owner[torch.randperm(T, generator=g)]
+    x = torch.randn((T, d), generator=g) * 0.1
+    x[torch.arange(T), owner] += 4.0
+    inp["x"] = x.to(torch.bfloat16)
+    W_r = torch.randn((E, d), generator=g) * 0.01
+    W_r[torch.arange(E), torch.arange(E)] = 8.0
+    inp["W_r"], inp["b"] = W_r.contiguous(), torch.zeros(E)
+    _, r, _ = _full_parity(wl, inp, f"{w_dtype} row buckets", packed=True)
+    assert r["counts"].cpu().tolist() == sizes
+
+
 def test_forward_zero_tokens():
     wl = _custom(T=0)
     log("[gpu] forward T=0")
