@@ -94,8 +94,8 @@ def up_kernel(wl, layout):
     big_rows = wl.T * wl.K >= 64 * wl.E and wl.act_dtype == "bf16"
     if wl.w_dtype == "fp8":
         return ("k_gemm_wide FP8 (" + ("128x512" if big_rows else "16x512") +
-                ", register-fed, codes converted to bf16 in registers) + the shared expert's "
-                "dense bf16 launch")
+                ", register-fed, codes converted to bf16 in registers; the shared expert's "
+                "tiles take the bf16 path in the same launch)")
     if big_rows and layout == "frag16":
         return "k_gemm_wide (128x512, register-fed packed weights)"
     return "k_gemm_big (" + ("128x256" if big_rows else "16x512") + ", weights through LDS)"
