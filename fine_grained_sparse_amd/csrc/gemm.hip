@@ -651,8 +651,72 @@ __global__ __launch_bounds__(64 * WM * WN, (big_occupancy<BM, BN, NST, ROWB>()))
 // compile-time count (the first stages, after a prologue of A(0..NST-1) and
 // B(0), have their own).
 template <int BM>
-constexpr int wide_lds_bytes() {  // the A ring, or the epilogue's fp32 staging
-    return 4 * BM * 128 > BM * (256 + 4) * 4 ? 4 * BM * 128 : BM * (256 + 4) * 4;
+constexpr int wide_lds_bytes() {  // the A ring: four 64-K stages of BM rows
+    return 4 * BM * 128;
+}
+
+// Results of a register-fed tile straight to C (no LDS).  The MFMAs there
+// take the weight fragment as their first operand, so acc[i][j] holds rows
+// 16 i + lane % 16 and the four consecutive columns 16 j + 4 (lane / 16) ..
+// + 3 of the wave's block (for SwiGLU, blocks j < NB/2 are the gate and j +
+// NB/2 the matching up columns).  bf16: blocks go in pairs (j0, j0 + 1);
+// lanes l and l ^ 16 trade one 8-byte half (ds_swizzle, xor 16), after which
+// each lane holds 8 consecutive columns of one row and stores 16 bytes, and
+// the four lanes of a row cover 64 contiguous bytes.  fp32: 16 bytes per
+// block and lane.  Rows past `rows` and columns past N are not stored.
+template <typename TC, int EPI, int MB, int NB, int TN>
+__device__ __forceinline__ void store_direct(const f32x4 (&acc)[MB][NB], const GemmGroup& G, TC* C, int row0,
+                                             int rows, int n0, int wid) {
+    const int lane = threadIdx.x & 63;
+    const int N = G.N, q = lane >> 4;
+    constexpr int NJ = EPI == EPI_SWIGLU ? NB / 2 : NB;  // output blocks per row
+    const int cb = n0 + wid * (EPI == EPI_SWIGLU ? TN / 2 : TN);
+    auto val = [&](int i, int j, int e) {
+        if (EPI == EPI_SWIGLU) {
+            const float g = acc[i][j][e], u = acc[i][j + NB / 2][e];
+            return g / (1.0f + expf(-g)) * u;
+        }
+        return acc[i][j][e];
+    };
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        const int r = i * 16 + (lane & 15);
+        TC* dst = C + static_cast<int64_t>(row0 + (r < rows ? r : 0)) * G.ldc;
+        if constexpr (sizeof(TC) == 4) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int col = cb + j * 16 + 4 * q;
+                if (r < rows && col < N)
+                    *reinterpret_cast<float4*>(dst + col) = make_float4(val(i, j, 0), val(i, j, 1), val(i, j, 2),
+                                                                        val(i, j, 3));
+            }
+        } else {
+            static_assert(NJ % 2 == 0, "block pairs");
+#pragma unroll
+            for (int jp = 0; jp < NJ / 2; ++jp) {
+                const int j0 = 2 * jp, j1 = j0 + 1;
+                uint32_t p0[2], p1[2];  // bf16 pairs: columns 4q .. 4q+3 of blocks j0, j1
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    p0[h] = f32_to_bf16(val(i, j0, 2 * h)) |
+                            (static_cast<uint32_t>(f32_to_bf16(val(i, j0, 2 * h + 1))) << 16);
+                    p1[h] = f32_to_bf16(val(i, j1, 2 * h)) |
+                            (static_cast<uint32_t>(f32_to_bf16(val(i, j1, 2 * h + 1))) << 16);
+                }
+                // even q keeps block j0 and receives its neighbour's j0 columns;
+                // odd q keeps block j1 and receives its neighbour's j1 columns
+                const bool odd = q & 1;
+                uint32_t rcv[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    rcv[h] = static_cast<uint32_t>(
+                        __builtin_amdgcn_ds_swizzle(static_cast<int>(odd ? p0[h] : p1[h]), 0x401F));
+                const int col = odd ? cb + j1 * 16 + 4 * (q - 1) : cb + j0 * 16 + 4 * q;
+                const uint4 v = odd ? make_uint4(rcv[0], rcv[1], p1[0], p1[1]) : make_uint4(p0[0], p0[1], rcv[0], rcv[1]);
+                if (r < rows && col < N) *reinterpret_cast<uint4*>(dst + col) = v;
+            }
+        }
+    }
 }
 
 template <typename TC, int EPI, int NSEG, int BM, bool F8>
@@ -685,8 +749,7 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
     constexpr int kY0 = NAB * (NST - 2) + NBL + NB, kY1 = NAB * (NST - 3) + NBL + NB + LOADS;
     constexpr int kWait0 = kY0 < kWaitA ? kY0 : kWaitA, kWait1 = kY1 < kWaitA ? kY1 : kWaitA;
     static_assert(kWaitA < 64 && (NSEG == 1 || NSEG == 2) && NST == 4, "vmcnt range; shape");
-    constexpr int WP = 256;
-    static_assert(NST * STAGE <= wide_lds_bytes<BM>() && BM * (WP + 4) * 4 <= wide_lds_bytes<BM>(), "LDS");
+    static_assert(NST * STAGE <= wide_lds_bytes<BM>(), "LDS");
 
     const GemmGroup& G = jb.gi ? a.g[1] : a.g[0];
     const int N = G.N, row0 = jb.row0, rows = jb.rows, n0 = jb.n0;
@@ -818,10 +881,10 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
                 fp8x16_to_bf16(fb[0][j], (EPI == EPI_SWIGLU && j >= NB / 2) ? su : sg, f0, f1[j]);
                 fb[0][j] = load_b(kb, 0, j);
 #pragma unroll
-                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa0[i], f0, acc[i][j]);
+                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(f0, fa0[i], acc[i][j]);
             } else {
 #pragma unroll
-                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa0[i], fb[0][j], acc[i][j]);
+                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fb[0][j], fa0[i], acc[i][j]);
                 fb[0][j] = load_b(kb, 0, j);
             }
             if (j == 1) read_a(fa1, it, fo1);
@@ -836,10 +899,10 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
         for (int j = 0; j < NB; ++j) {
             if constexpr (F8) {
 #pragma unroll
-                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa1[i], f1[j], acc[i][j]);
+                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(f1[j], fa1[i], acc[i][j]);
             } else {
 #pragma unroll
-                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fa1[i], fb[1][j], acc[i][j]);
+                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fb[1][j], fa1[i], acc[i][j]);
                 fb[1][j] = load_b(kb, 1, j);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -864,10 +927,8 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
             else
                 wait_vmcnt<kWait1>();
         });
-    wait_vmcnt<0>();  // no DMA may land in LDS once the epilogue reuses it
-
-    store_tile<TC, EPI, BM, BNO, BM, TN, MB, NB, WP, 256>(acc, lds, 0, wid, G, static_cast<TC*>(G.C), row0, rows,
-                                                          n0);
+    wait_vmcnt<0>();  // every DMA has landed before the workgroup ends
+    store_direct<TC, EPI, MB, NB, TN>(acc, G, static_cast<TC*>(G.C), row0, rows, n0, wid);
 }
 
 // F8: group 0 (routed experts) has FP8 weights, group 1 (the shared
