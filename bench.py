@@ -450,13 +450,7 @@ def main():
     log(f"[bench] timing {wl.name}: warmup {args.warmup}, steps {args.steps}")
     main_r = measure_layer(moe, torch, wl, weights, args.steps, args.warmup, args.seed, args.layout)
     log(f"[bench] {wl.name}: {main_r['ms']:.3f} ms/step, stages {main_r['stages']}")
-    cpu = None
-    if args.cpu_baseline_seconds > 0:
-        log("[bench] CPU baseline (oracle)")
-        x, W_r, b = main_r["inputs"]
-        cpu = cpu_baseline(torch, wl, rows, x, W_r, b, args.cpu_baseline_seconds, args.seed)
-        log(f"[bench] oracle: {cpu['value']} tokens/s on {cpu['cores']} threads")
-    rows = None
+    main_wl = wl
     also = {}
     others = [s for s in args.also.split(",") if s]
     for name in others:
@@ -493,6 +487,15 @@ def main():
         also.update(measure_bias_steps(moe, torch, args.seed))
         log(f"[bench] bias: {also['bias_update_e384']['us_per_call']} us (sign), "
             f"{also['bias_quantile_k3_t4096']['ms_per_call']} ms (quantile)")
+    # The oracle runs last: its host copies of the experts (tens of GB) and
+    # threads must not share the host with any GPU timing.
+    cpu = None
+    if args.cpu_baseline_seconds > 0:
+        log("[bench] CPU baseline (oracle)")
+        x, W_r, b = main_r["inputs"]
+        cpu = cpu_baseline(torch, main_wl, rows, x, W_r, b, args.cpu_baseline_seconds, args.seed)
+        log(f"[bench] oracle: {cpu['value']} tokens/s on {cpu['cores']} threads")
+    rows = None
     mw = get_workload(args.workload)
     line = {
         "metric": METRIC, "value": round(main_r["value"], 1), "unit": "tokens/s", "n_gpus": 1,
