@@ -22,6 +22,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace moe {
 
 int tile_bm(TileCfg cfg);
@@ -287,6 +289,17 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// The same wait as a hard scheduling fence: no instruction moves across it.
+// Needed wherever it guards registers written by untracked loads, which the
+// compiler would otherwise read (an MFMA) or reuse (after their last use)
+// on its side of the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_fenced() {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<N>();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // 16 FP8 E4M3FN codes (two 8-code K chunks) -> two bf16 fragments of 8,
 // each code times `scale` (a power of two: the product is exact).
 __device__ __forceinline__ void fp8x16_to_bf16(uint4 q, float scale, uint4& lo, uint4& hi) {
@@ -294,6 +307,17 @@ __device__ __forceinline__ void fp8x16_to_bf16(uint4 q, float scale, uint4& lo, 
     lo = make_uint4(MOE_CVT(q.x, false), MOE_CVT(q.x, true), MOE_CVT(q.y, false), MOE_CVT(q.y, true));
     hi = make_uint4(MOE_CVT(q.z, false), MOE_CVT(q.z, true), MOE_CVT(q.w, false), MOE_CVT(q.w, true));
 #undef MOE_CVT
+}
+
+// 16 bytes per lane from base + voff (base wave-uniform), issued as inline
+// assembly: the compiler does not count it, so the caller waits for it with
+// an explicit vmcnt that also counts the A DMA loads in flight.  (Counted by
+// the compiler, its waits would leave out those DMA loads and hold each MFMA
+// until loads issued after its operand had landed too.)
+__device__ __forceinline__ uint4 gload16_untracked(const char* base, uint32_t voff) {
+    uint4 v;
+    asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(v) : "v"(voff), "s"(base));
+    return v;
 }
 
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
@@ -822,7 +846,8 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
         const char* m = s1 ? (up ? sU1 : sB1) : (up ? sU0 : sB0);
         const uint32_t kblk = F8 ? static_cast<uint32_t>(kt) : static_cast<uint32_t>((kt - (s1 ? nk0 : 0)) * 2 + sl);
         const uint32_t blk = static_cast<uint32_t>(rb[j]) * (s1 ? kb1 : kb0) + kblk;
-        return *reinterpret_cast<const uint4*>(m + blk * 1024u + lane * 16);
+        if constexpr (F8) return *reinterpret_cast<const uint4*>(m + blk * 1024u + lane * 16);
+        return gload16_untracked(m + blk * 1024u, lane * 16);
     };
     // FP8 block scales: lane l holds the exponent of K block l of this
     // wave's 128-row block (gate and up), placed as the bits of the float
@@ -864,7 +889,11 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
     // first slab; the barrier sits between the slabs, after which the slot
     // of this stage (read by every wave) takes A(it + NST) and the next
     // stage's first A fragments are read while the second slab computes.
-    auto step = [&](int it, auto wait_next) {
+    // bf16: the weight loads are issued untracked (like the A DMA), so the
+    // waits for them are explicit and exact.  A fragment's load is LOADS - 1
+    // loads older than the point of its first use, save the first stage's
+    // first slab, whose loads come from the prologue (2 NB - 1).
+    auto step = [&](int it, auto wait_next, auto first) {
         const int kb = min(it + 1, nkt - 1);
         uint4 fa1[MB];
         uint4 f1[F8 ? NB : 1];  // FP8: the second slab's converted fragments
@@ -883,6 +912,7 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
 #pragma unroll
                 for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(f0, fa0[i], acc[i][j]);
             } else {
+                wait_vmcnt_fenced<decltype(first)::value ? 2 * NB - 1 : LOADS - 1>();
 #pragma unroll
                 for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fb[0][j], fa0[i], acc[i][j]);
                 fb[0][j] = load_b(kb, 0, j);
@@ -901,6 +931,7 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
 #pragma unroll
                 for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(f1[j], fa1[i], acc[i][j]);
             } else {
+                wait_vmcnt_fenced<LOADS - 1>();
 #pragma unroll
                 for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fb[1][j], fa1[i], acc[i][j]);
                 fb[1][j] = load_b(kb, 1, j);
@@ -918,16 +949,25 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
     wait_vmcnt<(NST - 1) * NAB + NBL>();  // A(0): younger are A(1..NST-1) and B(0)
     __syncthreads();
     read_a(fa0, 0, fo0);
-    for (int it = 0; it < nkt; ++it)
+    step(0, [] { wait_vmcnt<kWait0>(); }, std::true_type{});
+    for (int it = 1; it < nkt; ++it)
         step(it, [it] {
             if (it >= NST - 2)
                 wait_vmcnt<kWaitA>();
-            else if (it == 0)
-                wait_vmcnt<kWait0>();
             else
                 wait_vmcnt<kWait1>();
-        });
-    wait_vmcnt<0>();  // every DMA has landed before the workgroup ends
+        }, std::false_type{});
+    wait_vmcnt_fenced<0>();  // every load has landed before its registers are reused
+    if constexpr (!F8) {
+        // The last stage's weight loads (re-reading that stage) are never
+        // used; this empty use keeps their registers allocated up to the
+        // wait, so nothing else is placed in them while they are in flight.
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                asm volatile("" ::"v"(fb[sl][j].x), "v"(fb[sl][j].y), "v"(fb[sl][j].z), "v"(fb[sl][j].w));
+    }
     store_direct<TC, EPI, MB, NB, TN>(acc, G, static_cast<TC*>(G.C), row0, rows, n0, wid);
 }
 
