@@ -695,10 +695,14 @@ __device__ __forceinline__ void store_direct(const f32x4 (&acc)[MB][NB], const G
     const int N = G.N, q = lane >> 4;
     constexpr int NJ = EPI == EPI_SWIGLU ? NB / 2 : NB;  // output blocks per row
     const int cb = n0 + wid * (EPI == EPI_SWIGLU ? TN / 2 : TN);
+    // silu(g) * u with the hardware exp2 and reciprocal (about 1 ulp each,
+    // against the 8 significant bits the bf16 result keeps): an IEEE
+    // division and the library exp cost some 20 VALU instructions per
+    // output, and this epilogue writes 32768 of them per workgroup.
     auto val = [&](int i, int j, int e) {
         if (EPI == EPI_SWIGLU) {
             const float g = acc[i][j][e], u = acc[i][j + NB / 2][e];
-            return g / (1.0f + expf(-g)) * u;
+            return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
         }
         return acc[i][j][e];
     };
