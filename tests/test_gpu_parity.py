@@ -303,6 +303,31 @@ def test_forward_tile_row_buckets(w_dtype):
     assert r["counts"].cpu().tolist() == sizes
 
 
+def test_forward_many_tiles_per_expert():
+    # Experts averaging more than 128 rows: one to four 128-row tiles per
+    # expert, last tiles on both sides of every 32-row body edge, and N
+    # tails in both projections (F = 192: the up projection's 256-column
+    # tile is three-quarters full; d = 320: the down projection's
+    # 512-column tile holds 320).
+    sizes = [1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 159, 160, 161, 191, 192, 193, 300, 384,
+             385, 500]
+    E, T, d = len(sizes), sum(sizes), 320
+    assert T >= 128 * E
+    wl = _custom(E=E, K=1, T=T, d=d, F=192, n_shared=1, F_shared=128)
+    inp = make_layer_inputs(wl, "cpu", seed=9)
+    g = torch.Generator().manual_seed(9)
+    owner = torch.cat([torch.full((c,), e, dtype=torch.int64) for e, c in enumerate(sizes)])
+    owner = owner[torch.randperm(T, generator=g)]
+    x = torch.randn((T, d), generator=g) * 0.1
+    x[torch.arange(T), owner] += 4.0
+    inp["x"] = x.to(torch.bfloat16)
+    W_r = torch.randn((E, d), generator=g) * 0.01
+    W_r[torch.arange(E), torch.arange(E)] = 8.0
+    inp["W_r"], inp["b"] = W_r.contiguous(), torch.zeros(E)
+    _, r, _ = _full_parity(wl, inp, "many tiles per expert", packed=True)
+    assert r["counts"].cpu().tolist() == sizes
+
+
 def test_forward_zero_tokens():
     wl = _custom(T=0)
     log("[gpu] forward T=0")

@@ -153,7 +153,7 @@ def _kernels(isa):
         # bf16-output register-fed kernels ("It": unsigned short); the FP8
         # form's own weight loads are compiler-tracked (its shared-expert
         # tiles are not), which the walk treats as untracked: stricter
-        if name.startswith("_ZN") and "k_gemm_wideIt" in name:
+        if name.startswith("_ZN") and ("k_gemm_wideIt" in name or "k_gemm_w192It" in name):
             found[name] = f
     return found
 
