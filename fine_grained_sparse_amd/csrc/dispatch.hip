@@ -62,26 +62,48 @@ __device__ int block_exclusive_scan(int x, int* total, int* sh) {
     return res;
 }
 
-// One block of 1024 threads; thread e owns expert e.
-__global__ __launch_bounds__(1024) void k_dispatch_scan(const uint64_t* __restrict__ masks, int nch, int E, int bm,
-                                                        int shared_rows, int32_t* __restrict__ chunk_base,
+// Per-expert running bases over the chunks: one wave per expert.  Lane l
+// takes the chunks [l * cpl, (l + 1) * cpl), sums their token counts, the
+// wave scans the lane sums, and each lane writes the exclusive base of its
+// chunks in order; lane 63 holds the expert's total.
+// grid: ceil(E / 4) blocks of 4 waves; wave w owns expert 4 * block + w.
+__global__ __launch_bounds__(256) void k_dispatch_chunk_scan(const uint64_t* __restrict__ masks, int nch, int E,
+                                                             int32_t* __restrict__ chunk_base,
+                                                             int32_t* __restrict__ counts) {
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;
+    const int cpl = (nch + 63) / 64;
+    const int c0 = lane * cpl, c1 = min(nch, c0 + cpl);
+    int mine = 0;
+    for (int c = c0; c < c1; ++c) mine += __popcll(masks[static_cast<int64_t>(c) * E + e]);
+    int incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    int base = incl - mine;
+    for (int c = c0; c < c1; ++c) {
+        chunk_base[static_cast<int64_t>(c) * E + e] = base;
+        base += __popcll(masks[static_cast<int64_t>(c) * E + e]);
+    }
+    if (lane == 63) counts[e] = incl;
+}
+
+// One block of 1024 threads; thread e owns expert e (its count from
+// k_dispatch_chunk_scan).
+__global__ __launch_bounds__(1024) void k_dispatch_scan(int E, int bm, int shared_rows,
                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                         TileInfo* __restrict__ tiles, int32_t* __restrict__ ntiles) {
     __shared__ int sh[17];
     const int e = threadIdx.x;
-    int cnt = 0;
-    if (e < E) {
-        for (int c = 0; c < nch; ++c) {
-            chunk_base[static_cast<int64_t>(c) * E + e] = cnt;
-            cnt += __popcll(masks[static_cast<int64_t>(c) * E + e]);
-        }
-    }
+    const int cnt = e < E ? counts[e] : 0;
     int total = 0, ttotal = 0;
     const int off = block_exclusive_scan(cnt, &total, sh);
     const int nt = (cnt + bm - 1) / bm;
     const int toff = block_exclusive_scan(nt, &ttotal, sh);
     if (e < E) {
-        counts[e] = cnt;
         offsets[e] = off;
         for (int j = 0; j < nt; ++j) {
             TileInfo ti;
@@ -113,6 +135,10 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(const uint64_t* __restri
         ntiles[0] = ttotal + nsh;
         ntiles[1] = ttotal;
     }
+}
+
+__global__ __launch_bounds__(1024) void k_fill_counts_zero(int32_t* __restrict__ counts, int E) {
+    if (static_cast<int>(threadIdx.x) < E) counts[threadIdx.x] = 0;
 }
 
 __global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t* __restrict__ idx, int T, int E, int K, int nch,
@@ -173,9 +199,17 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int E, int K, int bm, int 
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024), 0, stream, masks, nch, E, bm, shared_rows, chunk_base,
-                       counts, offsets, tiles, ntiles);
+    if (nch > 0) {
+        hipLaunchKernelGGL(k_dispatch_chunk_scan, dim3((E + 3) / 4), dim3(256), 0, stream, masks, nch, E, chunk_base,
+                           counts);
+    } else {
+        hipLaunchKernelGGL(k_fill_counts_zero, dim3(1), dim3(1024), 0, stream, counts, E);
+    }
     hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024), 0, stream, E, bm, shared_rows, counts, offsets, tiles,
+                       ntiles);
+    err = hipGetLastError();
     if (err != hipSuccess || nch == 0) return err;
     hipLaunchKernelGGL(k_dispatch_scatter, g4, dim3(256), 0, stream, idx, T, E, K, nch, masks, chunk_base, offsets,
                        sorted_token, pos);
