@@ -420,7 +420,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer is measured on one GPU's share, see DESIGN.md)", file=sys.stderr)
+              "(the layer is measured on one GPU's share; the collectives that would shard it are not built)", file=sys.stderr)
         sys.exit(2)
 
     import torch
