@@ -113,7 +113,7 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
     // Router: small row tiles for small batches; split K until about a
     // thousand workgroups are in flight, keeping at least 8 K steps each.
     // (fp32 activations only serve small parity workloads: small tiles)
-    p.rcfg = (p.T <= 1024 || p.dt == DT_F32) ? TILE_SMALL : TILE_LARGE;
+    p.rcfg = (p.T <= 1024 || p.dt == DT_F32) ? TILE_SMALL : TILE_ROUTER;
     const int64_t rbm = tile_bm(p.rcfg), rbn = tile_bn_out(p.rcfg, EPI_STORE);
     p.rtiles = static_cast<int>(cdiv(p.T, rbm));
     const int64_t wgs = std::max<int64_t>(1, p.rtiles * cdiv(p.E, rbn));

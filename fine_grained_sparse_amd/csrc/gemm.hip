@@ -1021,6 +1021,9 @@ constexpr int kF32BN = 256;
 constexpr int kSmBM = 16, kSmBN = 512, kSmWM = 1, kSmWN = 4, kSmNST = 2, kSmROWB = 128;
 // prefill tile: BM x BN (B rows), waves WM x WN, NST LDS stages
 constexpr int kBigBM = 128, kBigBN = 256, kBigWM = 2, kBigWN = 2, kBigNST = 3, kBigROWB = 64;
+// router logits tile: the prefill tile with 192 B rows (E = 384 is two whole
+// N tiles, where 256 left half of the second one idle)
+constexpr int kRtBN = 192;
 // prefill expert tile with register-fed weights: 128 x 512
 constexpr int kWideBM = 128, kWideBN = 512;
 
@@ -1031,7 +1034,9 @@ static_assert(kBigBM == kWideBM, "prefill tiles share the tile table's 128-row M
 int tile_bm(TileCfg cfg) { return (cfg == TILE_SMALL || cfg == TILE_WIDE16) ? kSmBM : kBigBM; }
 int tile_bn_out(TileCfg cfg, Epi epi) {  // bf16 kernels (sizing heuristics only)
     // B rows per N tile (gate + up rows for SwiGLU)
-    const int bn = cfg == TILE_SMALL ? kSmBN : ((cfg == TILE_WIDE || cfg == TILE_WIDE16) ? kWideBN : kBigBN);
+    const int bn = cfg == TILE_SMALL ? kSmBN
+                   : (cfg == TILE_WIDE || cfg == TILE_WIDE16) ? kWideBN
+                   : cfg == TILE_ROUTER ? kRtBN : kBigBN;
     return epi == EPI_SWIGLU ? bn / 2 : bn;
 }
 
@@ -1073,11 +1078,15 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
     if constexpr (sizeof(T) == 4) {
         if (packed || cfg != TILE_SMALL) return hipErrorInvalidValue;  // fp32 runs the small tiles only
     }
+    if (cfg == TILE_ROUTER && (packed || EPI != EPI_STORE)) return hipErrorInvalidValue;
     if (cfg == TILE_WIDE && !(packed && wide_fits(args))) cfg = TILE_LARGE;
     if (cfg == TILE_WIDE16) cfg = TILE_SMALL;  // bf16 decode: the LDS tile streams slightly faster
     const bool wide = cfg == TILE_WIDE;
     // output columns per N tile of the kernel actually launched
-    const int bn = sizeof(T) == 4 ? kF32BN : (cfg == TILE_SMALL ? kSmBN : (wide ? kWideBN : kBigBN));
+    const int bn = sizeof(T) == 4 ? kF32BN
+                   : cfg == TILE_SMALL ? kSmBN
+                   : wide ? kWideBN
+                   : cfg == TILE_ROUTER ? kRtBN : kBigBN;
     const int bno = EPI == EPI_SWIGLU ? bn / 2 : bn;
     GemmArgs a = args;
     a.ntn = (max_n + bno - 1) / bno;
@@ -1097,6 +1106,10 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
             else
                 hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, kSmNST, kSmROWB, EPI, false>), grid,
                                    dim3(64 * kSmWM * kSmWN), 0, stream, a);
+        } else if (cfg == TILE_ROUTER) {
+            if constexpr (EPI == EPI_STORE)
+                hipLaunchKernelGGL((k_gemm_big<TC, kBigBM, kRtBN, kBigWM, kBigWN, kBigNST, kBigROWB, EPI, false>), grid,
+                                   dim3(64 * kBigWM * kBigWN), 0, stream, a);
         } else {
             if (packed)
                 hipLaunchKernelGGL((k_gemm_big<TC, kBigBM, kBigBN, kBigWM, kBigWN, kBigNST, kBigROWB, EPI, true>), grid,
