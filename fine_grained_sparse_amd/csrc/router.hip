@@ -106,6 +106,8 @@ __device__ __forceinline__ void limit_to_groups(float (&v)[J], int lane, int E, 
     }
 }
 
+constexpr int kMaxSplit = 16;  // split-K partial planes the gate sums (the router plan caps at 16)
+
 template <int J>
 __global__ __launch_bounds__(256) void k_topk_gate(const float* __restrict__ z, int nsplit, int64_t split_stride,
                                                    int ldz, const float* __restrict__ b, int T, int E, int K,
@@ -120,8 +122,17 @@ __global__ __launch_bounds__(256) void k_topk_gate(const float* __restrict__ z, 
     for (int j = 0; j < J; ++j) {
         const int e = j * 64 + lane;
         if (e < E) {
+            // every split-K partial is loaded before the first add (a loop of
+            // dependent load-adds waited out one memory latency per plane);
+            // the adds keep plane order
+            float part[kMaxSplit];
+#pragma unroll
+            for (int p = 0; p < kMaxSplit; ++p)
+                part[p] = p < nsplit ? z[p * split_stride + static_cast<int64_t>(t) * ldz + e] : 0.f;
             float zz = 0.f;
-            for (int p = 0; p < nsplit; ++p) zz += z[p * split_stride + static_cast<int64_t>(t) * ldz + e];
+#pragma unroll
+            for (int p = 0; p < kMaxSplit; ++p)
+                if (p < nsplit) zz += part[p];
             s[j] = 1.0f / (1.0f + expf(-zz));  // step 2: per-expert sigmoid
             v[j] = s[j] + b[e];                // step 3: the bias only chooses
             // A NaN score would never win a comparison and leave the arg-max
@@ -314,7 +325,7 @@ hipError_t launch_topk_gate(const float* z, int nsplit, int64_t split_stride, in
                             hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     if (n_group < 1 || n_group > 64 || E % n_group || topk_group < 1 || topk_group > n_group ||
-        (n_group > 1 && E / n_group < 2))
+        (n_group > 1 && E / n_group < 2) || nsplit < 1 || nsplit > kMaxSplit)
         return hipErrorInvalidValue;
     const dim3 grid((T + 3) / 4), block(256);
     const int J = (E + 63) / 64;
@@ -327,8 +338,12 @@ hipError_t launch_topk_gate(const float* z, int nsplit, int64_t split_stride, in
         MOE_TOPK(2);
     else if (J <= 4)
         MOE_TOPK(4);
+    else if (J <= 6)
+        MOE_TOPK(6);
     else if (J <= 8)
         MOE_TOPK(8);
+    else if (J <= 14)
+        MOE_TOPK(14);
     else
         MOE_TOPK(16);
 #undef MOE_TOPK
