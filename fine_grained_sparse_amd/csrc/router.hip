@@ -39,9 +39,16 @@ __global__ __launch_bounds__(256) void k_fill_i32(int32_t* p, int32_t v, int64_t
 }
 
 // (value, index) order of the selection: larger biased score first, the
-// lower expert index on equal scores.
-__device__ __forceinline__ bool better(float v, int e, float bv, int be) {
-    return v > bv || (v == bv && e < be);
+// lower expert index on equal scores, as one unsigned 64-bit key.  The top
+// half is the score's bits made monotone (negative floats flipped, positive
+// ones offset by the sign bit; -0 is first made +0, since the two compare
+// equal), the bottom half the complement of the index, so that of two equal
+// scores the lower index has the larger key.  Every valid pair's key is
+// above 0 (-inf maps to 0x007fffff in the top half).
+__device__ __forceinline__ uint64_t sel_key(float v, int e) {
+    uint32_t u = __float_as_uint(v + 0.0f);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(e));
 }
 
 // One wave per token.  Lane l holds experts l, l+64, l+128, ... (J of
@@ -145,32 +152,35 @@ __global__ __launch_bounds__(256) void k_topk_gate(const float* __restrict__ z, 
         }
     }
     if (n_group > 1) limit_to_groups<J>(v, lane, E, n_group, E / n_group, topk_group);
+    uint64_t key[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) key[j] = j * 64 + lane < E ? sel_key(v[j], j * 64 + lane) : 0ull;
     uint32_t taken = 0;
     int my_e = 0;
     float my_s = 0.f, den = 0.f;
     for (int k = 0; k < K; ++k) {
-        float bv = -INFINITY, bs = 0.f;
-        int be = 0x7fffffff;
+        // this lane's best untaken expert, then the wave-wide largest key;
+        // the winning lane's own best is the winner, so its score comes
+        // from that lane with one shuffle
+        uint64_t bk = 0;
+        float bs = 0.f;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int e = j * 64 + lane;
-            if (!((taken >> j) & 1u) && e < E && better(v[j], e, bv, be)) {
-                bv = v[j];
-                be = e;
+            if (!((taken >> j) & 1u) && key[j] > bk) {
+                bk = key[j];
                 bs = s[j];
             }
         }
+        uint64_t wk = bk;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oe = __shfl_xor(be, off);
-            const float os = __shfl_xor(bs, off);
-            if (better(ov, oe, bv, be)) {
-                bv = ov;
-                be = oe;
-                bs = os;
-            }
+            const uint32_t ohi = __shfl_xor(static_cast<uint32_t>(wk >> 32), off);
+            const uint32_t olo = __shfl_xor(static_cast<uint32_t>(wk), off);
+            const uint64_t ok = (static_cast<uint64_t>(ohi) << 32) | olo;
+            wk = ok > wk ? ok : wk;
         }
+        const int be = static_cast<int>(~static_cast<uint32_t>(wk));
+        bs = __shfl(bs, be & 63);
         if ((be & 63) == lane) taken |= 1u << (be >> 6);
         if (lane == k) {
             my_e = be;
