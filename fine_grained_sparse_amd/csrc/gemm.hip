@@ -14,7 +14,8 @@
 //                16 x 256 tiles, four v_mfma_f32_16x16x4_f32 per fragment.
 //   k_gemm_big   bf16, both operands DMA'd into an LDS ring
 //                (global_load_lds_dwordx4): 16 x 512 decode tiles, 128 x 256
-//                prefill tiles on row-major weights, the router logits.
+//                prefill tiles on row-major weights, 128 x 192 router-logit
+//                tiles.
 //   k_gemm_wide  bf16 prefill tiles on packed weights: 128 x 512, A through
 //                LDS, each wave's weight fragments straight into registers.
 // One 64-byte K slab feeds one v_mfma_f32_16x16x32_bf16 per 16x16 block; a

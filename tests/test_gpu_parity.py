@@ -282,12 +282,14 @@ def test_forward_fp8_edge_cases(case):
 
 @pytest.mark.parametrize("w_dtype", ["bf16", "fp8"])
 def test_forward_tile_row_buckets(w_dtype):
-    # Experts with 1, 31, 32, 33, ... 129, 200 rows: the ragged last 128-row
+    # Experts with 1, 15, 16, 17, ... 129, 200 rows: the ragged last 128-row
     # tile of each expert runs the 32-, 64-, 96- or 128-row body; every
-    # bucket edge appears.  Token t is steered to expert f(t) by a one-hot
-    # feature that only W_r[f(t)] weights heavily (K = 1, wide margins).
-    sizes = [1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 200]
+    # bucket edge appears, and every 16-row MFMA block edge inside a body.
+    # Token t is steered to expert f(t) by a one-hot feature that only
+    # W_r[f(t)] weights heavily (K = 1, wide margins).
+    sizes = [1] + [16 * m + o for m in range(1, 9) for o in (-1, 0, 1)] + [200]
     E, T, d = len(sizes), sum(sizes), 256
+    assert T >= 64 * E  # the 128-row register-fed tiles serve this layer
     wl = _custom(E=E, K=1, T=T, d=d, F=128, w_dtype=w_dtype)
     inp = make_layer_inputs(wl, "cpu", seed=8)
     g = torch.Generator().manual_seed(8)
