@@ -110,11 +110,13 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
     p.dt = D->act_dtype == MOE_BF16 ? DT_BF16 : DT_F32;
     p.es = p.dt == DT_BF16 ? 2 : 4;
 
-    // Router: small row tiles for small batches; split K until about 512
-    // workgroups (two per CU) are in flight, keeping at least 8 K steps each.
-    // Each split writes, and the gate reads back, a partial plane of logits.
-    // (fp32 activations only serve small parity workloads: small tiles)
-    p.rcfg = (p.T <= 1024 || p.dt == DT_F32) ? TILE_SMALL : TILE_ROUTER;
+    // Router: 16-row tiles for tiny batches, else 128 x 192 (each M tile
+    // streams the W_r planes once, so fewer, taller tiles read less); split
+    // K until about 512 workgroups (two per CU) are in flight, keeping at
+    // least 8 K steps each.  Each split writes, and the gate reads back, a
+    // partial plane of logits.  (fp32 activations only serve small parity
+    // workloads: small tiles)
+    p.rcfg = (p.T <= 64 || p.dt == DT_F32) ? TILE_SMALL : TILE_ROUTER;
     const int64_t rbm = tile_bm(p.rcfg), rbn = tile_bn_out(p.rcfg, EPI_STORE);
     p.rtiles = static_cast<int>(cdiv(p.T, rbm));
     const int64_t wgs = std::max<int64_t>(1, p.rtiles * cdiv(p.E, rbn));
