@@ -62,7 +62,10 @@ def _full_parity(wl, inp, seed_note="", packed=False):
 
 
 # ---------------------------------------------------------------- router
+# T = 64 and 65 sit on either side of the switch from 16-row to 128-row
+# logit tiles; 1024 and 4096 split K into different numbers of planes.
 @pytest.mark.parametrize("name,T", [("tiny_fp32_t128", None), ("mid_bf16_t300", None),
+                                    ("k2_router_t4096", 64), ("k2_router_t4096", 65),
                                     ("k2_router_t4096", None), ("k3_latent_t4096", 1024)])
 def test_router_parity(name, T):
     wl = get_workload(name)
