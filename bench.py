@@ -12,7 +12,7 @@ tokens, and the K3-shaped latent layer.
 Per-stage durations come from hipEvents the library records at its stage
 boundaries on the launch stream (include/moe.h, MOE_EV_*); the up-projection
 stage is a single kernel (the grouped SwiGLU GEMM), the one the "roofline"
-object describes.  Its "traffic" is read from profiles/traffic.md when that
+object describes.  Its "traffic" is read from profiles/up_gemm_hbm_traffic.md when that
 table holds a row for the workload taken with the current kernel sources
 (otherwise null); `--summarize-counters` writes such rows from two
 rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) of this script.
@@ -36,7 +36,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-TRAFFIC_MD = os.path.join(ROOT, "profiles", "traffic.md")
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "up_gemm_hbm_traffic.md")
 CAL_REPS = 3                # streaming copies of --calibrate-copy-gib each
 WEIGHTS_NOTE = {"frag16": "bf16, fragment-block layout (moe_pack_weights once at load, untimed)",
                 "rows": "bf16, row-major"}
@@ -74,7 +74,7 @@ def source_hash() -> str:
 
 def load_traffic(workload: str, layout: str):
     """GB per dispatch of the up-projection for this workload, weight layout
-    and kernel source (a row of profiles/traffic.md), else None."""
+    and kernel source (a row of profiles/up_gemm_hbm_traffic.md), else None."""
     if not os.path.exists(TRAFFIC_MD):
         return None
     want = source_hash()
@@ -356,7 +356,7 @@ def cpu_baseline(torch, wl, weights, x, W_r, b, target_s, seed):
 
 
 def summarize_counters(fetch_dir, write_dir, workload, layout, copy_gib):
-    """One markdown row of profiles/traffic.md from two rocprofv3 --pmc passes
+    """One markdown row of profiles/up_gemm_hbm_traffic.md from two rocprofv3 --pmc passes
     of this script (FETCH_SIZE, then WRITE_SIZE), each run with
     --calibrate-copy-gib so that it also holds CAL_REPS streaming copies
     (torch.neg, fp32) of known size.  Kernel names must not be truncated
@@ -412,7 +412,7 @@ def main():
                     help="also run a plain streaming copy (out = -in, fp32) of this many GiB "
                          "three times, to scale HBM byte counters (0 = off)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="print the profiles/traffic.md row of --workload from two rocprofv3 "
+                    help="print the profiles/up_gemm_hbm_traffic.md row of --workload from two rocprofv3 "
                          "--pmc output directories and exit (no GPU use)")
     args = ap.parse_args()
     if args.summarize_counters:
