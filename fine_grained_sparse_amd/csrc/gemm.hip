@@ -356,17 +356,8 @@ template <int BM, int BNO>
 __device__ __forceinline__ bool pick_job(const GemmArgs& a, Job& jb) {
     const int total = (a.tiles ? a.ntiles[0] : (a.M + BM - 1) / BM) * a.ntn;  // active (M, N) tile pairs
     const int total_r = a.tiles ? a.ntiles[1] * a.ntn : total;                // ... of them routed
-    const int per = (total_r + 7) >> 3, per_s = (total - total_r + 7) >> 3;
-    const int slot = static_cast<int>(blockIdx.x) >> 3, xcd = static_cast<int>(blockIdx.x) & 7;
-    int lin;
-    if (slot < per) {
-        lin = xcd * per + slot;
-        if (lin >= total_r) return false;
-    } else {
-        const int k = slot - per;
-        lin = total_r + xcd * per_s + k;
-        if (k >= per_s || lin >= total) return false;
-    }
+    const int lin = xcd_slot_pair(static_cast<int>(blockIdx.x), total_r, total);
+    if (lin < 0) return false;
     int first, cnt;
     if (a.tiles) {
         const TileInfo t0 = a.tiles[lin / a.ntn];
@@ -1042,17 +1033,6 @@ int tile_bn_out(TileCfg cfg, Epi epi) {  // bf16 kernels (sizing heuristics only
 }
 
 namespace {
-
-// Grid of a pick_job launch.  The XCD-aware remap sends block b to a
-// logical slot in the stretch of XCD b % 8; the routed and shared stretches
-// (ceil(routed / 8) + ceil(shared / 8) blocks per XCD) cover every active
-// slot only when the grid holds 8 times that, at most the active pairs plus
-// 14: round the grid up to a multiple of 8 and add 16 (blocks past the
-// active slots return at once).
-unsigned job_blocks(int max_tiles, int ntn) {
-    const unsigned blocks = static_cast<unsigned>(max_tiles) * static_cast<unsigned>(ntn);
-    return ((blocks + 7u) & ~7u) + 16u;
-}
 
 // What the wide kernel handles: packed weights, one or two K segments per
 // group (multiples of 64), no split K, fragment-block byte offsets in 31 bits.

@@ -62,6 +62,34 @@ struct TileInfo {
     int32_t first, count, pad0_, pad1_;
 };
 
+// XCD-aware slot map of a tile-table launch.  Blocks go to the eight XCDs
+// round robin (block b runs on XCD b % 8).  The active (M tile, N tile)
+// pairs are numbered 0 .. total-1, the first total_r of them routed, the
+// rest shared-expert pairs; each XCD walks one contiguous stretch of the
+// routed pairs, ceil(total_r / 8) long, and then one stretch of the shared
+// pairs, ceil((total - total_r) / 8) long.  Returns block b's pair, or -1
+// for a block without work.  Every pair has exactly one block as long as
+// the grid holds job_blocks(tiles, ntn) blocks for tiles * ntn >= total.
+__host__ __device__ inline int xcd_slot_pair(int b, int total_r, int total) {
+    const int per = (total_r + 7) >> 3, per_s = (total - total_r + 7) >> 3;
+    const int slot = b >> 3, xcd = b & 7;
+    if (slot < per) {
+        const int lin = xcd * per + slot;
+        return lin < total_r ? lin : -1;
+    }
+    const int k = slot - per, lin = total_r + xcd * per_s + k;
+    return (k < per_s && lin < total) ? lin : -1;
+}
+
+// Grid of a tile-table launch for up to max_tiles M tiles of ntn N tiles:
+// the routed and shared stretches take 8 * (ceil(routed / 8) + ceil(shared
+// / 8)) blocks, at most the pairs plus 14, so round the pairs up to a
+// multiple of 8 and add 16 (blocks past the active pairs return at once).
+inline unsigned job_blocks(int max_tiles, int ntn) {
+    const unsigned blocks = static_cast<unsigned>(max_tiles) * static_cast<unsigned>(ntn);
+    return ((blocks + 7u) & ~7u) + 16u;
+}
+
 struct GemmArgs {
     GemmGroup g[2];
     const TileInfo* tiles;   // device tile table (grouped) or NULL (dense)
