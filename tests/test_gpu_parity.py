@@ -360,6 +360,37 @@ def test_forward_deterministic_and_independent_of_workspace_contents():
         assert torch.equal(r1[k], r2[k]), k
 
 
+def test_forward_on_a_side_stream_and_replayed_from_a_graph():
+    # The layer only enqueues kernels on the stream it is given: the same
+    # call on a second stream, and a HIP graph captured from it and replayed
+    # with eager work in between, give the default stream's bits.
+    wl = get_workload("mid_bf16_t300")
+    log("[gpu] side stream and graph replay mid_bf16_t300")
+    dev = weights_to_device(make_layer_inputs(wl, "cpu", seed=42), DEV)
+    w = _weights(wl, dev, packed=True)
+    ref, _ = _run_forward(wl, dev, weights=w)
+    ws = moe.Workspace()
+    out = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):  # the second call also runs on a warm workspace
+            moe.forward(dev["x"], dev["W_r"], dev["b"], w, wl.K, wl.scale, n_shared=wl.n_shared,
+                        out=out, workspace=ws, stream=side)
+    side.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        moe.forward(dev["x"], dev["W_r"], dev["b"], w, wl.K, wl.scale, n_shared=wl.n_shared,
+                    out=out, workspace=ws, stream=side)
+    for rep in range(3):
+        out.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+
+
 # ---------------------------------------------------------------- full sizes, sampled tokens
 def _sampled_tokens(T, ref, counts, idx_eff, n_random=6):
     rng = np.random.default_rng(0)
