@@ -124,20 +124,42 @@ def _need(t, name, dtype=None, shape=None, device=None):
 
 
 class Workspace:
-    """A growable device byte buffer (allocated by torch, owned here)."""
+    """Growable device byte buffers (allocated by torch, owned here), one per
+    (device, stream).  A buffer is allocated while its stream is current, so
+    torch's caching allocator orders any reuse of its memory after the work
+    already queued on that stream; calls on different streams never share
+    scratch, and a buffer that grows is released only in that stream's
+    order."""
 
     def __init__(self):
         self._buf = {}
 
-    def get(self, device, nbytes):
-        buf = self._buf.get(device)
+    def get(self, device, nbytes, stream=None):
+        s = torch.cuda.current_stream(device) if stream is None else stream
+        key = (device, s.cuda_stream)
+        buf = self._buf.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-            self._buf[device] = buf
+            self._buf.pop(key, None)
+            with torch.cuda.stream(s):
+                buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self._buf[key] = buf
         return buf
 
 
 _default_ws = Workspace()
+
+
+def _on(stream):
+    """Context in which outputs are allocated: the launch stream."""
+    return torch.cuda.stream(stream) if stream is not None else _Nothing()
+
+
+class _Nothing:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *a):
+        return False
 
 
 def router(x, W_r, b, K, scale=2.827, *, counts=True, workspace=None, stream=None,
@@ -159,10 +181,11 @@ def router(x, W_r, b, K, scale=2.827, *, counts=True, workspace=None, stream=Non
     nbytes = workspace_size(D, False)
     if nbytes == 0:
         raise MoeError("moe_workspace_size", 2)
-    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
-    w = torch.empty((T, K), dtype=torch.float32, device=dev)
-    cnt = torch.empty((E,), dtype=torch.int32, device=dev) if counts else None
-    ws = (workspace or _default_ws).get(dev, nbytes)
+    with _on(stream):
+        idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+        w = torch.empty((T, K), dtype=torch.float32, device=dev)
+        cnt = torch.empty((E,), dtype=torch.int32, device=dev) if counts else None
+    ws = (workspace or _default_ws).get(dev, nbytes, stream)
     rc = lib().moe_router(ctypes.byref(D), _ptr(x), _ptr(W_r), _ptr(b), _ptr(idx), _ptr(w),
                           _ptr(cnt), _ptr(ws), nbytes, _stream(stream))
     if rc:
@@ -249,9 +272,10 @@ def bias_quantile(x, W_r, K, *, out=None, workspace=None, stream=None):
     nbytes = workspace_size(D, False)
     if nbytes == 0:
         raise MoeError("moe_workspace_size", 2)
-    b = torch.empty((E,), dtype=torch.float32, device=dev) if out is None else out
+    with _on(stream):
+        b = torch.empty((E,), dtype=torch.float32, device=dev) if out is None else out
     _need(b, "out", torch.float32, (E,), dev)
-    ws = (workspace or _default_ws).get(dev, nbytes)
+    ws = (workspace or _default_ws).get(dev, nbytes, stream)
     rc = lib().moe_bias_quantile(ctypes.byref(D), _ptr(x), _ptr(W_r), _ptr(b), _ptr(ws), nbytes,
                                  _stream(stream))
     if rc:
@@ -273,7 +297,9 @@ def pack_weights(weights, *, n_shared=None, stream=None):
     E, F, din = Wg.shape
     d = weights["W_lat_down"].shape[1] if weights.get("W_lat_down") is not None else din
     D, src = _weights_desc(weights, 1, d, E, 1, 1.0, torch.bfloat16, Wg.device, n_shared)
-    out = {k: (torch.empty_like(weights[k]) if weights.get(k) is not None else None) for k in WEIGHT_NAMES}
+    with _on(stream):
+        out = {k: (torch.empty_like(weights[k]) if weights.get(k) is not None else None)
+               for k in WEIGHT_NAMES}
     dst = ExpertWeights(*[None if out[k] is None else out[k].data_ptr() for k in WEIGHT_NAMES])
     for k in SCALE_NAMES:
         if weights.get(k) is not None:
@@ -283,6 +309,38 @@ def pack_weights(weights, *, n_shared=None, stream=None):
         raise MoeError("moe_pack_weights", rc)
     out["layout"] = MOE_LAYOUT_FRAG16
     return out
+
+
+def _forward_call(x, W_r, b, weights, K, scale, n_shared, out, return_routing, stream,
+                  n_group, topk_group):
+    """Validate and marshal the arguments of moe_forward;
+    outputs are allocated on the launch stream.  Returns (desc, weights
+    struct, out, routing dict or None, pointer tuple of the outputs)."""
+    _need(x, "x")
+    if x.dim() != 2 or x.dtype not in _DT:
+        raise ValueError("x must be [T, d] fp32 or bf16")
+    T, d = x.shape
+    dev, dt = x.device, x.dtype
+    E = W_r.shape[0]
+    _need(W_r, "W_r", torch.float32, (E, d), dev)
+    _need(b, "b", torch.float32, (E,), dev)
+    D, W = _weights_desc(weights, T, d, E, K, scale, dt, dev, n_shared, n_group, topk_group)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((T, d), dtype=dt, device=dev)
+        routing = None
+        if return_routing:
+            routing = dict(idx=torch.empty((T, K), dtype=torch.int32, device=dev),
+                           w=torch.empty((T, K), dtype=torch.float32, device=dev),
+                           counts=torch.empty((E,), dtype=torch.int32, device=dev),
+                           offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+                           sorted_token=torch.empty((max(T * K, 1),), dtype=torch.int32,
+                                                    device=dev))
+    _need(out, "out", dt, (T, d), dev)
+    r = routing or {}
+    outs = (_ptr(out), _ptr(r.get("idx")), _ptr(r.get("w")), _ptr(r.get("counts")),
+            _ptr(r.get("offsets")), _ptr(r.get("sorted_token")))
+    return D, W, out, routing, outs
 
 
 def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
@@ -300,40 +358,19 @@ def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
     already-created torch.cuda.Event objects recorded at the stage
     boundaries listed in include/moe.h.  n_group > 1 limits the routing to
     the topk_group best expert groups (as router())."""
-    _need(x, "x")
-    if x.dim() != 2 or x.dtype not in _DT:
-        raise ValueError("x must be [T, d] fp32 or bf16")
-    T, d = x.shape
-    dev, dt = x.device, x.dtype
-    E = W_r.shape[0]
-    _need(W_r, "W_r", torch.float32, (E, d), dev)
-    _need(b, "b", torch.float32, (E,), dev)
-    D, W = _weights_desc(weights, T, d, E, K, scale, dt, dev, n_shared, n_group, topk_group)
+    D, W, out, routing, outs = _forward_call(x, W_r, b, weights, K, scale, n_shared, out,
+                                             return_routing, stream, n_group, topk_group)
     nbytes = workspace_size(D, True)
     if nbytes == 0:
         raise MoeError("moe_workspace_size", 2)
-    if out is None:
-        out = torch.empty((T, d), dtype=dt, device=dev)
-    else:
-        _need(out, "out", dt, (T, d), dev)
-    routing = None
-    if return_routing:
-        routing = dict(idx=torch.empty((T, K), dtype=torch.int32, device=dev),
-                       w=torch.empty((T, K), dtype=torch.float32, device=dev),
-                       counts=torch.empty((E,), dtype=torch.int32, device=dev),
-                       offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
-                       sorted_token=torch.empty((max(T * K, 1),), dtype=torch.int32, device=dev))
-    r = routing or {}
     ev = None
     if stage_events is not None:
         if len(stage_events) != NUM_STAGE_EVENTS:
             raise ValueError(f"stage_events needs {NUM_STAGE_EVENTS} events")
         ev = (ctypes.c_void_p * NUM_STAGE_EVENTS)(*[e.cuda_event or None for e in stage_events])
-    ws = (workspace or _default_ws).get(dev, nbytes)
-    rc = lib().moe_forward(ctypes.byref(D), _ptr(x), _ptr(W_r), _ptr(b), ctypes.byref(W),
-                           _ptr(out), _ptr(r.get("idx")), _ptr(r.get("w")), _ptr(r.get("counts")),
-                           _ptr(r.get("offsets")), _ptr(r.get("sorted_token")), _ptr(ws), nbytes,
-                           _stream(stream), ev)
+    ws = (workspace or _default_ws).get(x.device, nbytes, stream)
+    rc = lib().moe_forward(ctypes.byref(D), _ptr(x), _ptr(W_r), _ptr(b), ctypes.byref(W), *outs,
+                           _ptr(ws), nbytes, _stream(stream), ev)
     if rc:
         raise MoeError("moe_forward", rc)
     return (out, routing) if return_routing else out

@@ -147,3 +147,132 @@ def effective_routing_grouped(ref, gpu_idx, gpu_w, K, scale):
     assert err.max() <= WTOL, f"gate weight rel err {err.max():.3g} > {WTOL}"
     return idx_eff, w_eff, dict(near_tie=int(near.sum()), differ=int(differ.sum()),
                                 w_max_rel=float(err.max()))
+
+
+# ---------------------------------------------------------------- layer output
+# Budget of one output element (bf16 experts, fp32 accumulation).  The GPU
+# rounds the intermediates (H, the expert outputs Y and the shared output;
+# in the latent form also x_lat and the latent weighted sum R) to bf16 and
+# the output once; bf16 keeps 8 significant bits, so each rounding moves a
+# value by at most u = 2^-8 of itself.  An element then differs from the
+# exact fp64 value by
+#   * at most u |ref| from the final rounding, plus
+#   * the intermediate roundings carried through the following sums.  Each
+#     one is a sum of many independent errors, so it behaves like a normal
+#     variable of a few 1e-3 times the token's RMS output (this is the
+#     ~3e-3 relative L2 the arithmetic predicts).  Over a few million checked
+#     elements the largest such deviation is about 5.5 sigma, so ~1.5e-2 RMS
+#     (K2 form).  The latent form has twice as many roundings on the path
+#     (x_lat, R, the shared H) and a longer chain after them.
+# So |gpu - ref| <= u |ref| + beta * rms(ref of that token), with beta =
+# 2^-5 (K2 form) or 2^-4 (latent form), about twice the expected maximum.
+# A wrong 16-column block, a wrong row or a dropped expert moves elements by
+# O(rms) and fails it.  fp32 layers: no intermediate rounding; the fp32
+# accumulation error is below 1e-6 relative, so 1e-5 |ref| + 1e-4 rms.
+U_BF16 = 2.0 ** -8
+OUT_TOL = {"bf16": 2e-2, "f32": 1e-4}    # relative L2 error, per token and overall
+
+RESULTS = []     # one dict per parity case, printed by tests/conftest.py at the end
+
+
+def elem_budget(act_dtype, latent):
+    if act_dtype == "f32":
+        return 1e-5, 1e-4
+    return U_BF16, (2.0 ** -4 if latent else 2.0 ** -5)
+
+
+def check_output(case, got, ref, act_dtype, latent, routing_stats=None, extra=None):
+    """Compare the GPU layer output with the oracle's on the checked tokens
+    (rows of got / ref): every token's relative L2 error within the layer
+    tolerance, the whole set's too, and every element within its budget.
+    Records the numbers for the session summary and returns them."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    tol = OUT_TOL[act_dtype]
+    diff = got - ref
+    rn = np.linalg.norm(ref, axis=1)
+    per_tok = np.linalg.norm(diff, axis=1) / np.maximum(rn, 1e-300)
+    agg = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300))
+    rel_u, beta = elem_budget(act_dtype, latent)
+    rms = rn / np.sqrt(max(ref.shape[1], 1))
+    budget = rel_u * np.abs(ref) + beta * rms[:, None]
+    ratio = np.abs(diff) / budget
+    worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape) if ratio.size else (0, 0)
+    rec = dict(case=case, tokens=int(got.shape[0]), rel_l2=agg,
+               tok_max=float(per_tok.max()) if per_tok.size else 0.0,
+               elem_ratio=float(ratio.max()) if ratio.size else 0.0)
+    if routing_stats:
+        rec.update({k: routing_stats[k] for k in ("near_tie", "differ", "w_max_rel") if k in routing_stats})
+    if extra:
+        rec.update(extra)
+    RESULTS.append(rec)
+    log(f"  {case}: tokens={rec['tokens']} rel_l2={agg:.3e} token_max={rec['tok_max']:.3e} "
+        f"elem/budget max={rec['elem_ratio']:.3f}" +
+        (f" near_tie={rec.get('near_tie')} differ={rec.get('differ')} "
+         f"w_max_rel={rec.get('w_max_rel', 0):.2e}" if routing_stats else ""))
+    bad = np.nonzero(per_tok > tol)[0]
+    assert bad.size == 0, (f"{bad.size} tokens above relative L2 {tol}: rows {bad[:8].tolist()}, "
+                           f"max {per_tok.max():.3e}")
+    assert agg <= tol, f"relative L2 {agg:.3e} > {tol}"
+    assert rec["elem_ratio"] <= 1.0, (
+        f"element ({int(worst[0])}, {int(worst[1])}) off by {abs(diff[worst]):.3e}, budget "
+        f"{budget[worst]:.3e} (ref {ref[worst]:.4e})")
+    return rec
+
+
+def record_routing(case, stats, tokens):
+    """Routing-only cases (router, grouped router) in the session summary."""
+    RESULTS.append(dict(case=case, tokens=int(tokens), near_tie=stats["near_tie"],
+                        differ=stats["differ"], w_max_rel=stats["w_max_rel"]))
+
+
+def coverage_tokens(T, K, counts, offsets, sorted_token, idx_eff, gap, bm=128, n_random=512,
+                    seed=0, shared=True):
+    """Tokens for a sampled full-size check, chosen so that every tile of the
+    grouped GEMMs holds a checked row:
+      * one row of every bm-row chunk of every expert's segment of the
+        expert-sorted rows (the M tiles of the routed GEMMs), and the last
+        row of every expert (its ragged tail);
+      * one token of every bm-token chunk (the shared experts' M tiles);
+    plus every near-tie token, the first token of the hottest and of the
+    coldest used expert, the last token, and n_random random tokens.
+    A token covers the K expert rows it was routed to."""
+    rng = np.random.default_rng(seed)
+    counts = np.asarray(counts)
+    offsets = np.asarray(offsets)
+    st = np.asarray(sorted_token)[: T * K]
+    chosen = set(rng.choice(T, size=min(n_random, T), replace=False).tolist())
+    chosen.update(np.nonzero(np.asarray(gap) < TIE)[0].tolist())
+    chosen.add(T - 1)
+    nz = np.nonzero(counts > 0)[0]
+    for e in (nz[np.argmax(counts[nz])], nz[np.argmin(counts[nz])]):
+        chosen.add(int(st[offsets[e]]))
+    # sorted position of every (token, slot): pos[t] = rows token t occupies
+    covered_pos = np.zeros(T * K, bool)
+
+    def take(t):
+        chosen.add(int(t))
+
+    def mark_all():
+        toks = np.fromiter(chosen, np.int64)
+        mask = np.zeros(T, bool)
+        mask[toks] = True
+        covered_pos[:] = mask[st]
+        return mask
+
+    mask = mark_all()
+    for e in nz:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        targets = [(c, min(c + bm, hi)) for c in range(lo, hi, bm)] + [(hi - 1, hi)]
+        for a, b_ in targets:
+            if not covered_pos[a:b_].any():
+                t = int(st[rng.integers(a, b_)])
+                take(t)
+                mask[t] = True
+                covered_pos[mask[st]] = True
+    if shared:
+        for c in range(0, T, bm):
+            if not mask[c:c + bm].any():
+                take(int(rng.integers(c, min(c + bm, T))))
+    return np.array(sorted(chosen), np.int64)
