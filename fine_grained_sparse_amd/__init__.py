@@ -25,10 +25,12 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_LAYOUT_ROWS, MOE_LAYOUT_FRAG16 = 0, 1
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
-           4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_UNSUPPORTED", 6: "MOE_ERR_HIP"}
+           4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_UNSUPPORTED", 6: "MOE_ERR_HIP", 7: "MOE_ERR_SCRATCH"}
+MOE_ERR_SCRATCH = 7
+NOALLOC_SCRATCH_BYTES = 128 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
-EXPORTS = ("moe_workspace_size", "moe_router", "moe_forward", "moe_pack_weights", "moe_bias_update",
-           "moe_bias_quantile", "moe_status_str")
+EXPORTS = ("moe_workspace_size", "moe_router", "moe_forward", "moe_forward_noalloc", "moe_pack_weights",
+           "moe_bias_update", "moe_bias_quantile", "moe_status_str")
 WEIGHT_NAMES = ("W_gate", "W_up", "W_down", "Ws_gate", "Ws_up", "Ws_down", "W_lat_down", "W_lat_up")
 SCALE_NAMES = ("W_gate_scale", "W_up_scale", "W_down_scale")  # FP8 routed experts only
 STAGES = ("start", "router", "dispatch", "latent", "up", "down", "end")
@@ -76,6 +78,9 @@ def lib():
                                   ctypes.POINTER(ExpertWeights), vp, vp, vp, vp, vp, vp,
                                   vp, ctypes.c_size_t, vp, vp]
         L.moe_forward.restype = ctypes.c_int
+        L.moe_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, vp,
+                                          ctypes.POINTER(ExpertWeights), vp, vp, vp, vp, vp, vp, vp]
+        L.moe_forward_noalloc.restype = ctypes.c_int
         L.moe_pack_weights.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(ExpertWeights),
                                        ctypes.POINTER(ExpertWeights), vp]
         L.moe_pack_weights.restype = ctypes.c_int
@@ -313,7 +318,7 @@ def pack_weights(weights, *, n_shared=None, stream=None):
 
 def _forward_call(x, W_r, b, weights, K, scale, n_shared, out, return_routing, stream,
                   n_group, topk_group):
-    """Validate and marshal the arguments of moe_forward;
+    """Validate and marshal the arguments of moe_forward / moe_forward_noalloc;
     outputs are allocated on the launch stream.  Returns (desc, weights
     struct, out, routing dict or None, pointer tuple of the outputs)."""
     _need(x, "x")
@@ -376,6 +381,23 @@ def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
     return (out, routing) if return_routing else out
 
 
-__all__ = ["router", "forward", "pack_weights", "bias_update", "bias_quantile", "workspace_size", "desc", "lib", "MoeError",
+def forward_noalloc(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
+                    return_routing=False, stream=None, n_group=1, topk_group=1):
+    """moe_forward_noalloc: forward() with the library's fixed scratch array
+    (NOALLOC_SCRATCH_BYTES per GPU) instead of a workspace.  The library
+    allocates nothing; pass `out` (and no return_routing) for a call that
+    allocates nothing here either.  Raises MoeError with status
+    MOE_ERR_SCRATCH when the layer needs more scratch than the array holds.
+    Calls that overlap in time on one GPU share the array and race."""
+    D, W, out, routing, outs = _forward_call(x, W_r, b, weights, K, scale, n_shared, out,
+                                             return_routing, stream, n_group, topk_group)
+    rc = lib().moe_forward_noalloc(ctypes.byref(D), _ptr(x), _ptr(W_r), _ptr(b), ctypes.byref(W),
+                                   *outs, _stream(stream))
+    if rc:
+        raise MoeError("moe_forward_noalloc", rc)
+    return (out, routing) if return_routing else out
+
+
+__all__ = ["router", "forward", "forward_noalloc", "pack_weights", "bias_update", "bias_quantile", "workspace_size", "desc", "lib", "MoeError",
            "LayerDesc", "ExpertWeights", "Workspace", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3",
            "MOE_LAYOUT_ROWS", "MOE_LAYOUT_FRAG16", "EXPORTS", "WEIGHT_NAMES", "SCALE_NAMES"]

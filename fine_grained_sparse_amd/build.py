@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build", "moe")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.cpp", "gemm.hip", "router.hip", "dispatch.hip", "pack.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "router.hip", "dispatch.hip", "pack.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

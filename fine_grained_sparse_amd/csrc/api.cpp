@@ -380,6 +380,7 @@ const char* moe_status_str(moe_status st) {
         case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_size()";
         case MOE_ERR_UNSUPPORTED: return "unsupported dtype combination";
         case MOE_ERR_HIP: return "a HIP launch failed";
+        case MOE_ERR_SCRATCH: return "the layer needs more than the fixed scratch of moe_forward_noalloc";
     }
     return "unknown status";
 }

@@ -26,7 +26,8 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller, row-major,
  *     16-byte aligned.  The library never allocates, frees or retains memory;
- *     scratch lives in the caller's workspace (see moe_workspace_size).
+ *     scratch lives in the caller's workspace (see moe_workspace_size), or,
+ *     for moe_forward_noalloc only, in a fixed array the library holds.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work on it and return without synchronising; results are
  *     ready when the stream reaches them.  Concurrent calls need distinct
@@ -63,7 +64,9 @@ typedef enum {
     MOE_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned              */
     MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_size()   */
     MOE_ERR_UNSUPPORTED = 5, /* a dtype combination the library does not run  */
-    MOE_ERR_HIP = 6          /* a HIP launch failed                           */
+    MOE_ERR_HIP = 6,         /* a HIP launch failed                           */
+    MOE_ERR_SCRATCH = 7      /* moe_forward_noalloc: the layer needs more     */
+                             /* scratch than MOE_NOALLOC_SCRATCH_BYTES        */
 } moe_status;
 
 typedef struct {
@@ -190,6 +193,29 @@ moe_status moe_forward(const moe_layer_desc *desc, const void *x,
                        int32_t *sorted_token, void *workspace,
                        size_t workspace_bytes, void *stream,
                        void *const *stage_events);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * whole layer exactly as moe_forward (same arguments, kernels and results),
+ * but its scratch is a fixed array of MOE_NOALLOC_SCRATCH_BYTES (128 MiB)
+ * that the library holds on each GPU it runs on until the process ends, so
+ * no workspace is passed and nothing is allocated.  Enough for the K2 layer
+ * up to T = 512 tokens and the K3 latent layer at T = 256; a descriptor
+ * needing more (moe_workspace_size(desc, 1) > MOE_NOALLOC_SCRATCH_BYTES)
+ * returns MOE_ERR_SCRATCH with nothing enqueued.  The array of the current
+ * device is used (its address is resolved on the first call on that
+ * device), so `stream` must belong to the current device.  All calls on one
+ * GPU share that array and it keeps the last call's contents (no call reads
+ * a byte of it that the same call did not write first): calls that overlap
+ * in time on one GPU -- on different streams, or from several threads --
+ * race on it and must be serialised by the caller.                         */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+moe_status moe_forward_noalloc(const moe_layer_desc *desc, const void *x,
+                               const float *W_r, const float *b,
+                               const moe_expert_weights *weights, void *out,
+                               int32_t *topk_idx, float *topk_w,
+                               int32_t *expert_counts, int32_t *expert_offsets,
+                               int32_t *sorted_token, void *stream);
 
 /* Aux-loss-free bias update after a batch [llm-arch-kb "Kimi K2 MoE"
  * section 2: the selection bias follows DeepSeek V3's schedule, sign only,

@@ -31,8 +31,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["moe_bias_quantile", "moe_bias_update", "moe_forward",
-                                  "moe_pack_weights", "moe_router", "moe_status_str",
-                                  "moe_workspace_size"])
+                                  "moe_forward_noalloc", "moe_pack_weights", "moe_router",
+                                  "moe_status_str", "moe_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = moe.lib()
-    for code in range(7):
+    for code in range(8):
         assert L.moe_status_str(code)
     assert L.moe_status_str(99) == b"unknown status"
 
