@@ -232,8 +232,8 @@ moe_status moe_bias_update(const moe_layer_desc *desc,
                            float gamma, void *stream);
 
 /* Quantile Balancing [lilting.ch K3 essay, the load-balancing paragraph:
- * the threshold at which each expert receives its target number of tokens
- * is read off a quantile of the router scores and sets the selection bias].
+ * each expert's selection bias comes from a quantile of the router scores,
+ * namely the score theta_e at which expert e gets its target load].
  * This library's reading: over the batch x [T, d], s = sigmoid(x W_r^T)
  * (the unbiased scores, computed as in moe_router); every expert's target
  * is the mean load n = max(1, floor(T K / E)); theta_e = the n-th largest

@@ -561,9 +561,9 @@ static int cmp_desc(const void *a, const void *b)
     return (x < y) - (x > y);
 }
 
-/* Quantile Balancing [P4, the load-balancing paragraph: each expert's
- * threshold for receiving its target number of tokens is read off a
- * quantile of the router scores and sets the selection bias].  Reading:
+/* Quantile Balancing [P4, the load-balancing paragraph: a quantile of the
+ * router scores gives each expert's selection bias, namely the score at
+ * which that expert reaches its target load].  Reading:
  * over the batch, s[t, e] = sigmoid(x_t . W_r[e]) (the unbiased router
  * scores, as in oracle_router); every expert's target is the mean load
  * n = max(1, floor(T K / E)) tokens; its threshold theta_e is the n-th
