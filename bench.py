@@ -7,15 +7,22 @@ input already resident in HBM.  Prints ONE JSON line.
 
 Default workload: the K2-shaped layer at 16384 tokens (prefill-sized
 grouped GEMMs).  Measured in the same run and reported under "also": the
-256-token decode batch on the same weights, the router alone at 4096
-tokens, and the K3-shaped latent layer.
+256-token decode batch on the same weights, the same prefill batch with a
+stronger expert skew, the router alone at 4096 tokens, the K3-shaped latent
+layer, the FP8 layers and the bias updates.
 Per-stage durations come from hipEvents the library records at its stage
-boundaries on the launch stream (include/moe.h, MOE_EV_*); the up-projection
-stage is a single kernel (the grouped SwiGLU GEMM), the one the "roofline"
-object describes.  Its "traffic" is read from profiles/up_gemm_hbm_traffic.md when that
-table holds a row for the workload taken with the current kernel sources
-(otherwise null); `--summarize-counters` writes such rows from two
-rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) of this script.
+boundaries on the launch stream (include/moe.h, MOE_EV_*); the up, down and
+combine stages are one kernel each.  "roofline" describes the up projection
+(the grouped SwiGLU GEMM, the dominant kernel); "kernels" gives the same for
+the down projection and the combine.  Each "traffic" is read from
+profiles/hbm_traffic.md when that table holds a row for the workload and
+stage taken with the current kernel sources (otherwise null);
+`--summarize-counters` writes such rows from two rocprofv3 --pmc passes
+(FETCH_SIZE, WRITE_SIZE) of this script, `--summarize-sq` the rows of
+profiles/sq_counters.md (MFMA busy, shader clock) from one pass.
+The "yardsticks" leg measures, in the same run, a pure HBM streaming read and
+a register-only bf16 MFMA loop (with the shader clock it ran at); each
+roofline is also given as a fraction of those measured peaks.
 """
 import argparse
 import csv
@@ -36,12 +43,15 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-TRAFFIC_MD = os.path.join(ROOT, "profiles", "up_gemm_hbm_traffic.md")
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+SQ_MD = os.path.join(ROOT, "profiles", "sq_counters.md")
 CAL_REPS = 3                # streaming copies of --calibrate-copy-gib each
 WEIGHTS_NOTE = {"frag16": "bf16, fragment-block layout (moe_pack_weights once at load, untimed)",
                 "rows": "bf16, row-major"}
 FP8_NOTE = ("routed experts FP8 E4M3FN with one E8M0 scale per 128x128 block, shared experts "
             "bf16; fragment-block layout (moe_pack_weights once at load, untimed)")
+# the library's sources that define or launch the layer's kernels
+LAYER_SOURCES = ("api.cpp", "common.hpp", "launch.hpp", "gemm.hip", "router.hip", "dispatch.hip")
 
 
 def weights_note(wl, layout):
@@ -52,15 +62,12 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-GEMM_SOURCES = ("api.cpp", "common.hpp", "gemm.hip", "launch.hpp")  # define or launch the GEMMs
-
-
 def source_hash() -> str:
-    """Hash of the sources that define and launch the grouped GEMMs, with
+    """Hash of the sources that define and launch the layer's kernels, with
     comments and whitespace removed: counters taken on other code do not
     describe the kernels that run now."""
     h = hashlib.sha256()
-    for name in GEMM_SOURCES:
+    for name in LAYER_SOURCES:
         p = os.path.join(ROOT, "fine_grained_sparse_amd", "csrc", name)
         if os.path.exists(p):
             with open(p) as f:
@@ -72,20 +79,27 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, layout: str):
-    """GB per dispatch of the up-projection for this workload, weight layout
-    and kernel source (a row of profiles/up_gemm_hbm_traffic.md), else None."""
-    if not os.path.exists(TRAFFIC_MD):
-        return None
-    want = source_hash()
-    with open(TRAFFIC_MD) as f:
+def _md_rows(path):
+    if not os.path.exists(path):
+        return []
+    rows = []
+    with open(path) as f:
         for line in f:
-            cells = [c.strip() for c in line.strip().strip("|").split("|")]
-            if len(cells) >= 10 and cells[0] == workload and cells[1] == layout and cells[3] == want:
-                try:
-                    return float(cells[9])
-                except ValueError:
-                    return None
+            if line.startswith("|") and not line.startswith("|---"):
+                rows.append([c.strip() for c in line.strip().strip("|").split("|")])
+    return rows
+
+
+def load_traffic(workload: str, layout: str, stage: str):
+    """HBM-side GB per launch of one stage's kernel for this workload, weight
+    layout and kernel source (a row of profiles/hbm_traffic.md), else None."""
+    want = source_hash()
+    for c in _md_rows(TRAFFIC_MD):
+        if len(c) >= 11 and c[0] == workload and c[1] == layout and c[2] == stage and c[4] == want:
+            try:
+                return float(c[10])
+            except ValueError:
+                return None
     return None
 
 
@@ -101,17 +115,56 @@ def up_kernel(wl, layout):
     return "k_gemm_big (" + ("128x256" if big_rows else "16x512") + ", weights through LDS)"
 
 
-def is_up_kernel(name):
-    """Kernel name (untruncated) of an up-projection dispatch: the SwiGLU
-    instantiation of k_gemm_wide<TC, EPI, NSEG, BM, F8> or of
-    k_gemm_big<TC, BM, BN, WM, WN, NST, ROWB, EPI, PK>."""
-    m = re.search(r"k_gemm_(wide|big)<([^>]*)>", name)
+def gemm_epilogue(name):
+    """1 for the SwiGLU instantiation of a GEMM kernel (k_gemm_wide<TC, EPI,
+    NSEG, BM, F8>, k_gemm_big<TC, BM, BN, WM, WN, NST, ROWB, EPI, PK>,
+    k_gemm<TC, EPI, ...>), 0 for the store epilogue, None if not a GEMM."""
+    m = re.search(r"k_gemm(_wide|_big)?<([^>]*)>", name)
     if not m:
-        return False
+        return None
     args = m.group(2).replace(" ", "").split(",")
-    if m.group(1) == "wide":          # k_gemm_wide<TC, EPI, NSEG, BM, F8>
-        return args[1] == "1"
-    return args[7] == "1"
+    if m.group(1) == "_wide":
+        return int(args[1] == "1")
+    if m.group(1) == "_big":
+        return int(args[7] == "1")
+    return int(args[1] == "1")
+
+
+def label_stages(dispatches):
+    """Stage of every dispatch of the layer's kernels, in dispatch order.
+    dispatches: [(dispatch id, kernel name)].  A forward call starts with
+    k_split3; its GEMMs come in the order router logits, [x_lat], up (the
+    SwiGLU one), down, [latent output map]; the rest are named by their
+    kernel."""
+    out = {}
+    phase = None          # None, "router", "up", "combine": the last landmark of the call
+    for did, name in sorted(dispatches):
+        epi = gemm_epilogue(name)
+        if "k_split3" in name:
+            stage, phase = "split", None
+        elif "k_topk_gate" in name:
+            stage = "gate"
+        elif "k_dispatch" in name:
+            stage = "dispatch"
+        elif "k_combine" in name:
+            stage, phase = "combine", "combine"
+        elif epi == 1:
+            stage, phase = "up", "up"
+        elif epi == 0:
+            if phase is None:
+                stage, phase = "router", "router"
+            elif phase == "router":
+                stage = "latent"
+            elif phase == "up":
+                stage, phase = "down", "down"
+            elif phase == "combine":
+                stage = "end"
+            else:
+                continue
+        else:
+            continue
+        out[did] = stage
+    return out
 
 
 def get_workload_light(name):
@@ -120,15 +173,15 @@ def get_workload_light(name):
 
 
 def work_model(wl, counts):
-    """Algorithmic flops and bytes of one forward step and of the
-    up-projection kernel (routed rows + shared experts).  Bytes: weights of
-    the experts that received
-    tokens read once, shared / router / latent weights, x read and out
-    written once (temporaries excluded).  Flops: the selected experts'
-    SwiGLU, the shared experts, the latent maps; the router counted apart
+    """Algorithmic flops and bytes of one forward step and of the up, down,
+    combine and (latent form) output-map kernels.  Bytes: weights of the
+    experts that received tokens read once, shared / router / latent
+    weights, x read and out written once; a kernel's own inputs and outputs
+    (H, Y) count for that kernel only.  Flops: the selected experts' SwiGLU,
+    the shared experts, the latent maps; the router counted apart
     (fp32-class)."""
     es = 2 if wl.act_dtype == "bf16" else 4
-    din, F, d, T = wl.d_in, wl.F, wl.d, wl.T
+    din, F, d, T, dl = wl.d_in, wl.F, wl.d, wl.T, wl.d_latent
     Fsh = wl.n_shared * wl.F_shared
     A = wl.T * wl.K
     touched = int(sum(1 for c in counts if c > 0))
@@ -140,17 +193,55 @@ def work_model(wl, counts):
     w_expert = 3 * din * F * wes + 3 * sblk
     flops_routed = 2.0 * A * 3 * din * F
     flops_shared = 2.0 * T * 3 * d * Fsh
-    flops_latent = 2.0 * T * d * wl.d_latent * 2
+    flops_latent = 2.0 * T * d * dl * 2
     flops_router = 2.0 * T * d * wl.E
     bytes_step = (touched * w_expert + 3 * d * Fsh * es + wl.E * d * 4 + wl.E * 4
-                  + 2 * d * wl.d_latent * es + 2 * T * d * es)
-
-    up = dict(
-        flops=2.0 * A * din * 2 * F + 2.0 * T * d * 2 * Fsh,
-        bytes=(touched * (2 * F * din * wes + 2 * sblk) + 2 * Fsh * d * es + T * din * es
-               + A * F * es + T * Fsh * es))
+                  + 2 * d * dl * es + 2 * T * d * es)
+    x_in = T * d * es + (T * dl * es if dl else 0)      # x (and x_lat) read once
+    up = dict(flops=2.0 * A * din * 2 * F + 2.0 * T * d * 2 * Fsh,
+              bytes=(touched * (2 * F * din * wes + 2 * sblk) + 2 * Fsh * d * es + x_in
+                     + A * F * es + T * Fsh * es))
+    if dl:   # routed experts only; the shared down projection is part of the output map
+        down = dict(flops=2.0 * A * F * din,
+                    bytes=touched * (din * F * wes + sblk) + A * F * es + A * din * es)
+        combine = dict(flops=2.0 * A * din, bytes=A * din * es + A * 8 + T * din * es)
+        end = dict(flops=2.0 * T * (Fsh + dl) * d,
+                   bytes=(Fsh + dl) * d * es + T * (Fsh + dl) * es + T * d * es)
+    else:
+        down = dict(flops=2.0 * A * F * d + 2.0 * T * Fsh * d,
+                    bytes=(touched * (d * F * wes + sblk) + Fsh * d * es + A * F * es
+                           + T * Fsh * es + (A + (T if Fsh else 0)) * d * es))
+        combine = dict(flops=2.0 * A * d,
+                       bytes=(A + (T if Fsh else 0)) * d * es + A * 8 + T * d * es)
+        end = None
     return dict(touched=touched, flops_bf16=flops_routed + flops_shared + flops_latent,
-                flops_router=flops_router, bytes=bytes_step, up=up)
+                flops_router=flops_router, bytes=bytes_step, up=up, down=down, combine=combine,
+                end=end)
+
+
+def roofline(work, ms, kernel, traffic, ys=None):
+    """Roofline object of one kernel: algorithmic work per launch over its
+    average duration, against the spec peak of the bound its intensity
+    selects (and against the peak measured in this run, when known)."""
+    mfma = work["flops"] / work["bytes"] >= RIDGE_BF16
+    if mfma:
+        ach = work["flops"] / (ms * 1e-3) / 1e12
+        r = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                 frac=round(ach / PEAK_BF16_TFLOPS, 4))
+    else:
+        ach = work["bytes"] / (ms * 1e-3) / 1e9
+        r = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                 frac=round(ach / PEAK_HBM_GBS, 4))
+    r.update(traffic=traffic, kernel=kernel, avg_ms=round(ms, 4),
+             algorithmic_tflop=round(work["flops"] / 1e12, 4),
+             algorithmic_gb=round(work["bytes"] / 1e9, 3))
+    if traffic is not None:
+        r["traffic_unit"] = "GB per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    if ys:
+        key = "mfma_tflops" if mfma else "hbm_read_gbs"
+        r["measured_peak"] = ys[key]
+        r["frac_of_measured"] = round(ach / ys[key], 4)
+    return r
 
 
 def _events(torch, n, stream):
@@ -199,24 +290,6 @@ def measure_layer(moe, torch, wl, weights, steps, warmup, seed, layout):
     for j in range(1, nev):
         stages[moe.STAGES[j]] = sum(evs[i][j - 1].elapsed_time(evs[i][j]) for i in range(steps)) / steps
     wm = work_model(wl, counts)
-    up_ms = stages["up"]
-    up = wm["up"]
-    traffic = load_traffic(wl.name, layout)
-    kernel = up_kernel(wl, layout)
-    if up["flops"] / up["bytes"] >= RIDGE_BF16:
-        ach = up["flops"] / (up_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=traffic, kernel=kernel,
-                    avg_ms=round(up_ms, 4), algorithmic_tflop=round(up["flops"] / 1e12, 4),
-                    algorithmic_gb=round(up["bytes"] / 1e9, 3))
-    else:
-        ach = up["bytes"] / (up_ms * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(ach / PEAK_HBM_GBS, 4), traffic=traffic, kernel=kernel,
-                    avg_ms=round(up_ms, 4), algorithmic_gb=round(up["bytes"] / 1e9, 3),
-                    algorithmic_tflop=round(up["flops"] / 1e12, 4))
-    if traffic is not None:
-        roof["traffic_unit"] = "GB per launch"
     layer_s = ms * 1e-3
     layer = dict(tflops_bf16=round(wm["flops_bf16"] / layer_s / 1e12, 2),
                  mfma_frac=round(wm["flops_bf16"] / layer_s / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -227,8 +300,27 @@ def measure_layer(moe, torch, wl, weights, steps, warmup, seed, layout):
                  touched_experts=wm["touched"],
                  hist_min_mean_max=[min(counts), round(sum(counts) / len(counts), 2), max(counts)])
     return dict(value=wl.T / layer_s, ms=ms, stages={k: round(v, 4) for k, v in stages.items()},
-                roofline=roof, layer=layer, inputs=(x, W_r, b),
+                wm=wm, layer=layer, inputs=(x, W_r, b),
                 median_ms=round(per_step[len(per_step) // 2], 4), min_ms=round(per_step[0], 4))
+
+
+def kernel_rooflines(wl, r, layout, ys):
+    """Rooflines of the up projection (the dominant kernel) and of the down
+    projection and the combine, from the stage events of the timed steps.
+    In the latent form the combine stage also holds the output map
+    [Hs | R] [Ws_down | W_lat_up]^T, so its roofline is that of the pair."""
+    wm, st = r["wm"], r["stages"]
+    up = roofline(wm["up"], st["up"], up_kernel(wl, layout), load_traffic(wl.name, layout, "up"), ys)
+    down = roofline(wm["down"], st["down"], up_kernel(wl, layout).split(" ")[0] + " (store epilogue)",
+                    load_traffic(wl.name, layout, "down"), ys)
+    if wm["end"] is None:
+        comb = roofline(wm["combine"], st["end"], "k_combine (gather, fp32 sum, one bf16 rounding)",
+                        load_traffic(wl.name, layout, "combine"), ys)
+    else:
+        both = dict(flops=wm["combine"]["flops"] + wm["end"]["flops"],
+                    bytes=wm["combine"]["bytes"] + wm["end"]["bytes"])
+        comb = roofline(both, st["end"], "k_combine (latent weighted sum) + output map GEMM", None, ys)
+    return up, dict(down=down, combine=comb)
 
 
 def measure_router(moe, torch, wl, steps, warmup, seed):
@@ -259,17 +351,18 @@ def measure_router(moe, torch, wl, steps, warmup, seed):
     del flush
     fl = 2.0 * wl.T * wl.d * wl.E
     ach = fl / (ms * 1e-3) / 1e12
-    return dict(value=round(wl.T / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 4),
-                median_ms=round(per_call[steps // 2], 4), min_ms=round(per_call[0], 4),
-                mall="512 MB written between calls",
-                roofline=dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_F32_TFLOPS,
-                              unit="TFLOP/s", frac=round(ach / PEAK_F32_TFLOPS, 4), traffic=None,
-                              kernel="router logits + top-K gate (fp32-accurate, bf16x3 MFMA)",
-                              note="fp32 flops 2*T*d*E against the fp32 matrix peak; executed "
-                                   "as 3 bf16 MFMA passes",
-                              executed_bf16_tflops=round(3 * ach, 2)),
-                config=dict(workload=wl.name, T=wl.T, d=wl.d, E=wl.E, K=wl.K, n_group=wl.n_group,
-                            topk_group=wl.topk_group))
+    res = dict(value=round(wl.T / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 4),
+               median_ms=round(per_call[steps // 2], 4), min_ms=round(per_call[0], 4),
+               mall="512 MB written between calls",
+               roofline=dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_F32_TFLOPS,
+                             unit="TFLOP/s", frac=round(ach / PEAK_F32_TFLOPS, 4), traffic=None,
+                             kernel="router logits + top-K gate (fp32-accurate, bf16x3 MFMA)",
+                             note="fp32 flops 2*T*d*E against the fp32 matrix peak; executed "
+                                  "as 3 bf16 MFMA passes",
+                             executed_bf16_tflops=round(3 * ach, 2)),
+               config=dict(workload=wl.name, T=wl.T, d=wl.d, E=wl.E, K=wl.K, n_group=wl.n_group,
+                           topk_group=wl.topk_group))
+    return res, (x, W_r, b)
 
 
 def measure_bias_steps(moe, torch, seed):
@@ -315,80 +408,239 @@ def measure_bias_steps(moe, torch, seed):
     return out
 
 
-def cpu_baseline(torch, wl, weights, x, W_r, b, target_s, seed):
-    """The oracle as it stands, on a bounded token sample of the same
-    workload (router + K routed experts + shared experts per token, fp64,
-    OpenMP over tokens)."""
+def yardsticks(torch, read_gib=8.0, mfma_ms=20.0):
+    """Measured peaks of this GPU in this run (libyardstick.so): the best of
+    a plain and a non-temporal streaming read of read_gib GiB over a few grid
+    sizes, and the register-only bf16 MFMA loop on one workgroup (4 waves)
+    per CU, with the shader clock it ran at (clock64 over wall_clock64)."""
+    import ctypes
+    path = os.path.join(ROOT, "fine_grained_sparse_amd", "libyardstick.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build with fine_grained_sparse_amd/build.py")
+    L = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.ys_stream_read.argtypes = [vp, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    L.ys_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    L.ys_mfma_flops_per_block_iter.restype = i64
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    s = ctypes.c_void_p(stream.cuda_stream)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        best = None
+        for _ in range(reps):
+            t0.record(stream)
+            rc = fn()
+            t1.record(stream)
+            if rc:
+                raise RuntimeError(f"yardstick launch failed: hipError {rc}")
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    nbytes = int(read_gib * (1 << 30)) // 16 * 16
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    reads = {}
+    for nt in (0, 1):
+        for inflight in (8, 16):
+            for blocks in (512, 1024, 2048, 4096):
+                sink = torch.empty(blocks * 512, dtype=torch.int32, device=dev)
+                ms = timed(lambda: L.ys_stream_read(buf.data_ptr(), nbytes, nt, inflight, blocks,
+                                                    sink.data_ptr(), s), 4)
+                key = f"{'nt' if nt else 'plain'}_x{inflight}_{blocks}"
+                reads[key] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf, sink
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    per_iter = L.ys_mfma_flops_per_block_iter() * cus
+    sink = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(cus * 4, dtype=torch.int64, device=dev)
+    ms1 = timed(lambda: L.ys_mfma_loop(1000, cus, sink.data_ptr(), clocks.data_ptr(), s), 2)
+    iters = max(1000, int(1000 * mfma_ms / max(ms1, 1e-3)))
+    ms = timed(lambda: L.ys_mfma_loop(iters, cus, sink.data_ptr(), clocks.data_ptr(), s), 3)
+    c = clocks.view(cus, 4).cpu().double()
+    khz = ctypes.CDLL(path).ys_wall_clock_khz()
+    ghz = ((c[:, 1] - c[:, 0]) / (c[:, 3] - c[:, 2]) * khz / 1e6).median().item() if khz else None
+    best_key = max(reads, key=reads.get)
+    return dict(hbm_read_gbs=reads[best_key], hbm_read_best=best_key, hbm_read_all=reads,
+                mfma_tflops=round(per_iter * iters / (ms * 1e-3) / 1e12, 1),
+                mfma_clock_ghz=round(ghz, 3) if ghz else None, mfma_blocks=cus, mfma_iters=iters,
+                note=("HBM: one read of an 8 GiB buffer, 16 B per lane, 8 or 16 loads in flight, "
+                      "best of the sweep; MFMA: "
+                      "v_mfma_f32_16x16x32_bf16 chains on registers, one 4-wave workgroup per CU; "
+                      "clock = clock64 / wall_clock64 over the loop (median of the workgroups)"))
+
+
+def host_weights(weights):
+    """Host copies of a layer's weights for the oracle (one copy per tensor)."""
+    return {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in weights.items()
+            if k in ("W_gate", "W_up", "W_down", "Ws_gate", "Ws_up", "Ws_down", "W_lat_down",
+                     "W_lat_up", "W_gate_scale", "W_up_scale", "W_down_scale")}
+
+
+def _oracle_layer(oracle, wl, hw, W_r, b):
+    per = {k: ([hw[k][e] for e in range(wl.E)] if hw.get(k) is not None else None)
+           for k in ("W_gate", "W_up", "W_down", "W_gate_scale", "W_up_scale", "W_down_scale")}
+    return oracle.Layer(d=wl.d, E=wl.E, K=wl.K, F=wl.F, scale=wl.scale, W_r=W_r, b=b,
+                        W_gate=per["W_gate"], W_up=per["W_up"], W_down=per["W_down"],
+                        W_gate_scale=per["W_gate_scale"], W_up_scale=per["W_up_scale"],
+                        W_down_scale=per["W_down_scale"], n_shared=wl.n_shared,
+                        F_shared=wl.F_shared, Ws_gate=hw.get("Ws_gate"), Ws_up=hw.get("Ws_up"),
+                        Ws_down=hw.get("Ws_down"), d_latent=wl.d_latent,
+                        W_lat_down=hw.get("W_lat_down"), W_lat_up=hw.get("W_lat_up"))
+
+
+def cpu_baseline(wl, hw, inputs, target_s, seed, full=False, router_only=False):
+    """The oracle as it stands (plain fp64 loops, OpenMP over tokens) on the
+    host's cores: the whole layer per token (router over all experts, top-K,
+    K routed + the shared SwiGLU experts, latent maps), or the router alone.
+    full: every token of the batch.  Otherwise a random token sample sized to
+    about target_s seconds; rows are independent, so the per-token rate is
+    the batch's rate (labelled extrapolated)."""
     import numpy as np
     import oracle
     nth = oracle.default_threads()
-    xh, Wrh, bh = x.cpu(), W_r.cpu(), b.cpu()
+    x, W_r, b = (t.cpu() for t in inputs)
+    info = dict(unit="tokens/s", cores=nth, host_cores=oracle.host_cores(),
+                cpu_model=oracle.cpu_model(), kind="oracle")
+    if router_only:
+        t = time.perf_counter()
+        oracle.router(x, W_r, b, wl.K, wl.scale, nthreads=nth)
+        sec = time.perf_counter() - t
+        return dict(value=round(wl.T / sec, 1), seconds=round(sec, 2), **info,
+                    sample=f"all {wl.T} tokens (router over {wl.E} experts, top-{wl.K}), fp64")
+    lay = _oracle_layer(oracle, wl, hw, W_r, b)
+    what = (f"router over {wl.E} experts, top-{wl.K}, {wl.K} routed + {wl.n_shared} shared "
+            f"SwiGLU experts{', latent maps' if wl.d_latent else ''}, fp64")
+    if full:
+        t = time.perf_counter()
+        oracle.forward(lay, x, nthreads=nth)
+        sec = time.perf_counter() - t
+        return dict(value=round(wl.T / sec, 2), seconds=round(sec, 2), **info,
+                    sample=f"all {wl.T} tokens of the batch, whole layer per token ({what})")
     rng = np.random.default_rng(seed)
 
     def run(n):
         toks = np.sort(rng.choice(wl.T, size=min(n, wl.T), replace=False))
-        xs = xh[toks].contiguous()
-        r = oracle.router(xs, Wrh, bh, wl.K, wl.scale, nthreads=nth)   # which experts to copy
-        need = set(np.unique(r["idx"]).tolist())
-        per = {k: [weights[k][e].cpu() if e in need else None for e in range(wl.E)]
-               for k in ("W_gate", "W_up", "W_down")}
-        opt = {k: (weights[k].cpu() if weights.get(k) is not None else None)
-               for k in ("Ws_gate", "Ws_up", "Ws_down", "W_lat_down", "W_lat_up")}
-        lay = oracle.Layer(d=wl.d, E=wl.E, K=wl.K, F=wl.F, scale=wl.scale, W_r=Wrh, b=bh,
-                           W_gate=per["W_gate"], W_up=per["W_up"], W_down=per["W_down"],
-                           n_shared=wl.n_shared, F_shared=wl.F_shared, Ws_gate=opt["Ws_gate"],
-                           Ws_up=opt["Ws_up"], Ws_down=opt["Ws_down"], d_latent=wl.d_latent,
-                           W_lat_down=opt["W_lat_down"], W_lat_up=opt["W_lat_up"])
         t = time.perf_counter()
-        oracle.forward(lay, xs, nthreads=nth)
+        oracle.forward(lay, x[toks].contiguous(), nthreads=nth)
         return len(toks), time.perf_counter() - t
 
-    n, s = run(nth)
-    if s < target_s / 2:
-        n2 = int(min(wl.T, 96 * nth, max(nth, nth * int(target_s / max(s, 1e-3)))))
+    n, sec = run(nth)
+    if sec < target_s / 2:
+        n2 = int(min(wl.T, max(nth, nth * int(target_s / max(sec, 1e-3)))))
         if n2 > n:
-            n, s = run(n2)
-    return dict(value=round(n / s, 3), unit="tokens/s", cores=nth, kind="oracle",
+            n, sec = run(n2)
+    rate = n / sec
+    return dict(value=round(rate, 3), seconds=round(sec, 2), extrapolated=True,
+                full_batch_s=round(wl.T / rate, 1), **info,
                 sample=(f"{n} random tokens of the {wl.T}-token batch, whole layer per token "
-                        f"(router over {wl.E} experts, top-{wl.K}, {wl.K} routed + "
-                        f"{wl.n_shared} shared SwiGLU experts), fp64, {s:.1f} s"),
-                seconds=round(s, 2))
+                        f"({what}); per-token rate, extrapolated to the batch (rows independent)"))
+
+
+def _load_counter_csv(d):
+    rows = []
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            rows += list(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def _per_dispatch(rows):
+    """{dispatch id: dict(name, counters {name: value summed over the rows of
+    that dispatch}, start, end)}."""
+    out = {}
+    for r in rows:
+        did = int(r["Dispatch_Id"])
+        e = out.setdefault(did, dict(name=r["Kernel_Name"], counters={},
+                                     start=int(r.get("Start_Timestamp") or 0),
+                                     end=int(r.get("End_Timestamp") or 0)))
+        e["counters"][r["Counter_Name"]] = e["counters"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def _kernel_short(name):
+    m = re.search(r"(k_[a-z0-9_]+)(<[^>]*>)?", name)
+    if not m:
+        return name
+    return (m.group(1) + (m.group(2) or "")).replace("unsigned short", "bf16").replace(" ", "")
 
 
 def summarize_counters(fetch_dir, write_dir, workload, layout, copy_gib):
-    """One markdown row of profiles/up_gemm_hbm_traffic.md from two rocprofv3 --pmc passes
-    of this script (FETCH_SIZE, then WRITE_SIZE), each run with
-    --calibrate-copy-gib so that it also holds CAL_REPS streaming copies
-    (torch.neg, fp32) of known size.  Kernel names must not be truncated
-    (no -T; see is_up_kernel).  Counter rows of a kernel split into several
-    dispatches (the large copy) are summed."""
-    def load(d):
-        rows = []
-        for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            with open(p) as f:
-                rows += list(csv.DictReader(f))
-        return rows
-
+    """Rows of profiles/hbm_traffic.md (one per stage kernel of the layer)
+    from two rocprofv3 --pmc passes of this script (FETCH_SIZE, then
+    WRITE_SIZE), each run with --calibrate-copy-gib so that it also holds
+    CAL_REPS streaming copies (torch.neg, fp32) of known size.  The copy's
+    counts give the scale of each counter (bytes moved / bytes counted)."""
     if copy_gib <= 0:
         raise SystemExit("--calibrate-copy-gib must name the copy size the passes ran with")
     copy_bytes = CAL_REPS * (int(copy_gib * (1 << 30)) // 4) * 4   # read (= written) by the copies
-    out = {}
+    per = {}
     for tag, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rows = [r for r in load(d) if r["Counter_Name"] == tag]
-        up = [float(r["Counter_Value"]) for r in rows if is_up_kernel(r["Kernel_Name"])]
-        cal = [float(r["Counter_Value"]) for r in rows if "neg_kernel" in r["Kernel_Name"]]
-        if not up or not cal:
-            raise SystemExit(f"{tag}: no up-projection dispatches or no copy calibration in {d}")
-        scale = copy_bytes / (sum(cal) * 1024)
-        out[tag] = (sum(up) / len(up), len(up), scale)
-    f_kib, n, f_sc = out["FETCH_SIZE"]
-    w_kib, _, w_sc = out["WRITE_SIZE"]
-    gb = (f_kib * 1024 * f_sc + w_kib * 1024 * w_sc) / 1e9
-    wl = get_workload_light(workload)
-    row = (f"| {workload} | {layout} | {up_kernel(wl, layout).split(' ')[0]} | {source_hash()} | {n} | "
-           f"{f_kib:.6g} | {w_kib:.6g} | {f_sc:.3f} | {w_sc:.3f} | {gb:.3f} |")
-    print(row)
-    return row
+        disp = _per_dispatch(_load_counter_csv(d))
+        cal = sum(v["counters"].get(tag, 0.0) for v in disp.values() if "neg_kernel" in v["name"])
+        if not cal:
+            raise SystemExit(f"{tag}: no copy calibration dispatches in {d}")
+        scale = copy_bytes / (cal * 1024)
+        stages = label_stages([(k, v["name"]) for k, v in disp.items() if "neg_kernel" not in v["name"]])
+        acc = {}
+        for did, st in stages.items():
+            acc.setdefault(st, []).append((disp[did]["counters"].get(tag, 0.0), disp[did]["name"]))
+        per[tag] = (acc, scale)
+    get_workload_light(workload)      # the workload must exist
+    rows = []
+    f_acc, f_sc = per["FETCH_SIZE"]
+    w_acc, w_sc = per["WRITE_SIZE"]
+    for stage in ("router", "gate", "dispatch", "latent", "up", "down", "combine", "end"):
+        if stage not in f_acc or stage not in w_acc:
+            continue
+        fv = [v for v, _ in f_acc[stage]]
+        wv = [v for v, _ in w_acc[stage]]
+        # per launch of the stage: the dispatch stage is four kernels per call
+        nk = len({n for _, n in f_acc[stage]})
+        f_kib = sum(fv) / len(fv) * nk
+        w_kib = sum(wv) / len(wv) * nk
+        gb = (f_kib * 1024 * f_sc + w_kib * 1024 * w_sc) / 1e9
+        kname = _kernel_short(f_acc[stage][0][1]) if nk == 1 else f"{nk} kernels"
+        rows.append(f"| {workload} | {layout} | {stage} | `{kname}` | {source_hash()} | "
+                    f"{len(fv) // nk} | {f_kib:.6g} | {w_kib:.6g} | {f_sc:.3f} | {w_sc:.3f} | {gb:.3f} |")
+    for r in rows:
+        print(r)
+    return rows
+
+
+def summarize_sq(sq_dir, workload, layout):
+    """Rows of profiles/sq_counters.md from one rocprofv3 --kernel-trace
+    --pmc pass with SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CU_CYCLES and
+    GRBM_GUI_ACTIVE: per stage kernel, its duration under counter collection,
+    cycles per XCD (GRBM_GUI_ACTIVE is summed over the 8 XCDs), the shader
+    clock (cycles / duration) and the MFMA busy fraction per SIMD
+    (SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x CUs x cycles))."""
+    disp = _per_dispatch(_load_counter_csv(sq_dir))
+    stages = label_stages([(k, v["name"]) for k, v in disp.items()])
+    acc = {}
+    for did, st in stages.items():
+        acc.setdefault(st, []).append(disp[did])
+    rows = []
+    for stage in ("router", "latent", "up", "down", "combine", "end"):
+        if stage not in acc:
+            continue
+        ds = acc[stage]
+        n = len(ds)
+        ms = sum((d["end"] - d["start"]) for d in ds) / n / 1e6
+        grbm = sum(d["counters"].get("GRBM_GUI_ACTIVE", 0.0) for d in ds) / n
+        mfma = sum(d["counters"].get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for d in ds) / n
+        cyc = grbm / 8
+        ghz = cyc / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+        busy = mfma / (1024 * cyc) if cyc else 0.0
+        rows.append(f"| {workload} | {layout} | {stage} | `{_kernel_short(ds[0]['name'])}` | {source_hash()} | "
+                    f"{n} | {ms:.3f} | {cyc:.4g} | {ghz:.2f} | {busy:.3f} |")
+    for r in rows:
+        print(r)
+    return rows
 
 
 def main():
@@ -397,14 +649,17 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="k2_prefill_t16384")
-    ap.add_argument("--also", default="k2_decode_t256,k2_router_t4096,k2_router_g8_t4096,k3_latent_t4096,"
-                                      "k2_decode_fp8_t256,k2_prefill_fp8_t16384",
+    ap.add_argument("--also", default="k2_decode_t256,k2_prefill_skew4_t16384,k2_router_t4096,"
+                                      "k2_router_g8_t4096,k3_latent_t4096,k2_decode_fp8_t256,"
+                                      "k2_prefill_fp8_t16384",
                     help="comma-separated extra workloads ('' for none)")
-    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
-                    help="target seconds of oracle time (0 skips the CPU baseline)")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
+                    help="target seconds of oracle time per sampled workload (0 skips the CPU baselines)")
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--bias-steps", type=int, default=1,
                     help="also time the bias updates (moe_bias_update, moe_bias_quantile); 0 = skip")
+    ap.add_argument("--yardsticks", type=int, default=1,
+                    help="measure the HBM read and bf16 MFMA yardsticks in this run (0 = skip)")
     ap.add_argument("--layout", choices=("frag16", "rows"), default="frag16",
                     help="weight layout the layer reads: packed once at load (frag16, "
                          "moe_pack_weights, outside the timed steps) or row-major")
@@ -412,11 +667,17 @@ def main():
                     help="also run a plain streaming copy (out = -in, fp32) of this many GiB "
                          "three times, to scale HBM byte counters (0 = off)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="print the profiles/up_gemm_hbm_traffic.md row of --workload from two rocprofv3 "
+                    help="print the profiles/hbm_traffic.md rows of --workload from two rocprofv3 "
                          "--pmc output directories and exit (no GPU use)")
+    ap.add_argument("--summarize-sq", metavar="SQ_DIR",
+                    help="print the profiles/sq_counters.md rows of --workload from one rocprofv3 "
+                         "--pmc output directory and exit (no GPU use)")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.workload, args.layout, args.calibrate_copy_gib)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, args.workload, args.layout)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -427,6 +688,7 @@ def main():
     import fine_grained_sparse_amd as moe
     from moe_inputs import get_workload, make_expert_weights
 
+    cpu_on = args.cpu_baseline_seconds > 0
     if args.calibrate_copy_gib > 0:
         n = int(args.calibrate_copy_gib * (1 << 30)) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -443,23 +705,29 @@ def main():
     log(f"[bench] generating weights for {wl.name} on the GPU")
     rows = make_expert_weights(wl, "cuda:0", seed=args.seed)
     weights = prepare(moe, torch, wl, rows, args.layout)
-    if args.cpu_baseline_seconds <= 0:
-        del rows
-        rows = None
     torch.cuda.synchronize()
     log(f"[bench] timing {wl.name}: warmup {args.warmup}, steps {args.steps}")
     main_r = measure_layer(moe, torch, wl, weights, args.steps, args.warmup, args.seed, args.layout)
     log(f"[bench] {wl.name}: {main_r['ms']:.3f} ms/step, stages {main_r['stages']}")
     main_wl = wl
-    also = {}
+    # host copies for the oracle legs, taken between GPU timings (nothing is timed meanwhile)
+    host = {}
+    if cpu_on:
+        log(f"[bench] host copy of the {wl.name} weights for the oracle")
+        host[(wl.d, wl.E, wl.F, wl.d_latent, wl.w_dtype)] = host_weights(rows)
+    del rows
+    cpu_jobs = [(main_wl.name, main_wl, main_r["inputs"], dict())]
+    also, also_raw = {}, {}
     others = [s for s in args.also.split(",") if s]
     for name in others:
         awl = get_workload(name)
         log(f"[bench] timing {name}")
         if awl.router_only:
-            r = measure_router(moe, torch, awl, max(args.steps, 100), args.warmup, args.seed)
+            r, inputs = measure_router(moe, torch, awl, max(args.steps, 100), args.warmup, args.seed)
             log(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step")
             also[name] = r
+            if cpu_on and awl.n_group <= 1:
+                cpu_jobs.append((name, awl, inputs, dict(router_only=True)))
             continue
         same = (awl.d, awl.E, awl.F, awl.n_shared, awl.F_shared, awl.d_latent, awl.act_dtype, awl.w_dtype) == \
                (wl.d, wl.E, wl.F, wl.n_shared, wl.F_shared, wl.d_latent, wl.act_dtype, wl.w_dtype)
@@ -467,36 +735,64 @@ def main():
             del weights
             torch.cuda.empty_cache()
             log(f"[bench] generating weights for {name} on the GPU")
-            weights = prepare(moe, torch, awl, make_expert_weights(awl, "cuda:0", seed=args.seed),
-                              args.layout)
+            arows = make_expert_weights(awl, "cuda:0", seed=args.seed)
+            weights = prepare(moe, torch, awl, arows, args.layout)
+            key = (awl.d, awl.E, awl.F, awl.d_latent, awl.w_dtype)
+            if cpu_on and awl.d_latent and key not in host:
+                log(f"[bench] host copy of the {name} weights for the oracle")
+                host[key] = host_weights(arows)
+            del arows
             wl = awl
         n_steps = max(args.steps, 50 if awl.T <= 1024 else 20)   # decode-sized: more, shorter steps
         r = measure_layer(moe, torch, awl, weights, n_steps, args.warmup, args.seed, args.layout)
         log(f"[bench] {name}: {r['ms']:.3f} ms/step, stages {r['stages']}")
+        also_raw[name] = (awl, r)
         also[name] = dict(value=round(r["value"], 1), unit="tokens/s", ms_per_step=round(r["ms"], 4),
-                          median_ms=r["median_ms"], min_ms=r["min_ms"],
-                          roofline=r["roofline"], layer=r["layer"], stages_ms=r["stages"],
+                          median_ms=r["median_ms"], min_ms=r["min_ms"], layer=r["layer"],
+                          stages_ms=r["stages"],
                           config=dict(workload=name, T=awl.T, d=awl.d, E=awl.E, K=awl.K,
                                       F=awl.F, n_shared=awl.n_shared, F_shared=awl.F_shared,
                                       d_latent=awl.d_latent, scale=awl.scale,
+                                      zipf_scale=awl.zipf_scale if awl.zipf_skew else None,
                                       weights=weights_note(awl, args.layout)))
+        if cpu_on and awl.w_dtype != "fp8" and name in ("k2_decode_t256", "k3_latent_t4096"):
+            cpu_jobs.append((name, awl, r["inputs"], dict(full=awl.T <= 256)))
+    del weights
+    torch.cuda.empty_cache()
     if args.bias_steps:
         log("[bench] bias updates")
-        del weights
-        torch.cuda.empty_cache()
         also.update(measure_bias_steps(moe, torch, args.seed))
         log(f"[bench] bias: {also['bias_update_e384']['us_per_call']} us (sign), "
             f"{also['bias_quantile_k3_t4096']['ms_per_call']} ms (quantile)")
-    # The oracle runs last: its host copies of the experts (tens of GB) and
-    # threads must not share the host with any GPU timing.
+    ys = None
+    if args.yardsticks:
+        log("[bench] yardsticks: HBM streaming read, bf16 MFMA loop")
+        ys = yardsticks(torch)
+        log(f"[bench] yardsticks: {ys['hbm_read_gbs']} GB/s ({ys['hbm_read_best']}), "
+            f"{ys['mfma_tflops']} TFLOP/s at {ys['mfma_clock_ghz']} GHz")
+    main_roof, main_kernels = kernel_rooflines(main_wl, main_r, args.layout, ys)
+    for name, (awl, r) in also_raw.items():
+        roof, kern = kernel_rooflines(awl, r, args.layout, ys)
+        also[name]["roofline"] = roof
+        also[name]["kernels"] = kern
+    # The oracle runs last: its host copies of the experts and its threads
+    # must not share the host with any GPU timing.
     cpu = None
-    if args.cpu_baseline_seconds > 0:
-        log("[bench] CPU baseline (oracle)")
-        x, W_r, b = main_r["inputs"]
-        cpu = cpu_baseline(torch, main_wl, rows, x, W_r, b, args.cpu_baseline_seconds, args.seed)
-        log(f"[bench] oracle: {cpu['value']} tokens/s on {cpu['cores']} threads")
-    rows = None
-    mw = get_workload(args.workload)
+    for name, jwl, inputs, kw in cpu_jobs:
+        hw = None
+        if not kw.get("router_only"):
+            hw = host.get((jwl.d, jwl.E, jwl.F, jwl.d_latent, jwl.w_dtype))
+            if hw is None:
+                continue
+        log(f"[bench] CPU baseline (oracle): {name}")
+        res = cpu_baseline(jwl, hw, inputs, args.cpu_baseline_seconds, args.seed, **kw)
+        log(f"[bench] oracle {name}: {res['value']} tokens/s on {res['cores']} threads ({res['seconds']} s)")
+        if name == main_wl.name:
+            cpu = res
+        else:
+            also[name]["cpu_baseline"] = res
+    host = None
+    mw = main_wl
     line = {
         "metric": METRIC, "value": round(main_r["value"], 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(main_r["ms"], 4),
@@ -505,10 +801,11 @@ def main():
         "data": "synthetic (seeded N(0,1) x, N(0,1/fan_in) weights, Zipf(1.1) expert skew)",
         "config": dict(workload=mw.name, T=mw.T, d=mw.d, E=mw.E, K=mw.K, F=mw.F,
                        n_shared=mw.n_shared, F_shared=mw.F_shared, d_latent=mw.d_latent,
-                       scale=mw.scale, weights=weights_note(mw, args.layout),
-                       parallelism="single-gpu"),
-        "roofline": main_r["roofline"], "cpu_baseline": cpu, "layer": main_r["layer"],
-        "stages_ms": main_r["stages"], "kernel_source": source_hash(), "also": also,
+                       scale=mw.scale, zipf_scale=mw.zipf_scale,
+                       weights=weights_note(mw, args.layout), parallelism="single-gpu"),
+        "roofline": main_roof, "cpu_baseline": cpu, "kernels": main_kernels,
+        "layer": main_r["layer"], "stages_ms": main_r["stages"], "yardsticks": ys,
+        "kernel_source": source_hash(), "also": also,
     }
     print(json.dumps(line), flush=True)
 

@@ -16,7 +16,8 @@ FP8 routed experts (w_dtype "fp8"; shared experts and latent maps bf16):
   (torch's round-to-nearest cast is only the sampler: the layer takes the
   codes as given), so code * 2^(s - 127) has std about sigma.
 Zipf skew: a seeded permutation gives each expert a rank r in 1..E and an
-offset o = 0.5 * r**-1.1 (fp32).  The offset is placed inside the inputs:
+offset o = a * r**-1.1 (fp32), a = the workload's zipf_scale (0.5 unless
+stated).  The offset is placed inside the inputs:
 the last feature of every token is set to 1.0 and the last column of W_r to
 o, so every logit of expert e gains exactly o_e without touching the layer.
 
@@ -67,7 +68,7 @@ def make_router_inputs(wl, device="cpu", seed=42, T=None):
     if wl.zipf_skew:
         perm = torch.randperm(wl.E, generator=_gen(seed, STREAM["zipf"], torch.device("cpu")))
         rank = (perm + 1).to(torch.float64)
-        offset = (0.5 * rank.pow(-1.1)).to(torch.float32)
+        offset = (wl.zipf_scale * rank.pow(-1.1)).to(torch.float32)
         x[:, wl.d - 1] = 1.0
         W_r[:, wl.d - 1] = offset.to(dev)
     return dict(x=x.contiguous(), W_r=W_r.contiguous(), b=b.contiguous())

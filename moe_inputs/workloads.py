@@ -33,6 +33,7 @@ class Workload:
     router_only: bool  # the workload measures the router alone
     n_group: int = 1   # group-limited choice: expert groups (1: plain top-K)
     topk_group: int = 1  # groups kept per token when n_group > 1
+    zipf_scale: float = 0.5  # logit offset of the rank-1 expert when zipf_skew
 
     @property
     def d_in(self) -> int:
@@ -71,6 +72,13 @@ WORKLOADS = {
     # K2 layer, prefill-sized batch: grouped GEMMs.
     "k2_prefill_t16384": Workload(name="k2_prefill_t16384", T=16384,
                                   router_only=False, **_K2),
+    # The K2 prefill layer with a stronger skew: the rank-1 expert's logit
+    # offset is 0.8 instead of 0.5, so that the hottest expert of the batch
+    # gets about 4x the mean load (0.5 gives 2.25x on this draw: the bias
+    # b ~ U(+-0.02) moves a score near the selection threshold by as much as
+    # a logit offset of about 0.2, comparable to all but the top offsets).
+    "k2_prefill_skew4_t16384": Workload(name="k2_prefill_skew4_t16384", T=16384,
+                                        router_only=False, **dict(_K2, zipf_scale=0.8)),
     # The same two K2 layers with the routed experts stored in FP8 with
     # 128 x 128 block scales (the router card's checkpoint note).
     "k2_decode_fp8_t256": Workload(name="k2_decode_fp8_t256", T=256, router_only=False,

@@ -68,12 +68,34 @@ def lib():
     return _lib
 
 
-def default_threads() -> int:
+def host_cores() -> int:
+    """CPU cores this process may run on (its affinity mask)."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return os.cpu_count() or 1
+
+
+def default_threads() -> int:
+    """Threads of the oracle's OpenMP loops: every core of the affinity mask,
+    or fewer when OMP_NUM_THREADS is set lower (a share of a shared host)."""
+    n = host_cores()
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _host(a, what):
