@@ -928,6 +928,14 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
             if constexpr (F8) {
                 uint4 f0;
                 fp8x16_to_bf16(fb[0][j], (EPI == EPI_SWIGLU && j >= NB / 2) ? su : sg, f0, f1[j]);
+                // Both halves are converted before the codes' registers take the
+                // next stage's load (the empty asm uses the second half here, and
+                // its memory clobber keeps the load below it).  Left to itself the
+                // compiler converts the second half in the second slab, keeps the
+                // old codes in other registers and copies the new ones back at the
+                // loop's end -- a copy that must wait for every load in flight
+                // (vmcnt(0)) once per stage.
+                asm volatile("" ::"v"(f1[j].x), "v"(f1[j].y), "v"(f1[j].z), "v"(f1[j].w) : "memory");
                 fb[0][j] = load_b(kb, 0, j);
 #pragma unroll
                 for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(f0, fa0[i], acc[i][j]);
