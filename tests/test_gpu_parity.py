@@ -215,7 +215,7 @@ def test_forward_parity_every_token(name, packed):
 @pytest.mark.parametrize("packed", [False, True], ids=["rows", "packed"])
 @pytest.mark.parametrize("case", ["one_token", "K_equals_E", "no_shared", "skewed_few_experts",
                                   "latent_no_shared", "large_tiles", "large_tiles_latent",
-                                  "half_tiles"])
+                                  "half_tiles", "max_limits"])
 def test_forward_edge_cases(case, packed):
     if case == "one_token":
         wl = _custom(T=1)
@@ -234,6 +234,9 @@ def test_forward_edge_cases(case, packed):
         # 512-wide tile
         wl = _custom(E=5, K=2, T=1100, d=320, F=192, n_shared=1, F_shared=128, d_latent=192,
                      scale=1.0)
+    elif case == "max_limits":  # the ABI's limits: 1024 experts, top-16, 8 shared experts,
+        # the narrowest widths (64)
+        wl = _custom(E=1024, K=16, T=300, d=192, F=64, n_shared=8, F_shared=64)
     else:  # half_tiles: expert 0 gets four full 128-row tiles + 8 rows, the others ~35
         # rows each: 128-row tiles that are mostly padding
         wl = _custom(E=16, K=2, T=520, d=256, F=128, n_shared=1, F_shared=128)

@@ -89,3 +89,32 @@ def test_noalloc_calls_take_no_device_memory():
     torch.cuda.synchronize()
     free1, _ = torch.cuda.mem_get_info()
     assert free1 == free0
+
+
+def test_noalloc_captured_in_a_graph():
+    # The use it exists for: the call captured into a HIP graph (no
+    # allocation may happen under capture) and replayed, with eager work in
+    # between, gives moe_forward's bits on every replay.
+    wl = get_workload("mid_bf16_t300")
+    log("[gpu] noalloc under graph capture, mid_bf16_t300")
+    dev = weights_to_device(make_layer_inputs(wl, "cpu", seed=42), DEV)
+    w = moe.pack_weights(expert_weights(dev), n_shared=wl.n_shared)
+    ref = moe.forward(dev["x"], dev["W_r"], dev["b"], w, wl.K, wl.scale, n_shared=1)
+    out = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # first call on the device, outside the capture
+        moe.forward_noalloc(dev["x"], dev["W_r"], dev["b"], w, wl.K, wl.scale, n_shared=1, out=out,
+                            stream=side)
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        moe.forward_noalloc(dev["x"], dev["W_r"], dev["b"], w, wl.K, wl.scale, n_shared=1, out=out,
+                            stream=side)
+    for rep in range(3):
+        out.fill_(0.0)
+        moe.forward(dev["x"][:50].contiguous(), dev["W_r"], dev["b"], w, wl.K, wl.scale, n_shared=1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
