@@ -14,8 +14,9 @@ enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1 };
 // LDS) and WIDE (128 x 512, weights fed to registers) are the prefill tiles.
 // All bf16 prefill tiles are 128 rows, so one tile table serves both.
 // WIDE16 is the register-fed tile at 16 rows (FP8 decode; bf16 decode runs
-// SMALL).  ROUTER is the LARGE tile at 128 x 192 for the router logits
-// (unpacked fp32-out store only): 384 experts fill two N tiles exactly.
+// SMALL).  ROUTER is the LDS tile at 128 x 192 for the router logits, in
+// 128-byte row pieces and two stages (unpacked fp32-out store only): 384
+// experts fill two N tiles exactly.
 enum TileCfg { TILE_SMALL = 0, TILE_LARGE = 1, TILE_WIDE = 2, TILE_WIDE16 = 3, TILE_ROUTER = 4 };
 
 int tile_bm(TileCfg cfg);         // rows per M tile
