@@ -215,7 +215,8 @@ def test_forward_parity_every_token(name, packed):
 @pytest.mark.parametrize("packed", [False, True], ids=["rows", "packed"])
 @pytest.mark.parametrize("case", ["one_token", "K_equals_E", "no_shared", "skewed_few_experts",
                                   "latent_no_shared", "large_tiles", "large_tiles_latent",
-                                  "half_tiles", "max_limits"])
+                                  "half_tiles", "max_limits", "prefill_k8", "prefill_k6_two_shared",
+                                  "prefill_k16"])
 def test_forward_edge_cases(case, packed):
     if case == "one_token":
         wl = _custom(T=1)
@@ -234,6 +235,13 @@ def test_forward_edge_cases(case, packed):
         # 512-wide tile
         wl = _custom(E=5, K=2, T=1100, d=320, F=192, n_shared=1, F_shared=128, d_latent=192,
                      scale=1.0)
+    elif case == "prefill_k8":  # prefill-sized: 128-row expert tiles and 128-row dense tiles
+        # (T >= 1024), a ragged last row tile
+        wl = _custom(E=32, K=8, T=1100, d=256, F=128, n_shared=1, F_shared=128)
+    elif case == "prefill_k6_two_shared":  # N tail (d = 320 in 512-column tiles), two shared
+        wl = _custom(E=24, K=6, T=1030, d=320, F=128, n_shared=2, F_shared=64)
+    elif case == "prefill_k16":
+        wl = _custom(E=64, K=16, T=1024, d=192, F=64, n_shared=1, F_shared=64)
     elif case == "max_limits":  # the ABI's limits: 1024 experts, top-16, 8 shared experts,
         # the narrowest widths (64)
         wl = _custom(E=1024, K=16, T=300, d=192, F=64, n_shared=8, F_shared=64)
@@ -255,7 +263,7 @@ def test_forward_edge_cases(case, packed):
 
 
 @pytest.mark.parametrize("case", ["one_token", "K_equals_E", "no_shared", "latent_no_shared",
-                                  "large_tiles", "large_tiles_latent", "half_tiles"])
+                                  "large_tiles", "large_tiles_latent", "half_tiles", "prefill_k8"])
 def test_forward_fp8_edge_cases(case):
     # FP8 routed experts (packed): 16-row tiles below 64 rows per expert on
     # average, 128-row tiles above; the shared experts and latent maps run
@@ -275,6 +283,8 @@ def test_forward_fp8_edge_cases(case):
     elif case == "large_tiles_latent":  # 128-row expert tiles; bf16 128-row dense tiles
         wl = _custom(E=5, K=2, T=1100, d=320, F=256, n_shared=1, F_shared=128, d_latent=256,
                      scale=1.0, **fp8)
+    elif case == "prefill_k8":  # prefill-sized tiles, top-8
+        wl = _custom(E=32, K=8, T=1100, d=256, F=128, n_shared=1, F_shared=128, **fp8)
     else:  # half_tiles: expert 0 takes every token, the others ~35 rows each
         wl = _custom(E=16, K=2, T=520, **fp8)
     inp = make_layer_inputs(wl, "cpu", seed=6)
