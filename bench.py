@@ -55,6 +55,8 @@ LAYER_SOURCES = ("api.cpp", "common.hpp", "launch.hpp", "gemm.hip", "router.hip"
 
 
 def weights_note(wl, layout):
+    if wl.w_dtype == "f32":
+        return "fp32, row-major (the fp32 layer has no packed layout)"
     return FP8_NOTE if wl.w_dtype == "fp8" else WEIGHTS_NOTE[layout]
 
 
@@ -106,6 +108,8 @@ def load_traffic(workload: str, layout: str, stage: str):
 def up_kernel(wl, layout):
     """The kernel the library runs for the up projection of this workload."""
     big_rows = wl.T * wl.K >= 64 * wl.E and wl.act_dtype == "bf16"
+    if wl.w_dtype == "f32":
+        return "k_gemm (fp32, 16 x 256 register-staged tiles)"
     if wl.w_dtype == "fp8":
         return ("k_gemm_wide FP8 (" + ("128x512" if big_rows else "16x512") +
                 ", register-fed, codes converted to bf16 in registers; the shared expert's "
@@ -254,8 +258,8 @@ def _events(torch, n, stream):
 def prepare(moe, torch, wl, rows, layout):
     """The weights the layer reads: row-major as generated, or packed once
     (a one-time load step, not part of the timed forward)."""
-    if layout == "rows" and wl.w_dtype != "fp8":   # FP8 experts are read packed only
-        return rows
+    if (layout == "rows" and wl.w_dtype != "fp8") or wl.w_dtype == "f32":
+        return rows                  # FP8 experts are read packed only; fp32 row-major only
     packed = moe.pack_weights(rows, n_shared=wl.n_shared)
     torch.cuda.synchronize()
     return packed
@@ -651,7 +655,7 @@ def main():
     ap.add_argument("--workload", default="k2_prefill_t16384")
     ap.add_argument("--also", default="k2_decode_t256,k2_prefill_skew4_t16384,k2_router_t4096,"
                                       "k2_router_g8_t4096,k3_latent_t4096,k2_decode_fp8_t256,"
-                                      "k2_prefill_fp8_t16384",
+                                      "k2_prefill_fp8_t16384,tiny_fp32_t128",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
                     help="target seconds of oracle time per sampled workload (0 skips the CPU baselines)")
@@ -738,7 +742,7 @@ def main():
             arows = make_expert_weights(awl, "cuda:0", seed=args.seed)
             weights = prepare(moe, torch, awl, arows, args.layout)
             key = (awl.d, awl.E, awl.F, awl.d_latent, awl.w_dtype)
-            if cpu_on and awl.d_latent and key not in host:
+            if cpu_on and (awl.d_latent or awl.w_dtype == "f32") and key not in host:
                 log(f"[bench] host copy of the {name} weights for the oracle")
                 host[key] = host_weights(arows)
             del arows
@@ -755,7 +759,7 @@ def main():
                                       d_latent=awl.d_latent, scale=awl.scale,
                                       zipf_scale=awl.zipf_scale if awl.zipf_skew else None,
                                       weights=weights_note(awl, args.layout)))
-        if cpu_on and awl.w_dtype != "fp8" and name in ("k2_decode_t256", "k3_latent_t4096"):
+        if cpu_on and awl.w_dtype != "fp8" and name in ("k2_decode_t256", "k3_latent_t4096", "tiny_fp32_t128"):
             cpu_jobs.append((name, awl, r["inputs"], dict(full=awl.T <= 256)))
     del weights
     torch.cuda.empty_cache()
