@@ -861,12 +861,10 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
         const char* m = s1 ? (up ? sU1 : sB1) : (up ? sU0 : sB0);
         const uint32_t kblk = F8 ? static_cast<uint32_t>(kt) : static_cast<uint32_t>((kt - (s1 ? nk0 : 0)) * 2 + sl);
         const uint32_t blk = static_cast<uint32_t>(rb[j]) * (s1 ? kb1 : kb0) + kblk;
-        if constexpr (F8) {
-            // decode tiles (16 rows) stream each expert's codes once;
-            // prefill tiles share them through L2 across an expert's M tiles
-            if constexpr (BM == 16) return gload16_once(m + blk * 1024u + lane * 16);
-            return *reinterpret_cast<const uint4*>(m + blk * 1024u + lane * 16);
-        }
+        // decode tiles (16 rows) stream each expert's FP8 codes once, with
+        // the non-temporal hint and compiler-counted waits (exact explicit
+        // waits measured the same there); everything else is untracked
+        if constexpr (F8 && BM == 16) return gload16_once(m + blk * 1024u + lane * 16);
         return gload16_untracked(m + blk * 1024u, lane * 16);
     };
     // FP8 block scales: lane l holds the exponent of K block l of this
@@ -909,10 +907,14 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
     // first slab; the barrier sits between the slabs, after which the slot
     // of this stage (read by every wave) takes A(it + NST) and the next
     // stage's first A fragments are read while the second slab computes.
-    // bf16: the weight loads are issued untracked (like the A DMA), so the
-    // waits for them are explicit and exact.  A fragment's load is LOADS - 1
-    // loads older than the point of its first use, save the first stage's
-    // first slab, whose loads come from the prologue (2 NB - 1).
+    // The weight loads (bf16 fragments; FP8 codes at 128 rows) are issued
+    // untracked (like the A DMA), so the waits for them are explicit and
+    // exact.  A fragment's load is LOADS - 1 loads older than the point of
+    // its first use, save the first stage's first slab, whose loads come
+    // from the prologue (2 NB - 1 for bf16, NB - 1 for FP8 codes, which
+    // carry both slabs).  Waits counted by the compiler would leave out the
+    // A DMA loads and hold each fragment until NAB loads issued after it
+    // had landed too (K2 FP8 prefill: 12.24 -> 11.90 ms from exact waits).
     auto step = [&](int it, auto wait_next, auto first) {
         const int kb = min(it + 1, nkt - 1);
         uint4 fa1[MB];
@@ -927,6 +929,7 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
         for (int j = 0; j < NB; ++j) {
             if constexpr (F8) {
                 uint4 f0;
+                if constexpr (BM != 16) wait_vmcnt_fenced<decltype(first)::value ? NB - 1 : LOADS - 1>();
                 fp8x16_to_bf16(fb[0][j], (EPI == EPI_SWIGLU && j >= NB / 2) ? su : sg, f0, f1[j]);
                 // Both halves are converted before the codes' registers take the
                 // next stage's load (the empty asm uses the second half here, and
@@ -986,16 +989,14 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
                 wait_vmcnt<kWait1>();
         }, std::false_type{});
     wait_vmcnt_fenced<0>();  // every load has landed before its registers are reused
-    if constexpr (!F8) {
-        // The last stage's weight loads (re-reading that stage) are never
-        // used; this empty use keeps their registers allocated up to the
-        // wait, so nothing else is placed in them while they are in flight.
+    // The last stage's weight loads (re-reading that stage) are never used;
+    // this empty use keeps their registers allocated up to the wait, so
+    // nothing else is placed in them while they are in flight.
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl)
+    for (int sl = 0; sl < (F8 ? 1 : 2); ++sl)
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
-                asm volatile("" ::"v"(fb[sl][j].x), "v"(fb[sl][j].y), "v"(fb[sl][j].z), "v"(fb[sl][j].w));
-    }
+        for (int j = 0; j < NB; ++j)
+            asm volatile("" ::"v"(fb[sl][j].x), "v"(fb[sl][j].y), "v"(fb[sl][j].z), "v"(fb[sl][j].w));
     store_direct<TC, EPI, MB, NB, TN>(acc, G, static_cast<TC*>(G.C), row0, rows, n0, wid);
 }
 

@@ -150,9 +150,12 @@ def _kernels(isa):
     found = {}
     for f in funcs:
         name = f.split(":")[0]
-        # bf16-output register-fed kernels ("It": unsigned short); the FP8
-        # form's own weight loads are compiler-tracked (its shared-expert
-        # tiles are not), which the walk treats as untracked: stricter
+        # bf16-output register-fed kernels ("It": unsigned short), FP8
+        # forms included: their 128-row tiles load the codes untracked; the
+        # 16-row ones load them through the compiler, and the walk counts
+        # those loads in the queue but leaves their registers to the
+        # compiler's own waits (the shared-expert tiles of both are bf16
+        # and untracked)
         if name.startswith("_ZN") and ("k_gemm_wideIt" in name or "k_gemm_w192It" in name):
             found[name] = f
     return found
