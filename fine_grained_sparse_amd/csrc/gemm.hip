@@ -310,6 +310,18 @@ __device__ __forceinline__ void fp8x16_to_bf16(uint4 q, float scale, uint4& lo, 
 #undef MOE_CVT
 }
 
+// Scheduling hint for a region holding NM MFMAs and about NV VALU
+// instructions: alternate one MFMA with a share of the VALU work, so the
+// VALU instructions issue while the matrix pipe is busy.
+template <int NM, int NV>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+    for (int k = 0; k < NM; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, (NV + NM - 1) / NM, 0);
+    }
+}
+
 // 16 bytes per lane from base + voff (base wave-uniform), issued as inline
 // assembly: the compiler does not count it, so the caller waits for it with
 // an explicit vmcnt that also counts the A DMA loads in flight.  (Counted by
@@ -915,21 +927,51 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
     // carry both slabs).  Waits counted by the compiler would leave out the
     // A DMA loads and hold each fragment until NAB loads issued after it
     // had landed too (K2 FP8 prefill: 12.24 -> 11.90 ms from exact waits).
+    //
+    // FP8 at 128 rows converts one fragment ahead of the MFMAs: fragment
+    // j + 1 of the first slab while fragment j's MFMAs run, and fragment 0
+    // of the next stage in the second slab, each conversion interleaved
+    // with the MFMAs of its slot.  (Converted right before its own MFMAs,
+    // a fragment's conversions left the matrix pipe idle while they
+    // issued.)  Code j of stage it + 1 is loaded right after code j of
+    // stage it is converted, so the loads keep their order and their
+    // waits keep their counts.
+    constexpr bool PIPE = F8 && BM != 16;
+    uint4 fq0 = make_uint4(0u, 0u, 0u, 0u);  // PIPE: stage's first-slab fragment 0
+    uint4 fh[PIPE ? NB : 1];                 // PIPE: stage's second-slab fragments
+    auto scale = [&](int stage, int j) {
+        const uint32_t v = (EPI == EPI_SWIGLU && j >= NB / 2) ? scu : scg;
+        return __uint_as_float(__builtin_amdgcn_readlane(v, stage >> 1));
+    };
+    auto convert = [&](int stage, int j, uint4& lo, uint4& hi, int kload) {
+        fp8x16_to_bf16(fb[0][j], scale(stage, j), lo, hi);
+        asm volatile("" ::"v"(hi.x), "v"(hi.y), "v"(hi.z), "v"(hi.w) : "memory");
+        fb[0][j] = load_b(kload, 0, j);
+    };
     auto step = [&](int it, auto wait_next, auto first) {
         const int kb = min(it + 1, nkt - 1);
         uint4 fa1[MB];
-        uint4 f1[F8 ? NB : 1];  // FP8: the second slab's converted fragments
+        uint4 f1[F8 && !PIPE ? NB : 1];  // FP8 at 16 rows: the second slab's converted fragments
         float sg = 0.f, su = 0.f;
-        if constexpr (F8) {
+        if constexpr (F8 && !PIPE) {
             sg = __uint_as_float(__builtin_amdgcn_readlane(scg, it >> 1));
             su = EPI == EPI_SWIGLU ? __uint_as_float(__builtin_amdgcn_readlane(scu, it >> 1)) : sg;
         }
+        uint4 fq[PIPE ? NB : 1];
+        fq[0] = fq0;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            if constexpr (F8) {
+            if constexpr (PIPE) {
+                if (j + 1 < NB) {
+                    wait_vmcnt_fenced<decltype(first)::value ? NB - 1 : LOADS - 1>();
+                    convert(it, j + 1, fq[j + 1], fh[j + 1], kb);
+                }
+#pragma unroll
+                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fq[j], fa0[i], acc[i][j]);
+                if (j + 1 < NB) interleave<MB, 8>();
+            } else if constexpr (F8) {
                 uint4 f0;
-                if constexpr (BM != 16) wait_vmcnt_fenced<decltype(first)::value ? NB - 1 : LOADS - 1>();
                 fp8x16_to_bf16(fb[0][j], (EPI == EPI_SWIGLU && j >= NB / 2) ? su : sg, f0, f1[j]);
                 // Both halves are converted before the codes' registers take the
                 // next stage's load (the empty asm uses the second half here, and
@@ -958,7 +1000,15 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            if constexpr (F8) {
+            if constexpr (PIPE) {
+                if (j == 1) {
+                    wait_vmcnt_fenced<LOADS - 1>();
+                    convert(kb, 0, fq0, fh[0], min(it + 2, nkt - 1));
+                }
+#pragma unroll
+                for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(fh[j], fa1[i], acc[i][j]);
+                if (j == 1) interleave<MB, 8>();
+            } else if constexpr (F8) {
 #pragma unroll
                 for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<T>::run(f1[j], fa1[i], acc[i][j]);
             } else {
@@ -980,6 +1030,10 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
     wait_vmcnt<(NST - 1) * NAB + NBL>();  // A(0): younger are A(1..NST-1) and B(0)
     __syncthreads();
     read_a(fa0, 0, fo0);
+    if constexpr (PIPE) {
+        wait_vmcnt_fenced<NB - 1>();  // code 0 of stage 0: younger are codes 1 .. NB - 1
+        convert(0, 0, fq0, fh[0], min(1, nkt - 1));
+    }
     step(0, [] { wait_vmcnt<kWait0>(); }, std::true_type{});
     for (int it = 1; it < nkt; ++it)
         step(it, [it] {
