@@ -880,9 +880,12 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
         return gload16_untracked(m + blk * 1024u, lane * 16);
     };
     // FP8 block scales: lane l holds the exponent of K block l of this
-    // wave's 128-row block (gate and up), placed as the bits of the float
-    // 2^(s - 127); the wave's rows never straddle a 128-row block (n0 is a
-    // multiple of 256, the wave's B rows a 64- or 128-row aligned range).
+    // wave's 128-row block (gate and up), placed as the exponent field of
+    // the float 2^(s - 127); the wave's rows never straddle a 128-row block
+    // (n0 is a multiple of 256, the wave's B rows a 64- or 128-row aligned
+    // range).  Exponent 0 gives the bits of +0.0, which the scaled
+    // conversion reads as 2^-127 like any E8M0 scale (the parity test of
+    // extreme block scales pins both ends of the range).
     uint32_t scg = 0, scu = 0;
     if constexpr (F8) {
         const int kbl = G.seg[0].K / 128;

@@ -293,6 +293,30 @@ def test_forward_fp8_edge_cases(case):
     _full_parity(wl, inp, "fp8 " + case, packed=True)
 
 
+@pytest.mark.parametrize("tiles", ["16-row", "128-row"])
+@pytest.mark.parametrize("exps", [(0, 1, 2), (198, 199, 200)])
+def test_forward_fp8_extreme_block_scales(tiles, exps):
+    # E8M0 exponents at both ends of the range on every down projection
+    # block: 2^-127 .. 2^-125 (exponent 0 is the smallest scale, not zero)
+    # and 2^71 .. 2^73.  Without a shared expert the layer output is the
+    # routed sum alone, so it scales with them and the per-token check
+    # sees a scale decoded wrong.  The down codes are kept at magnitude 8
+    # or more, so every scaled weight stays in bf16's normal range (the
+    # range the library's FP8 contract covers).  The gate and up
+    # projections keep their generated scales.
+    T = 40 if tiles == "16-row" else 600
+    wl = _custom(E=8, K=2, T=T, n_shared=0, F_shared=0, w_dtype="fp8")
+    inp = make_layer_inputs(wl, "cpu", seed=9)
+    g = torch.Generator().manual_seed(9)
+    pick = torch.randint(0, 3, inp["W_down_scale"].shape, generator=g)
+    inp["W_down_scale"] = torch.tensor(exps, dtype=torch.uint8)[pick]
+    c = inp["W_down"].float()
+    c = torch.where(c.abs() < 8, torch.where(c < 0, -8.0, 8.0), c)
+    inp["W_down"] = c.to(torch.float8_e4m3fn)
+    _, _, rel = _full_parity(wl, inp, f"fp8 down scales 2^({exps[0]}-127).. {tiles}", packed=True)
+    assert rel < 2e-2
+
+
 @pytest.mark.parametrize("w_dtype", ["bf16", "fp8"])
 def test_forward_tile_row_buckets(w_dtype):
     # Experts with 1, 15, 16, 17, ... 129, 200 rows: the ragged last 128-row
