@@ -506,6 +506,41 @@ def test_forward_parity_full_size(name, packed):
                  wl.d_latent > 0, st, extra=dict(hist=hist, experts=len(experts)))
 
 
+@pytest.mark.parametrize("packed,w_dtype", [(False, "bf16"), (True, "bf16"), (True, "fp8")])
+def test_forward_past_32bit_offsets(packed, w_dtype):
+    # x [300000, 8192] (2.46e9 elements, 4.9 GB) and the routed outputs
+    # [600000, 8192] (9.8 GB): element offsets past 2^31 and byte offsets
+    # past 2^32 in the row gathers, the stores and the combine.  Sampled
+    # tokens cover every M tile of every expert (the rows past the 32-bit
+    # limits included) plus 256 random ones.
+    wl = _custom(T=300000, d=8192, E=16, K=2, F=128, n_shared=1, F_shared=128, w_dtype=w_dtype)
+    tag = f"{'packed ' if packed else ''}{w_dtype}"
+    log(f"[gpu] past 32-bit offsets ({tag}): generating inputs on the GPU")
+    inp = make_layer_inputs(wl, DEV, seed=21)
+    w = moe.pack_weights(expert_weights(inp), n_shared=wl.n_shared) if packed else None
+    log(f"[gpu] past 32-bit offsets ({tag}): moe_forward")
+    out, r = _run_forward(wl, inp, weights=w)
+    del w
+    x_h, Wr_h, b_h = host(inp["x"]), host(inp["W_r"]), host(inp["b"])
+    log(f"[cpu] oracle router over all {wl.T} tokens")
+    ref = oracle.router(x_h, Wr_h, b_h, wl.K, wl.scale, want_scores=True)
+    idx_eff, w_eff, st = effective_routing(ref, r["idx"].cpu().numpy(), r["w"].cpu().numpy(),
+                                           b_h.numpy(), wl.K, wl.scale)
+    check_dispatch(r, wl.E)
+    toks = coverage_tokens(wl.T, wl.K, r["counts"].cpu().numpy(), r["offsets"].cpu().numpy(),
+                           r["sorted_token"].cpu().numpy(), idx_eff, ref["gap"], bm=128, n_random=256)
+    assert toks.max() >= 2 ** 31 // wl.d  # rows whose x elements lie past 2^31
+    log(f"[cpu] oracle over {len(toks)} tokens")
+    lay = oracle.layer_from_inputs(wl, {k: host(v) if isinstance(v, torch.Tensor) else v
+                                        for k, v in inp.items() if k != "x"})
+    out_ref = oracle.forward_given_routing(lay, x_h[toks], idx_eff[toks], w_eff[toks])
+    got = out[torch.from_numpy(toks).to(DEV)].float().cpu().numpy()
+    del inp, out, r, lay
+    torch.cuda.empty_cache()
+    check_output(f"past 32-bit offsets {tag}", got, out_ref, wl.act_dtype, False, st,
+                 extra=dict(tokens=len(toks)))
+
+
 def test_nan_rows_still_route_to_valid_experts():
     # Unsupported input, but it must not produce invalid expert ids: a NaN
     # score ranks below every number, so each token still selects K
