@@ -25,6 +25,7 @@ a register-only bf16 MFMA loop (with the shader clock it ran at); each
 roofline is also given as a fraction of those measured peaks.
 """
 import argparse
+import dataclasses
 import csv
 import glob
 import hashlib
@@ -673,6 +674,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the profiles/hbm_traffic.md rows of --workload from two rocprofv3 "
                          "--pmc output directories and exit (no GPU use)")
+    ap.add_argument("--sweep", metavar="T1,T2,...",
+                    help="time --workload's layer at these batch sizes (same weights, seeded inputs "
+                         "per size), print one JSON line of the results and exit")
     ap.add_argument("--summarize-sq", metavar="SQ_DIR",
                     help="print the profiles/sq_counters.md rows of --workload from one rocprofv3 "
                          "--pmc output directory and exit (no GPU use)")
@@ -710,6 +714,22 @@ def main():
     rows = make_expert_weights(wl, "cuda:0", seed=args.seed)
     weights = prepare(moe, torch, wl, rows, args.layout)
     torch.cuda.synchronize()
+    if args.sweep:
+        del rows
+        sweep = []
+        for T in (int(t) for t in args.sweep.split(",") if t):
+            swl = dataclasses.replace(wl, T=T, name=f"{wl.name}@T={T}")
+            r = measure_layer(moe, torch, swl, weights, args.steps, args.warmup, args.seed, args.layout)
+            line = dict(T=T, ms=round(r["ms"], 4), tokens_per_s=round(r["value"], 1),
+                        rows_per_expert=round(T * wl.K / wl.E, 2), stages=r["stages"])
+            log(f"[bench] sweep {wl.name} T={T}: {r['ms']:.3f} ms/step, {r['value']:.0f} tokens/s, "
+                f"{line['rows_per_expert']} rows per expert")
+            sweep.append(line)
+            del r
+            torch.cuda.empty_cache()
+        print(json.dumps(dict(workload=wl.name, layout=args.layout, steps=args.steps, warmup=args.warmup,
+                              sweep=sweep)), flush=True)
+        return
     log(f"[bench] timing {wl.name}: warmup {args.warmup}, steps {args.steps}")
     main_r = measure_layer(moe, torch, wl, weights, args.steps, args.warmup, args.seed, args.layout)
     log(f"[bench] {wl.name}: {main_r['ms']:.3f} ms/step, stages {main_r['stages']}")

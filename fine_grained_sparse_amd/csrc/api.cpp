@@ -126,14 +126,23 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
     p.nsplit = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(16, ns)));
     p.ldz = static_cast<int>(up(p.E, 8));
 
-    // Experts: big M tiles once experts average 64 rows or more (the
-    // register-fed WIDE tile on packed weights, the LDS tile otherwise).
+    // Experts: 128-row M tiles once experts average 10 rows or more (the
+    // register-fed WIDE tile on packed weights, the LDS tile otherwise),
+    // 16-row tiles below.  A 16-row tile streams its expert's weights once
+    // per 16 rows, a 128-row tile once per 128, so the small tiles lose as
+    // soon as experts hold a few of them.  Measured on K2 shapes (bf16,
+    // 16-row vs 128-row tiles): 5.78 vs 5.86 ms at 10.7 rows per expert,
+    // 6.91 vs 5.92 at 16, 13.1 vs 6.1 at 43; FP8 3.19 vs 3.13 at 10.7,
+    // 8.28 vs 3.37 at 43; K3 shapes 10.7 vs 10.6 at 9.1, 22.1 vs 10.5 at 37.
     p.packed = forward && D->w_layout == MOE_LAYOUT_FRAG16;
     p.f8 = forward && D->w_dtype == MOE_FP8_E4M3;
     const TileCfg big = p.packed ? TILE_WIDE : TILE_LARGE;
-    p.ecfg = (p.A >= 64ll * p.E && p.dt == DT_BF16) ? big : (p.f8 ? TILE_WIDE16 : TILE_SMALL);
+    p.ecfg = (p.A >= 10ll * p.E && p.dt == DT_BF16) ? big : (p.f8 ? TILE_WIDE16 : TILE_SMALL);
     p.bm = tile_bm(p.ecfg);
-    p.dcfg = (p.T >= 1024 && p.dt == DT_BF16) ? big : TILE_SMALL;
+    // dense maps of the latent form: 128-row tiles from 512 tokens (K3
+    // shapes: 12.5 -> 10.3 ms at 768 tokens with the expert switch above;
+    // below 512 the two measured the same within run-to-run noise)
+    p.dcfg = (p.T >= 512 && p.dt == DT_BF16) ? big : TILE_SMALL;
     p.nch = static_cast<int>(cdiv(p.T, 64));
     p.max_tiles = static_cast<int>(cdiv(p.A, p.bm) + p.E + (p.ns ? cdiv(p.T, p.bm) : 0));
 

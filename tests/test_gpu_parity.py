@@ -216,7 +216,7 @@ def test_forward_parity_every_token(name, packed):
 @pytest.mark.parametrize("case", ["one_token", "K_equals_E", "no_shared", "skewed_few_experts",
                                   "latent_no_shared", "large_tiles", "large_tiles_latent",
                                   "half_tiles", "max_limits", "prefill_k8", "prefill_k6_two_shared",
-                                  "prefill_k16"])
+                                  "prefill_k16", "decode_hot_expert"])
 def test_forward_edge_cases(case, packed):
     if case == "one_token":
         wl = _custom(T=1)
@@ -231,12 +231,12 @@ def test_forward_edge_cases(case, packed):
     elif case == "large_tiles":  # enough rows per expert for the 128-row tiles, ragged tails
         wl = _custom(E=6, K=2, T=700, d=384, F=192, n_shared=2, F_shared=64)
     elif case == "large_tiles_latent":  # 128-row tiles for the experts and the dense
-        # latent maps (T >= 1024), two K segments in the last GEMM, N tails inside a
+        # latent maps (T >= 512), two K segments in the last GEMM, N tails inside a
         # 512-wide tile
         wl = _custom(E=5, K=2, T=1100, d=320, F=192, n_shared=1, F_shared=128, d_latent=192,
                      scale=1.0)
     elif case == "prefill_k8":  # prefill-sized: 128-row expert tiles and 128-row dense tiles
-        # (T >= 1024), a ragged last row tile
+        # (T >= 512), a ragged last row tile
         wl = _custom(E=32, K=8, T=1100, d=256, F=128, n_shared=1, F_shared=128)
     elif case == "prefill_k6_two_shared":  # N tail (d = 320 in 512-column tiles), two shared
         wl = _custom(E=24, K=6, T=1030, d=320, F=128, n_shared=2, F_shared=64)
@@ -245,15 +245,20 @@ def test_forward_edge_cases(case, packed):
     elif case == "max_limits":  # the ABI's limits: 1024 experts, top-16, 8 shared experts,
         # the narrowest widths (64)
         wl = _custom(E=1024, K=16, T=300, d=192, F=64, n_shared=8, F_shared=64)
+    elif case == "decode_hot_expert":  # 6.25 rows per expert on average (16-row tiles,
+        # below the switch at 10), but expert 0 takes all 200 tokens: 13 tiles of it
+        wl = _custom(E=64, K=2, T=200)
     else:  # half_tiles: expert 0 gets four full 128-row tiles + 8 rows, the others ~35
         # rows each: 128-row tiles that are mostly padding
         wl = _custom(E=16, K=2, T=520, d=256, F=128, n_shared=1, F_shared=128)
     inp = make_layer_inputs(wl, "cpu", seed=5)
     if case == "skewed_few_experts":
         inp["b"][:3] = 10.0     # every token picks experts 0, 1, 2; the rest get none
-    if case == "half_tiles":
+    if case in ("half_tiles", "decode_hot_expert"):
         inp["b"][0] = 10.0
     _, r, _ = _full_parity(wl, inp, case, packed=packed)
+    if case == "decode_hot_expert":
+        assert r["counts"].cpu().numpy()[0] == 200 and wl.T * wl.K < 10 * wl.E
     if case == "skewed_few_experts":
         c = r["counts"].cpu().numpy()
         assert c[:3].tolist() == [200, 200, 200] and c[3:].sum() == 0
@@ -263,9 +268,10 @@ def test_forward_edge_cases(case, packed):
 
 
 @pytest.mark.parametrize("case", ["one_token", "K_equals_E", "no_shared", "latent_no_shared",
-                                  "large_tiles", "large_tiles_latent", "half_tiles", "prefill_k8"])
+                                  "large_tiles", "large_tiles_latent", "half_tiles", "prefill_k8",
+                                  "decode_hot_expert"])
 def test_forward_fp8_edge_cases(case):
-    # FP8 routed experts (packed): 16-row tiles below 64 rows per expert on
+    # FP8 routed experts (packed): 16-row tiles below 10 rows per expert on
     # average, 128-row tiles above; the shared experts and latent maps run
     # as bf16 launches of their own.  Block-scale rows past N (down
     # projections narrower than the 512-row tile) are clamped.
@@ -285,10 +291,12 @@ def test_forward_fp8_edge_cases(case):
                      scale=1.0, **fp8)
     elif case == "prefill_k8":  # prefill-sized tiles, top-8
         wl = _custom(E=32, K=8, T=1100, d=256, F=128, n_shared=1, F_shared=128, **fp8)
+    elif case == "decode_hot_expert":  # 16-row tiles, expert 0 in 13 of them
+        wl = _custom(E=64, K=2, T=200, **fp8)
     else:  # half_tiles: expert 0 takes every token, the others ~35 rows each
         wl = _custom(E=16, K=2, T=520, **fp8)
     inp = make_layer_inputs(wl, "cpu", seed=6)
-    if case == "half_tiles":
+    if case in ("half_tiles", "decode_hot_expert"):
         inp["b"][0] = 10.0
     _full_parity(wl, inp, "fp8 " + case, packed=True)
 
