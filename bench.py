@@ -708,6 +708,17 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     wl = get_workload(args.workload)
+    if wl.router_only and args.sweep:
+        sweep = []
+        for T in (int(t) for t in args.sweep.split(",") if t):
+            swl = dataclasses.replace(wl, T=T, name=f"{wl.name}@T={T}")
+            r, _ = measure_router(moe, torch, swl, max(args.steps, 100), args.warmup, args.seed)
+            log(f"[bench] sweep {wl.name} T={T}: {r['ms_per_step']:.4f} ms/step, {r['value']:.0f} tokens/s")
+            sweep.append(dict(T=T, ms=r["ms_per_step"], tokens_per_s=r["value"]))
+            torch.cuda.empty_cache()
+        print(json.dumps(dict(workload=wl.name, steps=max(args.steps, 100), warmup=args.warmup, sweep=sweep)),
+              flush=True)
+        return
     if wl.router_only:
         sys.exit("choose a whole-layer workload")
     log(f"[bench] generating weights for {wl.name} on the GPU")
