@@ -1099,8 +1099,17 @@ __global__ __launch_bounds__(256, BM >= 64 ? 1 : 2) void k_gemm_wide(const GemmA
 
 // fp32 operands: register-staged 16 x 256 tiles
 constexpr int kF32BN = 256;
-// decode tile (few rows per expert): 16 x 512, two stages of 128-byte row pieces
-constexpr int kSmBM = 16, kSmBN = 512, kSmWM = 1, kSmWN = 4, kSmNST = 2, kSmROWB = 128;
+// decode tile (few rows per expert): 16 x 512.  bf16 output (expert and
+// dense GEMMs): a ring of four slots of 64-byte row pieces, three stages
+// (99 KiB) in flight.  A workgroup walks its whole K in sequence, and with
+// few workgroups per CU (small batches) the latency of each stage is the
+// cost: against two slots of 128-byte pieces (one 66 KiB stage in flight),
+// K2 layer 0.36 -> 0.32 ms at 1 token, 5.37 -> 5.19-5.28 ms at 256, 5.43 ->
+// 5.17-5.30 ms at 384; K3 shapes 4-5% at 32-256 tokens.  fp32 output (the
+// router logits of up to 64 tokens): two slots of 128-byte pieces, 7%
+// faster there than four.
+constexpr int kSmBM = 16, kSmBN = 512, kSmWM = 1, kSmWN = 4;
+constexpr int kSmNST = 4, kSmROWB = 64, kSmNST32 = 2, kSmROWB32 = 128;
 // prefill tile: BM x BN (B rows), waves WM x WN, NST LDS stages
 constexpr int kBigBM = 128, kBigBN = 256, kBigWM = 2, kBigWN = 2, kBigNST = 3, kBigROWB = 64;
 // router logits tile: 128 x 192 (E = 384 is two whole N tiles, where 256
@@ -1174,11 +1183,12 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
             else
                 hipLaunchKernelGGL((k_gemm_wide<TC, EPI, 2, kWideBM, false>), grid, dim3(256), 0, stream, a);
         } else if (cfg == TILE_SMALL) {
+            constexpr int nst = sizeof(TC) == 4 ? kSmNST32 : kSmNST, rowb = sizeof(TC) == 4 ? kSmROWB32 : kSmROWB;
             if (packed)
-                hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, kSmNST, kSmROWB, EPI, true>), grid,
+                hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, nst, rowb, EPI, true>), grid,
                                    dim3(64 * kSmWM * kSmWN), 0, stream, a);
             else
-                hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, kSmNST, kSmROWB, EPI, false>), grid,
+                hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, nst, rowb, EPI, false>), grid,
                                    dim3(64 * kSmWM * kSmWN), 0, stream, a);
         } else if (cfg == TILE_ROUTER) {
             if constexpr (EPI == EPI_STORE)
