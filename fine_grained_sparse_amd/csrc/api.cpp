@@ -138,6 +138,14 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
     p.f8 = forward && D->w_dtype == MOE_FP8_E4M3;
     const TileCfg big = p.packed ? TILE_WIDE : TILE_LARGE;
     p.ecfg = (p.A >= 10ll * p.E && p.dt == DT_BF16) ? big : (p.f8 ? TILE_WIDE16 : TILE_SMALL);
+    // ... at 16 x 256 when the 512-wide 16-row tiles would make fewer than
+    // 128 workgroups (at most one tile per assignment, plus the shared rows'
+    // tiles, times the N tiles of the wider of the two expert GEMMs)
+    if (p.ecfg == TILE_SMALL && p.dt == DT_BF16) {
+        const int64_t mt = std::min<int64_t>(p.A, p.E) + (p.ns ? cdiv(p.T, 16) : 0);
+        const int64_t nt = std::max<int64_t>(cdiv(std::max(p.F, p.Fsh), 256), cdiv(p.din, 512));
+        if (mt * nt < 128) p.ecfg = TILE_NARROW;
+    }
     p.bm = tile_bm(p.ecfg);
     // dense maps of the latent form: 128-row tiles from 512 tokens (K3
     // shapes: 12.5 -> 10.3 ms at 768 tokens with the expert switch above;

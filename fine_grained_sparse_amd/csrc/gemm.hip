@@ -1110,6 +1110,14 @@ constexpr int kF32BN = 256;
 // faster there than four.
 constexpr int kSmBM = 16, kSmBN = 512, kSmWM = 1, kSmWN = 4;
 constexpr int kSmNST = 4, kSmROWB = 64, kSmNST32 = 2, kSmROWB32 = 128;
+// 256-wide form: twice the workgroups, each streaming half the bytes, for
+// launches of too few 512-wide workgroups to fill the chip (each walks its
+// whole K in sequence).  K2 layer at 1 token: up 0.167 -> 0.098 ms, the
+// layer 0.30-0.32 -> 0.24 ms; at 2-4 tokens the 512-wide tiles already
+// make 136-264 workgroups and measured the same or 3% better.  The router
+// logits of up to 64 tokens always take it (E = 384 fills 1.5 of them
+// instead of 0.75 of one; 0.046 -> 0.039 ms at 1 token).
+constexpr int kNarBN = 256;
 // prefill tile: BM x BN (B rows), waves WM x WN, NST LDS stages
 constexpr int kBigBM = 128, kBigBN = 256, kBigWM = 2, kBigWN = 2, kBigNST = 3, kBigROWB = 64;
 // router logits tile: 128 x 192 (E = 384 is two whole N tiles, where 256
@@ -1125,10 +1133,13 @@ constexpr int kWideBM = 128, kWideBN = 512;
 
 static_assert(kSmBM == 16, "fp32 small tiles share the 16-row M tiling");
 static_assert(kBigBM == kWideBM, "prefill tiles share the tile table's 128-row M tiling");
-int tile_bm(TileCfg cfg) { return (cfg == TILE_SMALL || cfg == TILE_WIDE16) ? kSmBM : kBigBM; }
+int tile_bm(TileCfg cfg) {
+    return (cfg == TILE_SMALL || cfg == TILE_WIDE16 || cfg == TILE_NARROW) ? kSmBM : kBigBM;
+}
 int tile_bn_out(TileCfg cfg, Epi epi) {  // bf16 kernels (sizing heuristics only)
     // B rows per N tile (gate + up rows for SwiGLU)
     const int bn = cfg == TILE_SMALL ? kSmBN
+                   : cfg == TILE_NARROW ? kNarBN
                    : (cfg == TILE_WIDE || cfg == TILE_WIDE16) ? kWideBN
                    : cfg == TILE_ROUTER ? kRtBN : kBigBN;
     return epi == EPI_SWIGLU ? bn / 2 : bn;
@@ -1164,10 +1175,12 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
     if (cfg == TILE_ROUTER && (packed || EPI != EPI_STORE)) return hipErrorInvalidValue;
     if (cfg == TILE_WIDE && !(packed && wide_fits(args))) cfg = TILE_LARGE;
     if (cfg == TILE_WIDE16) cfg = TILE_SMALL;  // bf16 decode: the LDS tile streams slightly faster
+    if (cfg == TILE_SMALL && sizeof(TC) == 4) cfg = TILE_NARROW;  // the router logits (fp32 out)
     const bool wide = cfg == TILE_WIDE;
     // output columns per N tile of the kernel actually launched
     const int bn = sizeof(T) == 4 ? kF32BN
                    : cfg == TILE_SMALL ? kSmBN
+                   : cfg == TILE_NARROW ? kNarBN
                    : wide ? kWideBN
                    : cfg == TILE_ROUTER ? kRtBN : kBigBN;
     const int bno = EPI == EPI_SWIGLU ? bn / 2 : bn;
@@ -1182,14 +1195,23 @@ hipError_t launch_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n,
                 hipLaunchKernelGGL((k_gemm_wide<TC, EPI, 1, kWideBM, false>), grid, dim3(256), 0, stream, a);
             else
                 hipLaunchKernelGGL((k_gemm_wide<TC, EPI, 2, kWideBM, false>), grid, dim3(256), 0, stream, a);
-        } else if (cfg == TILE_SMALL) {
+        } else if (cfg == TILE_SMALL || cfg == TILE_NARROW) {
             constexpr int nst = sizeof(TC) == 4 ? kSmNST32 : kSmNST, rowb = sizeof(TC) == 4 ? kSmROWB32 : kSmROWB;
-            if (packed)
-                hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, nst, rowb, EPI, true>), grid,
-                                   dim3(64 * kSmWM * kSmWN), 0, stream, a);
-            else
-                hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, nst, rowb, EPI, false>), grid,
-                                   dim3(64 * kSmWM * kSmWN), 0, stream, a);
+            if (cfg == TILE_NARROW) {
+                if (packed)
+                    hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kNarBN, kSmWM, kSmWN, nst, rowb, EPI, true>), grid,
+                                       dim3(64 * kSmWM * kSmWN), 0, stream, a);
+                else
+                    hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kNarBN, kSmWM, kSmWN, nst, rowb, EPI, false>), grid,
+                                       dim3(64 * kSmWM * kSmWN), 0, stream, a);
+            } else if constexpr (sizeof(TC) == 2) {
+                if (packed)
+                    hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, nst, rowb, EPI, true>), grid,
+                                       dim3(64 * kSmWM * kSmWN), 0, stream, a);
+                else
+                    hipLaunchKernelGGL((k_gemm_big<TC, kSmBM, kSmBN, kSmWM, kSmWN, nst, rowb, EPI, false>), grid,
+                                       dim3(64 * kSmWM * kSmWN), 0, stream, a);
+            }
         } else if (cfg == TILE_ROUTER) {
             if constexpr (EPI == EPI_STORE)
                 hipLaunchKernelGGL((k_gemm_big<TC, kBigBM, kRtBN, kBigWM, kBigWN, kRtNST, kRtROWB, EPI, false>), grid,

@@ -16,8 +16,9 @@ enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1 };
 // WIDE16 is the register-fed tile at 16 rows (FP8 decode; bf16 decode runs
 // SMALL).  ROUTER is the LDS tile at 128 x 192 for the router logits, in
 // 128-byte row pieces and two stages (unpacked fp32-out store only): 384
-// experts fill two N tiles exactly.
-enum TileCfg { TILE_SMALL = 0, TILE_LARGE = 1, TILE_WIDE = 2, TILE_WIDE16 = 3, TILE_ROUTER = 4 };
+// experts fill two N tiles exactly.  NARROW is SMALL at 16 x 256, for
+// batches so small that the 512-wide tiles would leave most CUs idle.
+enum TileCfg { TILE_SMALL = 0, TILE_LARGE = 1, TILE_WIDE = 2, TILE_WIDE16 = 3, TILE_ROUTER = 4, TILE_NARROW = 5 };
 
 int tile_bm(TileCfg cfg);         // rows per M tile
 int tile_bn_out(TileCfg cfg, Epi epi);  // output columns per N tile

@@ -216,7 +216,7 @@ def test_forward_parity_every_token(name, packed):
 @pytest.mark.parametrize("case", ["one_token", "K_equals_E", "no_shared", "skewed_few_experts",
                                   "latent_no_shared", "large_tiles", "large_tiles_latent",
                                   "half_tiles", "max_limits", "prefill_k8", "prefill_k6_two_shared",
-                                  "prefill_k16", "decode_hot_expert"])
+                                  "prefill_k16", "decode_hot_expert", "narrow_hot_expert"])
 def test_forward_edge_cases(case, packed):
     if case == "one_token":
         wl = _custom(T=1)
@@ -246,7 +246,11 @@ def test_forward_edge_cases(case, packed):
         # the narrowest widths (64)
         wl = _custom(E=1024, K=16, T=300, d=192, F=64, n_shared=8, F_shared=64)
     elif case == "decode_hot_expert":  # 6.25 rows per expert on average (16-row tiles,
-        # below the switch at 10), but expert 0 takes all 200 tokens: 13 tiles of it
+        # below the switch at 10), but expert 0 takes all 200 tokens: 13 tiles of it;
+        # 512-wide tiles (154 workgroups or more)
+        wl = _custom(E=64, K=2, T=200, d=1024, F=512, F_shared=512)
+    elif case == "narrow_hot_expert":  # the same routing at d = 256, F = 128: the
+        # 512-wide tiles would make 77 workgroups, so the 16 x 256 ones serve it
         wl = _custom(E=64, K=2, T=200)
     else:  # half_tiles: expert 0 gets four full 128-row tiles + 8 rows, the others ~35
         # rows each: 128-row tiles that are mostly padding
@@ -254,10 +258,10 @@ def test_forward_edge_cases(case, packed):
     inp = make_layer_inputs(wl, "cpu", seed=5)
     if case == "skewed_few_experts":
         inp["b"][:3] = 10.0     # every token picks experts 0, 1, 2; the rest get none
-    if case in ("half_tiles", "decode_hot_expert"):
+    if case in ("half_tiles", "decode_hot_expert", "narrow_hot_expert"):
         inp["b"][0] = 10.0
     _, r, _ = _full_parity(wl, inp, case, packed=packed)
-    if case == "decode_hot_expert":
+    if case in ("decode_hot_expert", "narrow_hot_expert"):
         assert r["counts"].cpu().numpy()[0] == 200 and wl.T * wl.K < 10 * wl.E
     if case == "skewed_few_experts":
         c = r["counts"].cpu().numpy()
