@@ -110,7 +110,7 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
     p.dt = D->act_dtype == MOE_BF16 ? DT_BF16 : DT_F32;
     p.es = p.dt == DT_BF16 ? 2 : 4;
 
-    // Router: 16-row tiles for tiny batches, else 128 x 192 (each M tile
+    // Router: 16-row tiles (16 x 256) for tiny batches, else 128 x 192 (each M tile
     // streams the W_r planes once, so fewer, taller tiles read less); split
     // K until about 512 workgroups (two per CU) are in flight, keeping at
     // least 8 K steps each.  Each split writes, and the gate reads back, a
