@@ -770,12 +770,19 @@ __device__ __forceinline__ void store_direct(const f32x4 (&acc)[MB][NB], const G
     }
 }
 
+// B rows per N tile of the register-fed tile: 512, and 256 for the 16-row
+// (FP8 decode) kernel, where twice the workgroups each stream half the
+// bytes (K2 FP8 layer 0.211-0.215 -> 0.204-0.205 ms at 1 token, 2.83 ->
+// 2.76-2.79 ms at 256).  The ragged bodies of the 128-row kernel (32, 64
+// rows) keep its 512.
+constexpr int wide_bn(int bm) { return bm == 16 ? 256 : 512; }
+
 template <typename TC, int EPI, int NSEG, int BM, bool F8>
 __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char* lds) {
     using T = bf16_t;
     static_assert(BM % 16 == 0 && BM <= 128 && (BM * 128 / 1024 < 4 || BM * 128 / 1024 % 4 == 0), "row tiles");
     static_assert(!F8 || NSEG == 1, "FP8 weights: one K segment");
-    constexpr int ES = 2, BN = 512, NW = 4, TN = BN / NW;
+    constexpr int ES = 2, BN = wide_bn(BM), NW = 4, TN = BN / NW;
     constexpr int WES = F8 ? 1 : 2;            // bytes per weight element
     constexpr int MB = BM / 16, NB = TN / 16;
     constexpr int ROWB = 128, BKE = ROWB / ES;  // a stage is 64 K = two 32-K slabs
@@ -882,8 +889,8 @@ __device__ __forceinline__ void wide_tile(const GemmArgs& a, const Job& jb, char
     // FP8 block scales: lane l holds the exponent of K block l of this
     // wave's 128-row block (gate and up), placed as the exponent field of
     // the float 2^(s - 127); the wave's rows never straddle a 128-row block
-    // (n0 is a multiple of 256, the wave's B rows a 64- or 128-row aligned
-    // range).  Exponent 0 gives the bits of +0.0, which the scaled
+    // (n0 is a multiple of 128, the wave's B rows an aligned range of 32 to
+    // 128 rows).  Exponent 0 gives the bits of +0.0, which the scaled
     // conversion reads as 2^-127 like any E8M0 scale (the parity test of
     // extreme block scales pins both ends of the range).
     uint32_t scg = 0, scu = 0;
@@ -1077,7 +1084,7 @@ __device__ __forceinline__ void wide_group(const GemmArgs& a, const Job& jb, cha
 template <typename TC, int EPI, int NSEG, int BM, bool F8>
 __global__ __launch_bounds__(256, BM >= 64 ? 1 : 2) void k_gemm_wide(const GemmArgs a) {
     __shared__ __attribute__((aligned(1024))) char lds[wide_lds_bytes<BM>()];
-    constexpr int BNO = EPI == EPI_SWIGLU ? 256 : 512;
+    constexpr int BNO = EPI == EPI_SWIGLU ? wide_bn(BM) / 2 : wide_bn(BM);
     Job jb;
     if (!pick_job<BM, BNO>(a, jb)) return;
     if constexpr (BM == 128) {
@@ -1127,7 +1134,7 @@ constexpr int kBigBM = 128, kBigBN = 256, kBigWM = 2, kBigWN = 2, kBigNST = 3, k
 // 0.134 ms at 4096, K3's 896 experts 0.27 -> 0.23 ms.
 constexpr int kRtBN = 192, kRtNST = 2, kRtROWB = 128;
 // prefill expert tile with register-fed weights: 128 x 512
-constexpr int kWideBM = 128, kWideBN = 512;
+constexpr int kWideBM = 128, kWideBN = wide_bn(kWideBM), kWide16BN = wide_bn(16);
 
 }  // namespace
 
@@ -1140,7 +1147,8 @@ int tile_bn_out(TileCfg cfg, Epi epi) {  // bf16 kernels (sizing heuristics only
     // B rows per N tile (gate + up rows for SwiGLU)
     const int bn = cfg == TILE_SMALL ? kSmBN
                    : cfg == TILE_NARROW ? kNarBN
-                   : (cfg == TILE_WIDE || cfg == TILE_WIDE16) ? kWideBN
+                   : cfg == TILE_WIDE ? kWideBN
+                   : cfg == TILE_WIDE16 ? kWide16BN
                    : cfg == TILE_ROUTER ? kRtBN : kBigBN;
     return epi == EPI_SWIGLU ? bn / 2 : bn;
 }
@@ -1246,7 +1254,8 @@ template <int EPI>
 hipError_t launch_f8_t(const GemmArgs& args, TileCfg cfg, int max_tiles, int max_n, hipStream_t stream) {
     if ((cfg != TILE_WIDE && cfg != TILE_WIDE16) || !wide_f8_fits(args, static_cast<Epi>(EPI)))
         return hipErrorInvalidValue;
-    constexpr int bno = EPI == EPI_SWIGLU ? kWideBN / 2 : kWideBN;
+    const int bn = cfg == TILE_WIDE ? kWideBN : kWide16BN;
+    const int bno = EPI == EPI_SWIGLU ? bn / 2 : bn;
     GemmArgs a = args;
     a.ntn = (max_n + bno - 1) / bno;
     const dim3 grid(job_blocks(max_tiles, a.ntn), 1, 1);

@@ -13,7 +13,7 @@ enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1 };
 // per expert (decode-sized batches); LARGE (128 x 256, both operands through
 // LDS) and WIDE (128 x 512, weights fed to registers) are the prefill tiles.
 // All bf16 prefill tiles are 128 rows, so one tile table serves both.
-// WIDE16 is the register-fed tile at 16 rows (FP8 decode; bf16 decode runs
+// WIDE16 is the register-fed tile at 16 x 256 (FP8 decode; bf16 decode runs
 // SMALL).  ROUTER is the LDS tile at 128 x 192 for the router logits, in
 // 128-byte row pieces and two stages (unpacked fp32-out store only): 384
 // experts fill two N tiles exactly.  NARROW is SMALL at 16 x 256, for

@@ -273,12 +273,13 @@ def test_forward_edge_cases(case, packed):
 
 @pytest.mark.parametrize("case", ["one_token", "K_equals_E", "no_shared", "latent_no_shared",
                                   "large_tiles", "large_tiles_latent", "half_tiles", "prefill_k8",
-                                  "decode_hot_expert"])
+                                  "decode_hot_expert", "decode_ragged_n"])
 def test_forward_fp8_edge_cases(case):
     # FP8 routed experts (packed): 16-row tiles below 10 rows per expert on
-    # average, 128-row tiles above; the shared experts and latent maps run
-    # as bf16 launches of their own.  Block-scale rows past N (down
-    # projections narrower than the 512-row tile) are clamped.
+    # average, 128-row tiles above; the shared experts ride in the same
+    # launches as a bf16 group, the latent maps run as bf16 launches of
+    # their own.  Block-scale rows past N (down projections narrower than
+    # the tile's weight rows) are clamped.
     fp8 = dict(w_dtype="fp8")
     if case == "one_token":
         wl = _custom(T=1, **fp8)
@@ -297,6 +298,10 @@ def test_forward_fp8_edge_cases(case):
         wl = _custom(E=32, K=8, T=1100, d=256, F=128, n_shared=1, F_shared=128, **fp8)
     elif case == "decode_hot_expert":  # 16-row tiles, expert 0 in 13 of them
         wl = _custom(E=64, K=2, T=200, **fp8)
+    elif case == "decode_ragged_n":  # 16-row tiles (256 weight rows, 128 SwiGLU columns):
+        # up F = 384 in three N tiles, down d = 640 in two and a half,
+        # the shared expert's F = 192 in one and a half
+        wl = _custom(E=32, K=2, T=100, d=640, F=384, F_shared=192, **fp8)
     else:  # half_tiles: expert 0 takes every token, the others ~35 rows each
         wl = _custom(E=16, K=2, T=520, **fp8)
     inp = make_layer_inputs(wl, "cpu", seed=6)
