@@ -276,3 +276,42 @@ def coverage_tokens(T, K, counts, offsets, sorted_token, idx_eff, gap, bm=128, n
             if not mask[c:c + bm].any():
                 take(int(rng.integers(c, min(c + bm, T))))
     return np.array(sorted(chosen), np.int64)
+
+
+RANDOM_LAYER_SEEDS = range(96)
+_RANDOM_MODES = ("bf16", "packed", "fp8", "f32")  # activations / weights of a drawn layer
+
+
+def random_layer(seed):
+    """A seeded random layer shape within the C ABI's limits, small enough for
+    the oracle to finish in about a second: E from 1 to 1024, K from 1 to
+    min(E, 16), T log-uniform over 1..1500 (so rows per expert fall on both
+    sides of the switch between 16-row and 128-row expert tiles, and latent
+    layers on both sides of the dense maps' switch), up to 8 shared experts,
+    sometimes one hot expert (bias raised, so it takes every token).  Modes
+    cycle with the seed: bf16 rows, bf16 packed, FP8 packed (sizes in whole
+    128 x 128 scale blocks), fp32 rows.  Returns (Workload kwargs, packed,
+    hot expert or None)."""
+    rng = np.random.default_rng(7919 + seed)
+    mode = _RANDOM_MODES[seed % len(_RANDOM_MODES)]
+    q = 128 if mode == "fp8" else 64
+    while True:
+        E = int(rng.choice([1, 2, 5, 8, 16, 33, 64, 100, 257, 384, 1024]))
+        K = int(rng.integers(1, min(E, 16) + 1))
+        T = max(1, int(np.exp(rng.uniform(0.0, np.log(1500.0)))))
+        d_latent = 0 if rng.random() < 0.6 else q * int(rng.integers(1, 384 // q + 1))
+        d = (q if d_latent == 0 else 64) * int(rng.integers(1, 640 // (q if d_latent == 0 else 64) + 1))
+        din = d_latent or d
+        F = q * int(rng.integers(1, 512 // q + 1))
+        n_shared = int(rng.choice([0, 1, 1, 2, 3, 8]))
+        F_shared = 64 * int(rng.integers(1, 5)) if n_shared else 0
+        flops = 6.0 * T * (K * din * F + n_shared * F_shared * d) + (4.0 * T * d * d_latent)
+        if flops <= 2.5e10 and 3 * E * F * din <= 4e7 and (mode != "f32" or flops <= 3e9):
+            break
+    hot = int(rng.integers(0, E)) if rng.random() < 0.25 else None
+    kw = dict(name=f"random{seed}_{mode}", T=T, d=d, E=E, K=K, F=F, n_shared=n_shared,
+              F_shared=F_shared, d_latent=d_latent, scale=float(rng.uniform(0.5, 3.0)),
+              act_dtype="f32" if mode == "f32" else "bf16",
+              w_dtype={"f32": "f32", "fp8": "fp8"}.get(mode, "bf16"), bias_range=0.02,
+              zipf_skew=bool(rng.random() < 0.5), router_only=False)
+    return kw, mode in ("packed", "fp8"), hot

@@ -10,9 +10,9 @@ import torch
 import fine_grained_sparse_amd as moe
 import oracle
 from moe_inputs import Workload, get_workload, make_layer_inputs, make_router_inputs
-from parity import (TIE, check_dispatch, check_output, coverage_tokens, effective_routing,
-                    effective_routing_grouped, expert_weights, host, log, record_routing,
-                    weights_to_device)
+from parity import (RANDOM_LAYER_SEEDS, TIE, check_dispatch, check_output, coverage_tokens,
+                    effective_routing, effective_routing_grouped, expert_weights, host, log,
+                    random_layer, record_routing, weights_to_device)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -308,6 +308,23 @@ def test_forward_fp8_edge_cases(case):
     if case in ("half_tiles", "decode_hot_expert"):
         inp["b"][0] = 10.0
     _full_parity(wl, inp, "fp8 " + case, packed=True)
+
+
+@pytest.mark.parametrize("seed", list(RANDOM_LAYER_SEEDS))
+def test_forward_random_layers(seed):
+    # Seeded random layers within the ABI's limits (random_layer in
+    # tests/parity.py): every token against the oracle, whichever tiles the
+    # planner picks for the drawn shape and batch.
+    kw, packed, hot = random_layer(seed)
+    wl = Workload(**kw)
+    inp = make_layer_inputs(wl, "cpu", seed=100 + seed)
+    if hot is not None:
+        inp["b"][hot] = 10.0  # every token selects it
+    note = (f"F={wl.F} shared={wl.n_shared}x{wl.F_shared} d_latent={wl.d_latent} "
+            f"{wl.act_dtype}/{wl.w_dtype}" + (f" hot={hot}" if hot is not None else ""))
+    _, r, _ = _full_parity(wl, inp, note, packed=packed)
+    if hot is not None:
+        assert r["counts"].cpu().numpy()[hot] == wl.T
 
 
 @pytest.mark.parametrize("tiles", ["16-row", "128-row"])

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import RESULTS, TIE, check_output, coverage_tokens
+from parity import RANDOM_LAYER_SEEDS, RESULTS, TIE, check_output, coverage_tokens, random_layer
 
 
 def _routing(T, E, K, seed, skew=0.5):
@@ -65,3 +65,36 @@ def test_check_output_catches_local_mistakes():
 
 def test_tie_threshold_is_the_stated_one():
     assert TIE == 1e-5
+
+
+def test_random_layers_span_the_tile_regimes():
+    # The seeded random layers of the GPU parity test fall on both sides of
+    # each batch-size switch: 16-row and 128-row expert tiles (below and from
+    # 10 rows per expert on average) for bf16 rows, packed bf16 and FP8;
+    # single tokens; latent layers below and from 512 tokens; hot experts;
+    # no and eight shared experts; fp32 and bf16 activations.  All within
+    # the ABI's limits.
+    draws = [random_layer(s) for s in RANDOM_LAYER_SEEDS]
+
+    def has(pred):
+        return any(pred(kw, packed, hot) for kw, packed, hot in draws)
+
+    def rows(kw):
+        return kw["T"] * kw["K"] / kw["E"]
+
+    for w, pk in (("bf16", False), ("bf16", True), ("fp8", True)):
+        assert has(lambda kw, p, h: kw["w_dtype"] == w and p == pk and rows(kw) >= 10), (w, pk)
+        assert has(lambda kw, p, h: kw["w_dtype"] == w and p == pk and rows(kw) < 10), (w, pk)
+    assert has(lambda kw, p, h: kw["T"] == 1)
+    assert has(lambda kw, p, h: kw["d_latent"] > 0 and kw["T"] >= 512)
+    assert has(lambda kw, p, h: kw["d_latent"] > 0 and kw["T"] < 512)
+    assert has(lambda kw, p, h: h is not None)
+    assert has(lambda kw, p, h: kw["n_shared"] == 0) and has(lambda kw, p, h: kw["n_shared"] == 8)
+    assert {kw["act_dtype"] for kw, _, _ in draws} == {"bf16", "f32"}
+    for kw, packed, hot in draws:
+        assert 1 <= kw["K"] <= min(kw["E"], 16) and kw["E"] <= 1024 and kw["T"] >= 1
+        assert kw["d"] % 64 == 0 and kw["F"] % 64 == 0 and kw["d_latent"] % 64 == 0
+        assert kw["n_shared"] <= 8 and kw["F_shared"] % 64 == 0
+        if kw["w_dtype"] == "fp8":
+            assert packed and (kw["d_latent"] or kw["d"]) % 128 == 0 and kw["F"] % 128 == 0
+        assert hot is None or 0 <= hot < kw["E"]
