@@ -315,3 +315,40 @@ def random_layer(seed):
               w_dtype={"f32": "f32", "fp8": "fp8"}.get(mode, "bf16"), bias_range=0.02,
               zipf_skew=bool(rng.random() < 0.5), router_only=False)
     return kw, mode in ("packed", "fp8"), hot
+
+
+RANDOM_ROUTER_SEEDS = range(64)
+
+
+def random_router(seed):
+    """A seeded random router shape within the C ABI's limits: E from 1 to
+    1024, K up to min(E, 16), T log-uniform over 1..16384 (both the 16-row
+    and the 128 x 192 logit tiles, one to sixteen split-K planes), d in
+    64-steps up to 4096, fp32 or bf16 activations, a wider bias range in a
+    third of them, and in a third group-limited choice (n_group a divisor of
+    E with at least two experts per group, any topk_group; K may exceed the
+    kept groups' experts, so that the masked scores are chosen too).
+    T·E·d stays under 4e9 for the oracle.  Returns (Workload kwargs,
+    n_group, topk_group)."""
+    rng = np.random.default_rng(104729 + seed)
+    while True:
+        E = int(rng.choice([1, 2, 3, 8, 24, 64, 100, 256, 384, 512, 896, 1024]))
+        K = int(rng.integers(1, min(E, 16) + 1))
+        T = max(1, int(np.exp(rng.uniform(0.0, np.log(16384.0)))))
+        d = 64 * int(rng.integers(1, 65))
+        if T * E * d <= 4e9:
+            break
+    n_group, topk_group = 1, 1
+    groups = [g for g in range(2, 65) if E % g == 0 and E // g >= 2]
+    if groups and rng.random() < 1 / 3:
+        if rng.random() < 1 / 3:  # two experts per group, one group kept
+            n_group, topk_group = max(groups), 1
+        else:
+            n_group = int(rng.choice(groups))
+            topk_group = int(rng.integers(1, n_group + 1))
+    act = "f32" if rng.random() < 0.25 else "bf16"
+    kw = dict(name=f"router{seed}", T=T, d=d, E=E, K=K, F=64, n_shared=0, F_shared=0,
+              d_latent=0, scale=float(rng.uniform(0.5, 3.0)), act_dtype=act, w_dtype=act,
+              bias_range=float(rng.choice([0.02, 0.02, 0.5])), zipf_skew=bool(rng.random() < 0.5),
+              router_only=True)
+    return kw, n_group, topk_group

@@ -10,9 +10,9 @@ import torch
 import fine_grained_sparse_amd as moe
 import oracle
 from moe_inputs import Workload, get_workload, make_layer_inputs, make_router_inputs
-from parity import (RANDOM_LAYER_SEEDS, TIE, check_dispatch, check_output, coverage_tokens,
-                    effective_routing, effective_routing_grouped, expert_weights, host, log,
-                    random_layer, record_routing, weights_to_device)
+from parity import (RANDOM_LAYER_SEEDS, RANDOM_ROUTER_SEEDS, TIE, check_dispatch, check_output,
+                    coverage_tokens, effective_routing, effective_routing_grouped, expert_weights,
+                    host, log, random_layer, random_router, record_routing, weights_to_device)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -134,6 +134,33 @@ def test_router_grouped_parity(name, T, n_group, topk_group, bias):
     record_routing(f"grouped router {name} T={T or wl.T} {n_group}/{topk_group}"
                    f"{' neg-bias' if bias is not None else ''}", st, T or wl.T)
     assert st["near_tie"] <= max(3, (T or wl.T) // 100)
+
+
+@pytest.mark.parametrize("seed", list(RANDOM_ROUTER_SEEDS))
+def test_router_random_shapes(seed):
+    # Seeded random router shapes within the ABI's limits (random_router in
+    # tests/parity.py), with and without the group-limited choice.
+    kw, n_group, topk_group = random_router(seed)
+    wl = Workload(**kw)
+    log(f"[gpu] router {wl.name} T={wl.T} d={wl.d} E={wl.E} K={wl.K} {wl.act_dtype} "
+        f"groups {n_group}/{topk_group}")
+    r = make_router_inputs(wl, "cpu", seed=200 + seed)
+    dev = weights_to_device(r, DEV)
+    idx, w, counts = moe.router(dev["x"], dev["W_r"], dev["b"], wl.K, wl.scale, n_group=n_group,
+                                topk_group=topk_group)
+    torch.cuda.synchronize()
+    gi, gw = idx.cpu().numpy(), w.cpu().numpy()
+    if n_group > 1:
+        ref = oracle.router_grouped(r["x"], r["W_r"], r["b"], wl.K, wl.scale, n_group, topk_group,
+                                    want_scores=True)
+        _, _, st = effective_routing_grouped(ref, gi, gw, wl.K, wl.scale)
+    else:
+        ref = oracle.router(r["x"], r["W_r"], r["b"], wl.K, wl.scale, want_scores=True)
+        _, _, st = effective_routing(ref, gi, gw, r["b"].numpy(), wl.K, wl.scale)
+    np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(gi.ravel(), minlength=wl.E))
+    np.testing.assert_allclose(gw.astype(np.float64).sum(1), float(np.float32(wl.scale)), rtol=1e-6)
+    record_routing(f"{wl.name} T={wl.T} E={wl.E} K={wl.K} d={wl.d} {wl.act_dtype} "
+                   f"{n_group}/{topk_group}", st, wl.T)
 
 
 def test_forward_with_grouped_routing():

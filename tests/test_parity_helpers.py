@@ -6,7 +6,8 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import RANDOM_LAYER_SEEDS, RESULTS, TIE, check_output, coverage_tokens, random_layer
+from parity import (RANDOM_LAYER_SEEDS, RANDOM_ROUTER_SEEDS, RESULTS, TIE, check_output,
+                    coverage_tokens, random_layer, random_router)
 
 
 def _routing(T, E, K, seed, skew=0.5):
@@ -98,3 +99,20 @@ def test_random_layers_span_the_tile_regimes():
         if kw["w_dtype"] == "fp8":
             assert packed and (kw["d_latent"] or kw["d"]) % 128 == 0 and kw["F"] % 128 == 0
         assert hot is None or 0 <= hot < kw["E"]
+
+
+def test_random_routers_span_the_regimes():
+    # The seeded random router shapes: both logit tile forms (up to 64
+    # tokens and above), one and several split-K planes, fp32 and bf16,
+    # flat and group-limited choice, groups kept with fewer experts than K
+    # (the masked scores are chosen), one expert; all within the ABI.
+    draws = [random_router(s) for s in RANDOM_ROUTER_SEEDS]
+    assert any(kw["T"] <= 64 for kw, _, _ in draws) and any(kw["T"] > 4096 for kw, _, _ in draws)
+    assert {kw["act_dtype"] for kw, _, _ in draws} == {"bf16", "f32"}
+    assert any(g > 1 for _, g, _ in draws) and any(g == 1 for _, g, _ in draws)
+    assert any(g > 1 and kw["K"] > tg * (kw["E"] // g) for kw, g, tg in draws)
+    assert any(kw["E"] == 1 for kw, _, _ in draws) and any(kw["E"] == 1024 for kw, _, _ in draws)
+    for kw, g, tg in draws:
+        assert 1 <= kw["K"] <= min(kw["E"], 16) and kw["E"] <= 1024 and kw["d"] % 64 == 0
+        if g > 1:
+            assert g <= 64 and kw["E"] % g == 0 and kw["E"] // g >= 2 and 1 <= tg <= g
