@@ -7,8 +7,8 @@ import pytest
 import torch
 
 import fine_grained_sparse_amd as moe
-from moe_inputs import get_workload, make_layer_inputs
-from parity import expert_weights, log, weights_to_device
+from moe_inputs import Workload, get_workload, make_layer_inputs
+from parity import expert_weights, log, random_layer, weights_to_device
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -42,6 +42,25 @@ def test_noalloc_matches_forward_small(name, packed):
     _same(wl, dev, w, wl.T)
     _same(wl, dev, w, 77)          # the second call, smaller: the array keeps the first's bytes
     _same(wl, dev, w, 0)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4, 6, 10, 29])
+def test_noalloc_matches_forward_random_layers(seed):
+    # the seeded random layers of the parity tests (all four modes, 16- and
+    # 128-row tiles, latent layers), then a third of their tokens
+    kw, packed, hot = random_layer(seed)
+    wl = Workload(**kw)
+    log(f"[gpu] noalloc {wl.name} T={wl.T} d={wl.d} E={wl.E} K={wl.K} F={wl.F} "
+        f"d_latent={wl.d_latent}, then T={wl.T // 3}")
+    inp = make_layer_inputs(wl, "cpu", seed=100 + seed)
+    if hot is not None:
+        inp["b"][hot] = 10.0
+    dev = weights_to_device(inp, DEV)
+    w = expert_weights(dev)
+    if packed:
+        w = moe.pack_weights(w, n_shared=wl.n_shared)
+    _same(wl, dev, w, wl.T)
+    _same(wl, dev, w, wl.T // 3)
 
 
 def test_noalloc_matches_forward_k2_decode():
