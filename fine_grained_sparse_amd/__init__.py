@@ -30,7 +30,8 @@ MOE_ERR_SCRATCH = 7
 NOALLOC_SCRATCH_BYTES = 128 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 EXPORTS = ("moe_workspace_size", "moe_router", "moe_forward", "moe_forward_noalloc", "moe_pack_weights",
-           "moe_bias_update", "moe_bias_quantile", "moe_status_str")
+           "moe_bias_update", "moe_bias_quantile", "moe_status_str", "moe_slice_workspace_size",
+           "moe_forward_slice")
 WEIGHT_NAMES = ("W_gate", "W_up", "W_down", "Ws_gate", "Ws_up", "Ws_down", "W_lat_down", "W_lat_up")
 SCALE_NAMES = ("W_gate_scale", "W_up_scale", "W_down_scale")  # FP8 routed experts only
 STAGES = ("start", "router", "dispatch", "latent", "up", "down", "end")
@@ -81,6 +82,12 @@ def lib():
         L.moe_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, vp,
                                           ctypes.POINTER(ExpertWeights), vp, vp, vp, vp, vp, vp, vp]
         L.moe_forward_noalloc.restype = ctypes.c_int
+        L.moe_slice_workspace_size.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_int32, ctypes.c_int32]
+        L.moe_slice_workspace_size.restype = ctypes.c_size_t
+        L.moe_forward_slice.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(ExpertWeights), vp, vp, vp,
+                                        ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                        vp]
+        L.moe_forward_slice.restype = ctypes.c_int
         L.moe_pack_weights.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(ExpertWeights),
                                        ctypes.POINTER(ExpertWeights), vp]
         L.moe_pack_weights.restype = ctypes.c_int
@@ -379,6 +386,54 @@ def forward(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,
     if rc:
         raise MoeError("moe_forward", rc)
     return (out, routing) if return_routing else out
+
+
+def slice_workspace_size(layer_desc: LayerDesc, e0: int, E_total: int) -> int:
+    return int(lib().moe_slice_workspace_size(ctypes.byref(layer_desc), e0, E_total))
+
+
+def forward_slice(x, topk_idx, topk_w, weights, e0, E_total, *, n_shared=None, out=None,
+                  return_dispatch=False, workspace=None, stream=None):
+    """moe_forward_slice: one GPU's share of an expert-parallel layer.
+    `weights` holds the slice's routed experts only (W_gate [E, F, d_in],
+    ... for experts e0 .. e0 + E - 1 of E_total), plus the shared experts
+    (added to every token) and latent maps as forward() takes them;
+    topk_idx / topk_w [T, K] are the routing router() returned over all
+    E_total experts.  Returns out [T, d], or (out, dict of counts [E],
+    offsets [E + 1] and sorted_token over the slice's local experts) with
+    return_dispatch=True."""
+    _need(x, "x")
+    if x.dim() != 2 or x.dtype not in _DT:
+        raise ValueError("x must be [T, d] fp32 or bf16")
+    T, d = x.shape
+    dev, dt = x.device, x.dtype
+    if topk_idx.dim() != 2 or topk_idx.shape[0] != T:
+        raise ValueError("topk_idx must be [T, K]")
+    K = topk_idx.shape[1]
+    _need(topk_idx, "topk_idx", torch.int32, (T, K), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, K), dev)
+    E = weights["W_gate"].shape[0]
+    D, W = _weights_desc(weights, T, d, E, K, 1.0, dt, dev, n_shared)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((T, d), dtype=dt, device=dev)
+        disp = None
+        if return_dispatch:
+            disp = dict(counts=torch.empty((E,), dtype=torch.int32, device=dev),
+                        offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+                        sorted_token=torch.empty((max(T * K, 1),), dtype=torch.int32, device=dev))
+    _need(out, "out", dt, (T, d), dev)
+    nbytes = slice_workspace_size(D, e0, E_total)
+    if nbytes == 0:
+        raise MoeError("moe_slice_workspace_size", 2)
+    ws = (workspace or _default_ws).get(x.device, nbytes, stream)
+    r = disp or {}
+    rc = lib().moe_forward_slice(ctypes.byref(D), ctypes.byref(W), _ptr(x), _ptr(topk_idx), _ptr(topk_w),
+                                 e0, E_total, _ptr(out), _ptr(r.get("counts")), _ptr(r.get("offsets")),
+                                 _ptr(r.get("sorted_token")), _ptr(ws), nbytes, _stream(stream))
+    if rc:
+        raise MoeError("moe_forward_slice", rc)
+    return (out, disp) if return_dispatch else out
 
 
 def forward_noalloc(x, W_r, b, weights, K, scale=2.827, *, n_shared=None, out=None,

@@ -91,7 +91,11 @@ moe_status check_desc(const moe_layer_desc* D, bool forward) {
     return MOE_OK;
 }
 
-Plan make_plan(const moe_layer_desc* D, bool forward) {
+// E_total > 0: an expert-parallel slice (moe_forward_slice) of D->E experts
+// out of E_total, whose routing comes from the caller: no router buffers,
+// and the tiles are chosen for the rows the slice expects, A E / E_total
+// (the grids and buffers still hold all A assignments).
+Plan make_plan(const moe_layer_desc* D, bool forward, int E_total = 0) {
     Plan p{};
     p.T = D->T;
     p.d = D->d;
@@ -116,6 +120,7 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
     // least 8 K steps each.  Each split writes, and the gate reads back, a
     // partial plane of logits.  (fp32 activations only serve small parity
     // workloads: small tiles)
+    const bool slice = E_total > 0;
     p.rcfg = (p.T <= 64 || p.dt == DT_F32) ? TILE_SMALL : TILE_ROUTER;
     const int64_t rbm = tile_bm(p.rcfg), rbn = tile_bn_out(p.rcfg, EPI_STORE);
     p.rtiles = static_cast<int>(cdiv(p.T, rbm));
@@ -137,12 +142,13 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
     p.packed = forward && D->w_layout == MOE_LAYOUT_FRAG16;
     p.f8 = forward && D->w_dtype == MOE_FP8_E4M3;
     const TileCfg big = p.packed ? TILE_WIDE : TILE_LARGE;
-    p.ecfg = (p.A >= 10ll * p.E && p.dt == DT_BF16) ? big : (p.f8 ? TILE_WIDE16 : TILE_SMALL);
+    const int64_t arows = slice ? cdiv(p.A * p.E, E_total) : p.A;  // expected routed rows
+    p.ecfg = (arows >= 10ll * p.E && p.dt == DT_BF16) ? big : (p.f8 ? TILE_WIDE16 : TILE_SMALL);
     // ... at 16 x 256 when the 512-wide 16-row tiles would make fewer than
     // 128 workgroups (at most one tile per assignment, plus the shared rows'
     // tiles, times the N tiles of the wider of the two expert GEMMs)
     if (p.ecfg == TILE_SMALL && p.dt == DT_BF16) {
-        const int64_t mt = std::min<int64_t>(p.A, p.E) + (p.ns ? cdiv(p.T, 16) : 0);
+        const int64_t mt = std::min<int64_t>(arows, p.E) + (p.ns ? cdiv(p.T, 16) : 0);
         const int64_t nt = std::max<int64_t>(cdiv(std::max(p.F, p.Fsh), 256), cdiv(p.din, 512));
         if (mt * nt < 128) p.ecfg = TILE_NARROW;
     }
@@ -161,10 +167,13 @@ Plan make_plan(const moe_layer_desc* D, bool forward) {
         return o;
     };
     const int64_t T = p.T, E = p.E;
-    p.o_planes = p.dt == DT_BF16 ? take(3 * E * p.d * 2) : -1;
-    p.o_z = take(static_cast<int64_t>(p.nsplit) * T * p.ldz * 4);
-    p.o_idx = take(p.A * 4);
-    p.o_w = take(p.A * 4);
+    p.o_planes = p.o_z = p.o_idx = p.o_w = -1;
+    if (!slice) {
+        p.o_planes = p.dt == DT_BF16 ? take(3 * E * p.d * 2) : -1;
+        p.o_z = take(static_cast<int64_t>(p.nsplit) * T * p.ldz * 4);
+        p.o_idx = take(p.A * 4);
+        p.o_w = take(p.A * 4);
+    }
     p.o_counts = take(E * 4);
     p.o_theta = take(E * 4);
     p.o_offsets = p.o_masks = p.o_cbase = p.o_sorted = p.o_pos = p.o_tiles = p.o_ntiles = -1;
@@ -259,11 +268,11 @@ hipError_t record(void* const* ev, int i, hipStream_t s) {
     return hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
 }
 
-moe_status run_forward(const Plan& p, const void* x, const float* W_r, const float* b, const moe_expert_weights* W,
-                       void* out, int32_t* u_idx, float* u_w, int32_t* u_counts, int32_t* u_offsets,
+// Everything after the router: dispatch of the experts e0 .. e0 + p.E - 1
+// of idx, the latent down-map, the up and down projections and the combine.
+moe_status run_experts(const Plan& p, const void* x, const int32_t* idx, const float* w, int e0,
+                       const moe_expert_weights* W, void* out, int32_t* u_counts, int32_t* u_offsets,
                        int32_t* u_sorted, void* ws, hipStream_t s, void* const* ev) {
-    int32_t* idx = u_idx ? u_idx : at<int32_t>(ws, p.o_idx);
-    float* w = u_w ? u_w : at<float>(ws, p.o_w);
     int32_t* counts = u_counts ? u_counts : at<int32_t>(ws, p.o_counts);
     int32_t* offsets = u_offsets ? u_offsets : at<int32_t>(ws, p.o_offsets);
     int32_t* sorted = u_sorted ? u_sorted : at<int32_t>(ws, p.o_sorted);
@@ -277,12 +286,8 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
     char* R = at<char>(ws, p.o_R);
     const bool latent = p.dl > 0;
 
-    MOE_HIP(record(ev, MOE_EV_START, s));
-    moe_status st = run_router(p, x, W_r, b, idx, w, nullptr, ws, s);
-    if (st != MOE_OK) return st;
-    MOE_HIP(record(ev, MOE_EV_ROUTER, s));
     // shared tiles ride in the routed launches (rows = tokens)
-    MOE_HIP(launch_dispatch(idx, p.T, p.E, p.K, p.bm, p.ns ? p.T : 0, at<uint64_t>(ws, p.o_masks),
+    MOE_HIP(launch_dispatch(idx, p.T, p.E, e0, p.K, p.bm, p.ns ? p.T : 0, at<uint64_t>(ws, p.o_masks),
                             at<int32_t>(ws, p.o_cbase), counts, offsets, sorted, pos, tiles, ntiles, s));
     MOE_HIP(record(ev, MOE_EV_DISPATCH, s));
 
@@ -379,6 +384,46 @@ moe_status run_forward(const Plan& p, const void* x, const float* W_r, const flo
     return MOE_OK;
 }
 
+moe_status run_forward(const Plan& p, const void* x, const float* W_r, const float* b, const moe_expert_weights* W,
+                       void* out, int32_t* u_idx, float* u_w, int32_t* u_counts, int32_t* u_offsets,
+                       int32_t* u_sorted, void* ws, hipStream_t s, void* const* ev) {
+    int32_t* idx = u_idx ? u_idx : at<int32_t>(ws, p.o_idx);
+    float* w = u_w ? u_w : at<float>(ws, p.o_w);
+    MOE_HIP(record(ev, MOE_EV_START, s));
+    moe_status st = run_router(p, x, W_r, b, idx, w, nullptr, ws, s);
+    if (st != MOE_OK) return st;
+    MOE_HIP(record(ev, MOE_EV_ROUTER, s));
+    return run_experts(p, x, idx, w, 0, W, out, u_counts, u_offsets, u_sorted, ws, s, ev);
+}
+
+// The checks of a slice: the descriptor as a whole layer of E_total experts
+// (K, shapes, dtypes), then the slice inside it.
+moe_status check_slice(const moe_layer_desc* desc, int e0, int E_total) {
+    if (!desc) return MOE_ERR_NULL;
+    if (E_total < 1 || E_total > 1024 || e0 < 0 || desc->E < 1 || e0 > E_total - desc->E) return MOE_ERR_SHAPE;
+    moe_layer_desc whole = *desc;
+    whole.E = E_total;
+    whole.n_group = 1;  // the routing comes from the caller
+    whole.topk_group = 1;
+    return check_desc(&whole, true);
+}
+
+// The weight pointers every forward needs, with their alignment.
+moe_status check_weights(const moe_layer_desc* desc, const moe_expert_weights* W) {
+    if (!W->W_gate || !W->W_up || !W->W_down) return MOE_ERR_NULL;
+    if (desc->w_dtype == MOE_FP8_E4M3 && (!W->W_gate_scale || !W->W_up_scale || !W->W_down_scale))
+        return MOE_ERR_NULL;
+    if (desc->n_shared > 0 && (!W->Ws_gate || !W->Ws_up || !W->Ws_down)) return MOE_ERR_NULL;
+    if (desc->d_latent > 0 && (!W->W_lat_down || !W->W_lat_up)) return MOE_ERR_NULL;
+    const void* need[] = {W->W_gate, W->W_up, W->W_down};
+    for (const void* q : need)
+        if (!aligned16(q)) return MOE_ERR_ALIGN;
+    if (desc->n_shared > 0 && (!aligned16(W->Ws_gate) || !aligned16(W->Ws_up) || !aligned16(W->Ws_down)))
+        return MOE_ERR_ALIGN;
+    if (desc->d_latent > 0 && (!aligned16(W->W_lat_down) || !aligned16(W->W_lat_up))) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -438,17 +483,11 @@ moe_status moe_forward(const moe_layer_desc* desc, const void* x, const float* W
     }
     if (!x || !W_r || !b || !weights || !out || !workspace) return MOE_ERR_NULL;
     const moe_expert_weights* W = weights;
-    if (!W->W_gate || !W->W_up || !W->W_down) return MOE_ERR_NULL;
-    if (desc->w_dtype == MOE_FP8_E4M3 && (!W->W_gate_scale || !W->W_up_scale || !W->W_down_scale))
-        return MOE_ERR_NULL;
-    if (desc->n_shared > 0 && (!W->Ws_gate || !W->Ws_up || !W->Ws_down)) return MOE_ERR_NULL;
-    if (desc->d_latent > 0 && (!W->W_lat_down || !W->W_lat_up)) return MOE_ERR_NULL;
-    const void* need[] = {x, W_r, b, out, workspace, W->W_gate, W->W_up, W->W_down};
+    st = check_weights(desc, W);
+    if (st != MOE_OK) return st;
+    const void* need[] = {x, W_r, b, out, workspace};
     for (const void* q : need)
         if (!aligned16(q)) return MOE_ERR_ALIGN;
-    if (desc->n_shared > 0 && (!aligned16(W->Ws_gate) || !aligned16(W->Ws_up) || !aligned16(W->Ws_down)))
-        return MOE_ERR_ALIGN;
-    if (desc->d_latent > 0 && (!aligned16(W->W_lat_down) || !aligned16(W->W_lat_up))) return MOE_ERR_ALIGN;
     const void* opt[] = {topk_idx, topk_w, expert_counts, expert_offsets, sorted_token};
     for (const void* q : opt)
         if (q && !aligned16(q)) return MOE_ERR_ALIGN;
@@ -456,6 +495,38 @@ moe_status moe_forward(const moe_layer_desc* desc, const void* x, const float* W
     if (workspace_bytes < static_cast<size_t>(p.total)) return MOE_ERR_WORKSPACE;
     return run_forward(p, x, W_r, b, W, out, topk_idx, topk_w, expert_counts, expert_offsets, sorted_token,
                        workspace, s, stage_events);
+}
+
+size_t moe_slice_workspace_size(const moe_layer_desc* desc, int32_t e0, int32_t E_total) {
+    if (check_slice(desc, e0, E_total) != MOE_OK) return 0;
+    return static_cast<size_t>(make_plan(desc, true, E_total).total);
+}
+
+moe_status moe_forward_slice(const moe_layer_desc* desc, const moe_expert_weights* weights, const void* x,
+                             const int32_t* topk_idx, const float* topk_w, int32_t e0, int32_t E_total, void* out,
+                             int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_token,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    moe_status st = check_slice(desc, e0, E_total);
+    if (st != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((expert_counts && !aligned16(expert_counts)) || (expert_offsets && !aligned16(expert_offsets)) ||
+        (sorted_token && !aligned16(sorted_token)))
+        return MOE_ERR_ALIGN;
+    if (desc->T == 0) {  // no tokens: empty tensors may come as NULL pointers
+        if (expert_counts) MOE_HIP(launch_fill_i32(expert_counts, 0, desc->E, s));
+        if (expert_offsets) MOE_HIP(launch_fill_i32(expert_offsets, 0, desc->E + 1, s));
+        return MOE_OK;
+    }
+    if (!x || !topk_idx || !topk_w || !weights || !out || !workspace) return MOE_ERR_NULL;
+    st = check_weights(desc, weights);
+    if (st != MOE_OK) return st;
+    const void* need[] = {x, topk_idx, topk_w, out, workspace};
+    for (const void* q : need)
+        if (!aligned16(q)) return MOE_ERR_ALIGN;
+    const Plan p = make_plan(desc, true, E_total);
+    if (workspace_bytes < static_cast<size_t>(p.total)) return MOE_ERR_WORKSPACE;
+    return run_experts(p, x, topk_idx, topk_w, e0, weights, out, expert_counts, expert_offsets, sorted_token,
+                       workspace, s, nullptr);
 }
 
 moe_status moe_bias_quantile(const moe_layer_desc* desc, const void* x, const float* W_r, float* b,

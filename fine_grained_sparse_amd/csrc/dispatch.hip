@@ -20,8 +20,10 @@ namespace {
 constexpr int kMaxE = 1024;
 
 // grid: ceil(nch / 4) blocks of 4 waves; wave w owns chunk 4*block + w.
-__global__ __launch_bounds__(256) void k_dispatch_masks(const int32_t* __restrict__ idx, int T, int E, int K, int nch,
-                                                        uint64_t* __restrict__ masks) {
+// Expert ids are taken relative to e0; ids outside [e0, e0 + E) are not
+// this dispatch's (an expert-parallel slice) and are skipped.
+__global__ __launch_bounds__(256) void k_dispatch_masks(const int32_t* __restrict__ idx, int T, int E, int e0, int K,
+                                                        int nch, uint64_t* __restrict__ masks) {
     __shared__ unsigned long long sm[4][kMaxE];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int c = blockIdx.x * 4 + w;
@@ -29,7 +31,10 @@ __global__ __launch_bounds__(256) void k_dispatch_masks(const int32_t* __restric
     __syncthreads();
     const int t = c * 64 + lane;
     if (c < nch && t < T)
-        for (int k = 0; k < K; ++k) atomicOr(&sm[w][idx[static_cast<int64_t>(t) * K + k]], 1ull << lane);
+        for (int k = 0; k < K; ++k) {
+            const unsigned e = static_cast<unsigned>(idx[static_cast<int64_t>(t) * K + k] - e0);
+            if (e < static_cast<unsigned>(E)) atomicOr(&sm[w][e], 1ull << lane);
+        }
     __syncthreads();
     if (c < nch)
         for (int e = lane; e < E; e += 64) masks[static_cast<int64_t>(c) * E + e] = sm[w][e];
@@ -141,8 +146,8 @@ __global__ __launch_bounds__(1024) void k_fill_counts_zero(int32_t* __restrict__
     if (static_cast<int>(threadIdx.x) < E) counts[threadIdx.x] = 0;
 }
 
-__global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t* __restrict__ idx, int T, int E, int K, int nch,
-                                                          const uint64_t* __restrict__ masks,
+__global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t* __restrict__ idx, int T, int E, int e0, int K,
+                                                          int nch, const uint64_t* __restrict__ masks,
                                                           const int32_t* __restrict__ chunk_base,
                                                           const int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted_token,
@@ -154,7 +159,11 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t* __restr
     const uint64_t below = (1ull << lane) - 1ull;
     for (int k = 0; k < K; ++k) {
         const int64_t a = static_cast<int64_t>(t) * K + k;
-        const int e = idx[a];
+        const int e = idx[a] - e0;
+        if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) {  // another slice's expert
+            pos[a] = -1;
+            continue;
+        }
         const int64_t ce = static_cast<int64_t>(c) * E + e;
         const int p = offsets[e] + chunk_base[ce] + __popcll(masks[ce] & below);
         sorted_token[p] = t;
@@ -191,6 +200,7 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ Y, int64_
         }
         for (int k = 0; k < K; ++k) {
             const int p = pos[static_cast<int64_t>(t) * K + k];
+            if (p < 0) continue;  // an expert of another slice
             const float wk = w[static_cast<int64_t>(t) * K + k];
             float y[8];
             unpack8_once(Y + static_cast<int64_t>(p) * ldy + c * 8, y);
@@ -203,13 +213,13 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ Y, int64_
 
 }  // namespace
 
-hipError_t launch_dispatch(const int32_t* idx, int T, int E, int K, int bm, int shared_rows, uint64_t* masks,
+hipError_t launch_dispatch(const int32_t* idx, int T, int E, int e0, int K, int bm, int shared_rows, uint64_t* masks,
                            int32_t* chunk_base, int32_t* counts, int32_t* offsets, int32_t* sorted_token, int32_t* pos,
                            TileInfo* tiles, int32_t* ntiles, hipStream_t stream) {
     const int nch = (T + 63) / 64;
     const dim3 g4((nch + 3) / 4);
     if (nch > 0) {
-        hipLaunchKernelGGL(k_dispatch_masks, g4, dim3(256), 0, stream, idx, T, E, K, nch, masks);
+        hipLaunchKernelGGL(k_dispatch_masks, g4, dim3(256), 0, stream, idx, T, E, e0, K, nch, masks);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -225,8 +235,8 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int E, int K, int bm, int 
                        ntiles);
     err = hipGetLastError();
     if (err != hipSuccess || nch == 0) return err;
-    hipLaunchKernelGGL(k_dispatch_scatter, g4, dim3(256), 0, stream, idx, T, E, K, nch, masks, chunk_base, offsets,
-                       sorted_token, pos);
+    hipLaunchKernelGGL(k_dispatch_scatter, g4, dim3(256), 0, stream, idx, T, E, e0, K, nch, masks, chunk_base,
+                       offsets, sorted_token, pos);
     return hipGetLastError();
 }
 

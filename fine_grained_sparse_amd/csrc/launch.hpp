@@ -157,15 +157,18 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n,
 
 // Histogram, scan and stable permutation; also the tile table for the
 // grouped GEMMs (routed tiles of bm rows, then shared tiles if
-// shared_rows > 0) and ntiles[0..1] = (all tiles, routed tiles).
-hipError_t launch_dispatch(const int32_t* idx, int T, int E, int K, int bm,
+// shared_rows > 0) and ntiles[0..1] = (all tiles, routed tiles).  Experts
+// e0 .. e0 + E - 1 of idx are dispatched, as local experts 0 .. E - 1; an
+// assignment to any other id (another slice's expert) gets pos = -1.
+hipError_t launch_dispatch(const int32_t* idx, int T, int E, int e0, int K, int bm,
                            int shared_rows, uint64_t* masks,
                            int32_t* chunk_base, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_token,
                            int32_t* pos, TileInfo* tiles, int32_t* ntiles,
                            hipStream_t stream);
 
-// out[t] = (Yshared ? Yshared[t] : 0) + sum_k w[t,k] * Y[pos[t,k]]
+// out[t] = (Yshared ? Yshared[t] : 0) + sum_k w[t,k] * Y[pos[t,k]], over
+// the slots with pos >= 0
 hipError_t launch_combine(DType dt, const void* Y, int64_t ldy,
                           const void* Yshared, const int32_t* pos,
                           const float* w, int T, int K, int N, void* out,

@@ -194,6 +194,44 @@ moe_status moe_forward(const moe_layer_desc *desc, const void *x,
                        size_t workspace_bytes, void *stream,
                        void *const *stage_events);
 
+/* One GPU's share of an expert-parallel layer [K3 essay, load-imbalance
+ * paragraph: the work of the tokens routed to an expert falls on the GPU
+ * that holds it; the routed sum of llm-arch-kb K2 MoE section 3, split by
+ * expert].  The layer has E_total routed experts; this call holds
+ * experts e0 .. e0 + desc->E - 1 and applies them to the tokens of x with
+ * the routing a moe_router call over all E_total experts returned:
+ *   out[t] = shared(x_t) + sum over the k with e0 <= topk_idx[t,k] < e0 + E
+ *            of topk_w[t,k] * expert_{topk_idx[t,k]}(x_t)
+ * (the shared term only when desc->n_shared > 0; latent form: the sum is
+ * taken in latent space, then mapped up together with the shared experts,
+ * as in moe_forward).  Summing the outputs of slices that cover all
+ * E_total experts, one of them with the shared experts, gives the whole
+ * layer up to rounding; the slice [0, E_total) with the shared experts is
+ * moe_forward after its router, bit for bit.
+ *   desc: the layer with E = the slice's expert count; K (at most
+ *         min(E_total, 16)), shapes and dtypes as for moe_forward (n_group,
+ *         topk_group and scale are not used: the routing is given).
+ *   weights: the slice's experts only (W_gate [E, F, din] ... in the
+ *         descriptor's layout), plus the shared and latent matrices as
+ *         moe_forward takes them.
+ *   topk_idx [T, K] int32, topk_w [T, K] fp32: any expert id; ids outside
+ *         the slice are skipped.
+ *   expert_counts [E], expert_offsets [E + 1], sorted_token [T*K]: as for
+ *         moe_forward over the slice's local experts 0 .. E - 1 (nullable).
+ *   workspace: at least moe_slice_workspace_size(desc, e0, E_total) bytes.
+ * MOE_ERR_SHAPE when e0 < 0, E_total outside 1 .. 1024 or e0 + E >
+ * E_total; the other errors as for moe_forward, all before anything is
+ * enqueued.                                                                 */
+size_t moe_slice_workspace_size(const moe_layer_desc *desc, int32_t e0,
+                                int32_t E_total);
+moe_status moe_forward_slice(const moe_layer_desc *desc,
+                             const moe_expert_weights *weights, const void *x,
+                             const int32_t *topk_idx, const float *topk_w,
+                             int32_t e0, int32_t E_total, void *out,
+                             int32_t *expert_counts, int32_t *expert_offsets,
+                             int32_t *sorted_token, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the
  * whole layer exactly as moe_forward (same arguments, kernels and results),

@@ -197,7 +197,9 @@ def check_output(case, got, ref, act_dtype, latent, routing_stats=None, extra=No
     rel_u, beta = elem_budget(act_dtype, latent)
     rms = rn / np.sqrt(max(ref.shape[1], 1))
     budget = rel_u * np.abs(ref) + beta * rms[:, None]
-    ratio = np.abs(diff) / budget
+    # a token whose reference is exactly zero (an expert-parallel slice with
+    # none of its experts) has no budget: only an exact zero passes
+    ratio = np.divide(np.abs(diff), budget, out=np.where(diff == 0, 0.0, np.inf), where=budget > 0)
     worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape) if ratio.size else (0, 0)
     rec = dict(case=case, tokens=int(got.shape[0]), rel_l2=agg,
                tok_max=float(per_tok.max()) if per_tok.size else 0.0,

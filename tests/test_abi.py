@@ -31,8 +31,9 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["moe_bias_quantile", "moe_bias_update", "moe_forward",
-                                  "moe_forward_noalloc", "moe_pack_weights", "moe_router",
-                                  "moe_status_str", "moe_workspace_size"])
+                                  "moe_forward_noalloc", "moe_forward_slice", "moe_pack_weights",
+                                  "moe_router", "moe_slice_workspace_size", "moe_status_str",
+                                  "moe_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -182,12 +183,57 @@ def test_pack_weights_rejects_bad_arguments():
                  W(far, None, None, None, None, None, None, None)) == UNSUP
 
 
+def _slice(D, W=None, x=FAKE, idx=FAKE, w=FAKE, e0=0, E_total=384, out=FAKE, counts=None,
+           offsets=None, sorted=None, ws=FAKE, nbytes=None):
+    if W is None:
+        W = moe.ExpertWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    if nbytes is None:
+        nbytes = max(moe.slice_workspace_size(D, e0, E_total), 1)
+    vp = ctypes.c_void_p
+    return moe.lib().moe_forward_slice(ctypes.byref(D), ctypes.byref(W), vp(x), vp(idx), vp(w), e0,
+                                       E_total, vp(out), vp(counts), vp(offsets), vp(sorted), vp(ws),
+                                       nbytes, None)
+
+
+def test_slice_workspace_size_valid_and_invalid():
+    # 48 of 384 experts (one GPU of eight): no router buffers, fewer experts
+    sl = moe.slice_workspace_size(_k2(E=48), 0, 384)
+    assert 0 < sl < moe.workspace_size(_k2(), True)
+    assert moe.slice_workspace_size(_k2(E=48), 336, 384) == sl
+    # K may exceed the slice's experts (not the layer's)
+    assert moe.slice_workspace_size(_k2(E=4, K=8), 380, 384) > 0
+    assert moe.slice_workspace_size(_k2(E=4, K=9), 0, 8) == 0
+    for e0, E, Et in ((-1, 48, 384), (337, 48, 384), (0, 48, 1025), (0, 48, 0), (0, 0, 384)):
+        assert moe.slice_workspace_size(_k2(E=E), e0, Et) == 0, (e0, E, Et)
+    assert moe.slice_workspace_size(_k2(E=48, F=100), 0, 384) == 0
+
+
+def test_forward_slice_rejects_bad_arguments():
+    D = _k2(E=48)
+    for kw in (dict(x=None), dict(idx=None), dict(w=None), dict(out=None), dict(ws=None)):
+        assert _slice(D, **kw) == NULL, kw
+    assert _slice(D, W=moe.ExpertWeights(FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None)) == NULL
+    assert _slice(D, W=moe.ExpertWeights(FAKE, FAKE, FAKE, None, None, None, None, None)) == NULL
+    assert _slice(D, idx=FAKE_ODD) == ALIGN
+    assert _slice(D, sorted=FAKE_ODD) == ALIGN
+    assert _slice(D, W=moe.ExpertWeights(FAKE, FAKE, FAKE_ODD, FAKE, FAKE, FAKE, None, None)) == ALIGN
+    assert _slice(D, nbytes=moe.slice_workspace_size(D, 0, 384) - 256) == WS
+    assert _slice(D, e0=337) == SHAPE
+    assert _slice(D, e0=-1) == SHAPE
+    assert _slice(D, E_total=2000) == SHAPE
+    assert _slice(_k2(E=48, F=2000)) == SHAPE
+    assert _slice(_k2(E=48, w_dtype=moe.MOE_F32)) == UNSUP
+
+
 def test_zero_tokens_accepts_null_data_pointers():
     # nothing to read or write: no kernel is launched without count outputs
     D = _k2(T=0)
     assert _router(D, x=None, W_r=None, b=None, idx=None, w=None, ws=None) == OK
     assert _forward(D, x=None, W_r=None, b=None, out=None, ws=None) == OK
     assert _forward(D, x=None, out=None, counts=FAKE_ODD) == ALIGN
+    Ds = _k2(T=0, E=48)
+    assert _slice(Ds, x=None, idx=None, w=None, out=None, ws=None) == OK
+    assert _slice(Ds, x=None, out=None, counts=FAKE_ODD) == ALIGN
 
 
 def test_bias_update_rejects_bad_arguments():

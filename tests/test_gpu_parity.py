@@ -3,6 +3,8 @@
 Every case prints its name before it touches the GPU.  Tolerances are
 documented in tests/parity.py.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -179,6 +181,133 @@ def test_forward_with_grouped_routing():
     out_ref = oracle.forward_given_routing(oracle.layer_from_inputs(wl, inp), inp["x"], idx_eff, w_eff)
     check_output("mid_bf16_t300 grouped 8/3", out.float().cpu().numpy(), out_ref, wl.act_dtype,
                  False, st)
+
+
+# ---------------------------------------------------------------- expert-parallel slices
+def _slice_weights(w, e0, e1, shared):
+    """The weights one GPU holds for experts e0 .. e1 - 1 (plus the shared
+    experts if it runs them; the latent maps always)."""
+    s = {k: w[k][e0:e1].contiguous() for k in ("W_gate", "W_up", "W_down")}
+    for k in ("W_gate_scale", "W_up_scale", "W_down_scale"):
+        if w.get(k) is not None:
+            s[k] = w[k][e0:e1].contiguous()
+    for k in ("W_lat_down", "W_lat_up") + (("Ws_gate", "Ws_up", "Ws_down") if shared else ()):
+        if w.get(k) is not None:
+            s[k] = w[k]
+    return s
+
+
+def _slice_reference(wl, inp, gi, gw, e0, e1, shared):
+    """The oracle layer with the other slices' gate weights set to zero
+    (their ids moved inside the slice, so any id is a valid index)."""
+    local = (gi >= e0) & (gi < e1)
+    wl_s = dataclasses.replace(wl, n_shared=wl.n_shared if shared else 0,
+                               F_shared=wl.F_shared if shared else 0)
+    return oracle.forward_given_routing(oracle.layer_from_inputs(wl_s, inp), inp["x"],
+                                        np.where(local, gi, e0), np.where(local, gw, 0.0)), local
+
+
+@pytest.mark.parametrize("name,packed", [("mid_bf16_t300", False), ("mid_bf16_t300", True),
+                                         ("mid_fp8_t300", True), ("mid_latent_t200", True),
+                                         ("mid_fp8_latent_t200", True), ("mid_fp32_t77", False)])
+def test_forward_slice_parity(name, packed):
+    # Expert-parallel slices under the layer's GPU routing: one expert (with
+    # the shared experts), fewer experts than K, then two halves of the
+    # rest; every token against the oracle.
+    wl = get_workload(name)
+    inp = make_layer_inputs(wl, "cpu", seed=21)
+    dev = weights_to_device(inp, DEV)
+    idx, w, _ = moe.router(dev["x"], dev["W_r"], dev["b"], wl.K, wl.scale)
+    torch.cuda.synchronize()
+    gi, gw = idx.cpu().numpy(), w.cpu().numpy().astype(np.float64)
+    full = expert_weights(dev)
+    E, k1 = wl.E, max(2, wl.K - 1)
+    for i, (e0, e1) in enumerate([(0, 1), (1, k1), (k1, E // 2), (E // 2, E)]):
+        shared = i == 0 and wl.n_shared > 0
+        sw = _slice_weights(full, e0, e1, shared)
+        if packed:
+            sw = moe.pack_weights(sw, n_shared=wl.n_shared if shared else None)
+        log(f"[gpu] slice {name} experts {e0}..{e1 - 1} of {E}{' + shared' if shared else ''}"
+            f"{' packed' if packed else ''}")
+        out, disp = moe.forward_slice(dev["x"], idx, w, sw, e0, E,
+                                      n_shared=wl.n_shared if shared else None, return_dispatch=True)
+        torch.cuda.synchronize()
+        ref, local = _slice_reference(wl, inp, gi, gw, e0, e1, shared)
+        counts = np.bincount(gi[local] - e0, minlength=e1 - e0)
+        assert np.array_equal(disp["counts"].cpu().numpy(), counts)
+        assert np.array_equal(disp["offsets"].cpu().numpy(), np.concatenate([[0], np.cumsum(counts)]))
+        check_output(f"{name}{' packed' if packed else ''} slice {e0}..{e1 - 1}"
+                     f"{' + shared' if shared else ''}", out.float().cpu().numpy(), ref, wl.act_dtype,
+                     wl.d_latent > 0)
+
+
+@pytest.mark.parametrize("name,packed", [("mid_bf16_t300", True), ("mid_fp8_t300", True),
+                                         ("mid_latent_t200", False), ("tiny_fp32_t128", False)])
+def test_forward_slice_whole_range_is_forward(name, packed):
+    # all experts and the shared ones, under moe_forward's own routing: the
+    # same kernels in the same order, so the same bits
+    wl = get_workload(name)
+    log(f"[gpu] slice {name}: whole range against moe_forward")
+    dev = weights_to_device(make_layer_inputs(wl, "cpu", seed=22), DEV)
+    w = expert_weights(dev)
+    if packed:
+        w = moe.pack_weights(w, n_shared=wl.n_shared)
+    ref, r = moe.forward(dev["x"], dev["W_r"], dev["b"], w, wl.K, wl.scale, n_shared=wl.n_shared,
+                         return_routing=True)
+    out, disp = moe.forward_slice(dev["x"], r["idx"], r["w"], w, 0, wl.E, n_shared=wl.n_shared,
+                                  return_dispatch=True)
+    torch.cuda.synchronize()
+    bits = (lambda t: t.view(torch.int16)) if ref.dtype == torch.bfloat16 else (lambda t: t)
+    assert torch.equal(bits(out), bits(ref))
+    for k in ("counts", "offsets"):
+        assert torch.equal(disp[k], r[k])
+    n = wl.T * wl.K
+    assert torch.equal(disp["sorted_token"][:n], r["sorted_token"][:n])
+
+
+def test_forward_slices_sum_to_the_layer():
+    # fp32 layer split over four GPUs (8 experts each, the first with the
+    # shared expert): the partial outputs add up to the layer
+    wl = get_workload("tiny_fp32_t128")
+    log("[gpu] slices of tiny_fp32_t128 summed against moe_forward")
+    dev = weights_to_device(make_layer_inputs(wl, "cpu", seed=23), DEV)
+    w = expert_weights(dev)
+    ref, r = moe.forward(dev["x"], dev["W_r"], dev["b"], w, wl.K, wl.scale, n_shared=wl.n_shared,
+                         return_routing=True)
+    total = torch.zeros_like(ref, dtype=torch.float64)
+    for g in range(4):
+        e0, e1 = 8 * g, 8 * g + 8
+        total += moe.forward_slice(dev["x"], r["idx"], r["w"], _slice_weights(w, e0, e1, g == 0), e0,
+                                   wl.E, n_shared=wl.n_shared if g == 0 else None).double()
+    torch.cuda.synchronize()
+    err = float((total - ref.double()).norm() / ref.double().norm())
+    log(f"  sum of 4 slices vs layer: relative L2 {err:.2e}")
+    assert err < 1e-6
+
+
+@pytest.mark.parametrize("n_shared", [0, 1])
+def test_forward_slice_skips_ids_outside_it(n_shared):
+    # routing ids anywhere in [-40, 60) for a slice of experts 4 .. 7 of 16:
+    # only those four count; a token with none of them gets the shared
+    # experts' output, or zeros
+    wl = _custom(E=16, K=4, T=150, n_shared=n_shared, F_shared=128 if n_shared else 0)
+    log(f"[gpu] slice 4..7 of 16 under ids in [-40, 60), n_shared={n_shared}")
+    inp = make_layer_inputs(wl, "cpu", seed=24)
+    g = torch.Generator().manual_seed(25)
+    gi = torch.stack([torch.randperm(100, generator=g)[:wl.K] - 40 for _ in range(wl.T)]).to(torch.int32)
+    gw = torch.rand(wl.T, wl.K, generator=g)
+    gi[:10] = torch.tensor([-1, 8, 16, 59], dtype=torch.int32)   # no expert of the slice
+    dev = weights_to_device(inp, DEV)
+    sw = _slice_weights(expert_weights(dev), 4, 8, n_shared > 0)
+    out = moe.forward_slice(dev["x"], gi.to(DEV), gw.to(DEV), sw, 4, 16,
+                            n_shared=n_shared or None)
+    torch.cuda.synchronize()
+    ref, local = _slice_reference(wl, inp, gi.numpy(), gw.numpy().astype(np.float64), 4, 8, n_shared > 0)
+    assert not local[:10].any() and local.any()
+    if n_shared == 0:
+        assert bool((out[:10] == 0).all())
+    check_output(f"slice 4..7 of 16, ids in [-40, 60), shared {n_shared}", out.float().cpu().numpy(), ref,
+                 wl.act_dtype, False)
 
 
 # ---------------------------------------------------------------- bias update

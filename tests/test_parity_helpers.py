@@ -61,6 +61,15 @@ def test_check_output_catches_local_mistakes():
     assert np.linalg.norm(tok - ref) / np.linalg.norm(ref) < 2e-2
     with pytest.raises(AssertionError, match="tokens above"):
         check_output("one token", tok, ref, "bf16", False)
+    # tokens whose reference is exactly zero (an expert-parallel slice with
+    # none of its experts): an exact zero passes, anything else fails
+    zref, zgot = ref.copy(), noise.copy()
+    zref[5] = 0.0
+    zgot[5] = 0.0
+    assert check_output("zero token", zgot, zref, "bf16", False)["elem_ratio"] < 1
+    zgot[5, 3] = 1e-30
+    with pytest.raises(AssertionError):
+        check_output("zero token, one tiny element", zgot, zref, "bf16", False)
     del RESULTS[n0:]
 
 
