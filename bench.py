@@ -23,6 +23,10 @@ profiles/sq_counters.md (MFMA busy, shader clock) from one pass.
 The "yardsticks" leg measures, in the same run, a pure HBM streaming read and
 a register-only bf16 MFMA loop (with the shader clock it ran at); each
 roofline is also given as a fraction of those measured peaks.
+Other modes, each printing its own JSON line instead: `--sweep T1,T2,...`
+(the layer over batch sizes) and `--ep G` (one GPU's share under G-way
+expert parallelism: each slice of E/G experts through moe_forward_slice
+under the layer's own routing, beside the whole layer on one GPU).
 """
 import argparse
 import dataclasses
@@ -307,6 +311,55 @@ def measure_layer(moe, torch, wl, weights, steps, warmup, seed, layout):
     return dict(value=wl.T / layer_s, ms=ms, stages={k: round(v, 4) for k, v in stages.items()},
                 wm=wm, layer=layer, inputs=(x, W_r, b),
                 median_ms=round(per_step[len(per_step) // 2], 4), min_ms=round(per_step[0], 4))
+
+
+def measure_slices(moe, torch, wl, weights, G, steps, warmup, seed):
+    """One GPU's share of the layer under G-way expert parallelism (E/G
+    experts per GPU), for each of the G slices: moe_forward_slice over the
+    layer's own routing of all T tokens, as if each GPU had received the
+    rows routed to its experts.  Routed experts only: the router and the
+    shared experts would run on each token's owner, and the all-to-all
+    exchange is not built.  Returns one dict per slice: its rows, touched
+    experts, time and algorithmic rates."""
+    from moe_inputs import make_router_inputs
+    dev = torch.device("cuda:0")
+    r_in = make_router_inputs(wl, dev, seed=seed)
+    x, W_r, b = r_in["x"], r_in["W_r"], r_in["b"]
+    idx, w, counts = moe.router(x, W_r, b, wl.K, wl.scale)
+    counts = counts.cpu().tolist()
+    out = torch.empty((wl.T, wl.d), dtype=x.dtype, device=dev)
+    ws = moe.Workspace()
+    stream = torch.cuda.current_stream()
+    f8 = wl.w_dtype == "fp8"
+    wes = 1 if f8 else (2 if wl.act_dtype == "bf16" else 4)
+    sblk = (wl.F // 128) * (wl.d_in // 128) if f8 else 0
+    per = wl.E // G
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = []
+    for g in range(G):
+        e0, e1 = g * per, (g + 1) * per
+        sw = {k: weights[k][e0:e1] for k in ("W_gate", "W_up", "W_down") + moe.SCALE_NAMES
+              if weights.get(k) is not None}
+        if "layout" in weights:
+            sw["layout"] = weights["layout"]
+        for _ in range(warmup):
+            moe.forward_slice(x, idx, w, sw, e0, wl.E, out=out, workspace=ws, stream=stream)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(steps):
+            moe.forward_slice(x, idx, w, sw, e0, wl.E, out=out, workspace=ws, stream=stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        rows = int(sum(counts[e0:e1]))
+        touched = int(sum(1 for c in counts[e0:e1] if c > 0))
+        flops = 2.0 * rows * 3 * wl.d_in * wl.F
+        wbytes = touched * (3 * wl.d_in * wl.F * wes + 3 * sblk)
+        res.append(dict(experts=[e0, e1], rows=rows, touched=touched, ms=round(ms, 4),
+                        tflops=round(flops / (ms * 1e-3) / 1e12, 1),
+                        weight_gbps=round(wbytes / (ms * 1e-3) / 1e9, 1)))
+        log(f"[bench] slice {e0}..{e1 - 1}: {rows} rows, {touched} experts touched, {ms:.3f} ms")
+    return res
 
 
 def kernel_rooflines(wl, r, layout, ys):
@@ -677,6 +730,10 @@ def main():
     ap.add_argument("--sweep", metavar="T1,T2,...",
                     help="time --workload's layer at these batch sizes (same weights, seeded inputs "
                          "per size), print one JSON line of the results and exit")
+    ap.add_argument("--ep", type=int, default=0, metavar="G",
+                    help="time --workload's routed experts as G expert-parallel slices of E/G experts "
+                         "(moe_forward_slice under the layer's own routing, K2 form), print one JSON "
+                         "line of the results and exit")
     ap.add_argument("--summarize-sq", metavar="SQ_DIR",
                     help="print the profiles/sq_counters.md rows of --workload from one rocprofv3 "
                          "--pmc output directory and exit (no GPU use)")
@@ -725,6 +782,23 @@ def main():
     rows = make_expert_weights(wl, "cuda:0", seed=args.seed)
     weights = prepare(moe, torch, wl, rows, args.layout)
     torch.cuda.synchronize()
+    if args.ep:
+        del rows
+        if wl.d_latent or wl.E % args.ep:
+            sys.exit("--ep takes a K2-form layer whose experts divide evenly (the latent maps would "
+                     "run on each token's owner, outside the slice)")
+        full = measure_layer(moe, torch, wl, weights, args.steps, args.warmup, args.seed, args.layout)
+        log(f"[bench] {wl.name} on one GPU: {full['ms']:.3f} ms/step, stages {full['stages']}")
+        res = measure_slices(moe, torch, wl, weights, args.ep, args.steps, args.warmup, args.seed)
+        ms = [r["ms"] for r in res]
+        rows = [r["rows"] for r in res]
+        print(json.dumps(dict(workload=wl.name, layout=args.layout, ep=args.ep, steps=args.steps,
+                              warmup=args.warmup, layer_ms=round(full["ms"], 4), layer_stages=full["stages"],
+                              slices=res, slice_ms_max=max(ms), slice_ms_mean=round(sum(ms) / len(ms), 4),
+                              slice_ms_sum=round(sum(ms), 4),
+                              rows_max_over_mean=round(max(rows) * len(rows) / max(sum(rows), 1), 3))),
+              flush=True)
+        return
     if args.sweep:
         del rows
         sweep = []
