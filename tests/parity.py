@@ -12,6 +12,7 @@ output bound derived from the arithmetic):
     accumulation (three bf16 roundings of ~2^-9 each are expected to give
     about 3e-3), <= 1e-4 for the fp32 path.
 """
+import os
 import sys
 
 import numpy as np
@@ -280,7 +281,9 @@ def coverage_tokens(T, K, counts, offsets, sorted_token, idx_eff, gap, bm=128, n
     return np.array(sorted(chosen), np.int64)
 
 
-RANDOM_LAYER_SEEDS = range(96)
+# seeded random shapes of the GPU parity tests; MOE_RANDOM_LAYERS /
+# MOE_RANDOM_ROUTERS widen a run (the defaults are the committed suite)
+RANDOM_LAYER_SEEDS = range(int(os.environ.get("MOE_RANDOM_LAYERS", "96")))
 _RANDOM_MODES = ("bf16", "packed", "fp8", "f32")  # activations / weights of a drawn layer
 
 
@@ -319,7 +322,7 @@ def random_layer(seed):
     return kw, mode in ("packed", "fp8"), hot
 
 
-RANDOM_ROUTER_SEEDS = range(64)
+RANDOM_ROUTER_SEEDS = range(int(os.environ.get("MOE_RANDOM_ROUTERS", "64")))
 
 
 def random_router(seed):
