@@ -241,6 +241,36 @@ def test_forward_slice_parity(name, packed):
                      wl.d_latent > 0)
 
 
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_forward_slice_random_layers(seed):
+    # a random slice of each seeded random layer (all modes, both tile
+    # sizes), with the shared experts in every other one, under the
+    # layer's GPU routing: every token against the oracle
+    kw, packed, hot = random_layer(seed)
+    wl = Workload(**kw)
+    rng = np.random.default_rng(500 + seed)
+    e0 = int(rng.integers(0, wl.E))
+    e1 = int(rng.integers(e0 + 1, wl.E + 1))
+    shared = wl.n_shared > 0 and seed % 2 == 0
+    log(f"[gpu] slice {wl.name} T={wl.T} E={wl.E} K={wl.K}: experts {e0}..{e1 - 1}"
+        f"{' + shared' if shared else ''}")
+    inp = make_layer_inputs(wl, "cpu", seed=100 + seed)
+    if hot is not None:
+        inp["b"][hot] = 10.0
+    dev = weights_to_device(inp, DEV)
+    idx, w, _ = moe.router(dev["x"], dev["W_r"], dev["b"], wl.K, wl.scale)
+    torch.cuda.synchronize()
+    sw = _slice_weights(expert_weights(dev), e0, e1, shared)
+    if packed:
+        sw = moe.pack_weights(sw, n_shared=wl.n_shared if shared else None)
+    out = moe.forward_slice(dev["x"], idx, w, sw, e0, wl.E, n_shared=wl.n_shared if shared else None)
+    torch.cuda.synchronize()
+    ref, _ = _slice_reference(wl, inp, idx.cpu().numpy(), w.cpu().numpy().astype(np.float64), e0, e1,
+                              shared)
+    check_output(f"{wl.name} slice {e0}..{e1 - 1}{' + shared' if shared else ''}",
+                 out.float().cpu().numpy(), ref, wl.act_dtype, wl.d_latent > 0)
+
+
 @pytest.mark.parametrize("name,packed", [("mid_bf16_t300", True), ("mid_fp8_t300", True),
                                          ("mid_latent_t200", False), ("tiny_fp32_t128", False)])
 def test_forward_slice_whole_range_is_forward(name, packed):
