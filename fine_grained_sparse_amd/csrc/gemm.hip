@@ -13,11 +13,12 @@
 //   k_gemm       fp32 operands (small parity workloads): register-staged
 //                16 x 256 tiles, four v_mfma_f32_16x16x4_f32 per fragment.
 //   k_gemm_big   bf16, both operands DMA'd into an LDS ring
-//                (global_load_lds_dwordx4): 16 x 512 decode tiles, 128 x 256
-//                prefill tiles on row-major weights, 128 x 192 router-logit
-//                tiles.
-//   k_gemm_wide  bf16 prefill tiles on packed weights: 128 x 512, A through
-//                LDS, each wave's weight fragments straight into registers.
+//                (global_load_lds_dwordx4): 16 x 512 and 16 x 256 decode
+//                tiles, 128 x 256 prefill tiles on row-major weights,
+//                128 x 192 router-logit tiles.
+//   k_gemm_wide  bf16 activations on packed weights: 128 x 512 prefill tiles,
+//                A through LDS, each wave's weight fragments straight into
+//                registers; its FP8 form also at 16 x 256 (decode).
 // One 64-byte K slab feeds one v_mfma_f32_16x16x32_bf16 per 16x16 block; a
 // lane supplies row lane % 16 and the 16-byte K chunk lane / 16 of it.
 #include "common.hpp"
@@ -666,9 +667,10 @@ __global__ __launch_bounds__(64 * WM * WN, (big_occupancy<BM, BN, NST, ROWB>()))
     store_tile<TC, EPI, BM, BNO, TM, TN, MB, NB, WP, NT>(acc, lds, wm, wn, G, C, row0, rows, n0);
 }
 
-// Register-fed tile for packed weights: BM A rows x 512 B rows per
-// workgroup of four waves; wave w owns B rows [128 w, 128 w + 128), a
-// BM x 128 output block held in 16x16 accumulators.  Only A is shared
+// Register-fed tile for packed weights: BM A rows x BN B rows per
+// workgroup of four waves (BN = 512; 256 for the 16-row kernel); wave w owns
+// B rows [w BN/4, (w + 1) BN/4), a BM x BN/4 output block held in 16x16
+// accumulators.  Only A is shared
 // between the waves, so only A goes through LDS (DMA into a ring of four
 // 64-K slots).  Each wave loads its own weight fragments from global memory
 // straight into registers one stage ahead, a fragment being reloaded with
