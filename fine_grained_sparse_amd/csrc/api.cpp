@@ -30,6 +30,8 @@ using namespace moe;
 namespace {
 
 constexpr int64_t kAlign = 256;
+constexpr int kRouterGemvT = 32;  // router logits by k_router_gemv up to this many tokens
+static_assert(kRouterGemvT <= kRouterGemvMaxT, "the kernel's token capacity");
 int64_t up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -43,6 +45,7 @@ struct Plan {
     bool f8;                                  // routed experts in block-scaled FP8
     int64_t es;                               // element size
     // router
+    bool gemv;                                // logits by k_router_gemv (a few tokens)
     TileCfg rcfg;
     int nsplit, ldz, rtiles;
     // experts
@@ -130,6 +133,10 @@ Plan make_plan(const moe_layer_desc* D, bool forward, int E_total = 0) {
     ns = std::min<int64_t>(ns, std::max<int64_t>(1, ksteps / 8));
     p.nsplit = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(16, ns)));
     p.ldz = static_cast<int>(up(p.E, 8));
+    // up to kRouterGemvT tokens the logits are T dot products per expert
+    // read straight from the fp32 W_r (one pass, no planes, no split)
+    p.gemv = p.T <= kRouterGemvT;
+    if (p.gemv) p.nsplit = 1;
 
     // Experts: 128-row M tiles once experts average 10 rows or more (the
     // register-fed WIDE tile on packed weights, the LDS tile otherwise),
@@ -169,7 +176,7 @@ Plan make_plan(const moe_layer_desc* D, bool forward, int E_total = 0) {
     const int64_t T = p.T, E = p.E;
     p.o_planes = p.o_z = p.o_idx = p.o_w = -1;
     if (!slice) {
-        p.o_planes = p.dt == DT_BF16 ? take(3 * E * p.d * 2) : -1;
+        p.o_planes = (p.dt == DT_BF16 && !p.gemv) ? take(3 * E * p.d * 2) : -1;
         p.o_z = take(static_cast<int64_t>(p.nsplit) * T * p.ldz * 4);
         p.o_idx = take(p.A * 4);
         p.o_w = take(p.A * 4);
@@ -216,6 +223,10 @@ GemmArgs gemm_args() {
 // Router logits into the split-K partial planes of the workspace.
 moe_status run_logits(const Plan& p, const void* x, const float* W_r, void* ws, hipStream_t s) {
     float* z = at<float>(ws, p.o_z);
+    if (p.gemv) {
+        MOE_HIP(launch_router_gemv(x, p.dt == DT_F32, W_r, p.T, p.d, p.E, p.ldz, z, s));
+        return MOE_OK;
+    }
     GemmArgs g = gemm_args();
     GemmGroup& G = g.g[0];
     if (p.dt == DT_BF16) {

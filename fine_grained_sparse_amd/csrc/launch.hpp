@@ -139,6 +139,12 @@ hipError_t launch_quantile_bias(const float* z, int nsplit, int64_t split_stride
 // b[e] += gamma * sgn(mean(counts) - counts[e]) for e < E (E <= 1024).
 hipError_t launch_bias_update(const int32_t* counts, int E, float gamma, float* b, hipStream_t stream);
 
+// Router logits z [T, ldz] = x W_r^T for T <= kRouterGemvMaxT tokens (x bf16,
+// or fp32 when x_f32), fp32 FMAs on the fp32 weight; one plane (nsplit 1).
+constexpr int kRouterGemvMaxT = 32;
+hipError_t launch_router_gemv(const void* x, bool x_f32, const float* W, int T, int d, int E, int ldz, float* z,
+                              hipStream_t stream);
+
 // W_r (fp32) -> three bf16 planes with hi + mid + lo == W_r exactly.
 hipError_t launch_split3(const float* W, int64_t n, uint16_t* hi,
                          uint16_t* mid, uint16_t* lo, hipStream_t stream);

@@ -3,8 +3,9 @@
 // scaled weights; the MoEGate excerpt computes the logits in fp32 and, with
 // more than one expert group, limits the choice to the best groups).
 //
-// The logits themselves come from the grouped GEMM (gemm.hip).  For bf16
-// activations the fp32 router weight is split exactly into three bf16
+// The logits of up to 32 tokens are fp32 dot products (k_router_gemv);
+// above that they come from the grouped GEMM (gemm.hip).  For bf16
+// activations the fp32 router weight is then split exactly into three bf16
 // planes, W_r = hi + mid + lo (Henry, Tang & Heinecke 2019, "Leveraging the
 // bfloat16 Artificial Intelligence Datatype for Higher-Precision
 // Computations"): every bf16 x bf16 product is exact in the fp32 MFMA
@@ -32,6 +33,69 @@ __global__ __launch_bounds__(256) void k_split3(const float* __restrict__ W, int
         mid[i] = m;
         lo[i] = f32_to_bf16(r2);
     }
+}
+
+// Router logits of a few tokens straight from the fp32 weight (T <=
+// kRouterGemvMaxT): one workgroup per expert reads its row of W_r once, 16
+// bytes per lane, and forms the T dot products with fp32 FMAs; the lanes'
+// partial sums are then added in a fixed tree (the wave's butterfly, then
+// the four waves in pairs), so the result does not depend on timing.
+// Each product of a bf16 (or fp32) activation and the fp32 weight is exact
+// inside the FMA, as in the three-plane form, and the sums are fp32.  At
+// these sizes the planes and a split-K GEMM cost more, in launches and in a
+// chip left mostly idle, than the arithmetic.
+__device__ __forceinline__ void load4(const bf16_t* p, float (&o)[4]) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    o[0] = __uint_as_float(v.x << 16);
+    o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16);
+    o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+__device__ __forceinline__ void load4(const float* p, float (&o)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x;
+    o[1] = v.y;
+    o[2] = v.z;
+    o[3] = v.w;
+}
+
+// TM: the kernel's token capacity (a power of two >= T); rows past T - 1
+// repeat row T - 1 and are not written, so every load of a chunk is issued
+// before its FMAs, with no branch between them.
+template <typename TX, int TM>
+__global__ __launch_bounds__(256) void k_router_gemv(const TX* __restrict__ x, const float* __restrict__ W, int T,
+                                                     int d, int ldz, float* __restrict__ z) {
+    __shared__ float red[4][TM];
+    const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const float* w = W + static_cast<int64_t>(e) * d;
+    const TX* xr[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) xr[t] = x + static_cast<int64_t>(t < T ? t : T - 1) * d;
+    float acc[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[t] = 0.f;
+    for (int c = tid * 4; c < d; c += 1024) {
+        const float4 wv = *reinterpret_cast<const float4*>(w + c);
+        float xv[TM][4];
+#pragma unroll
+        for (int t = 0; t < TM; ++t) load4(xr[t] + c, xv[t]);
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            acc[t] = fmaf(xv[t][0], wv.x, acc[t]);
+            acc[t] = fmaf(xv[t][1], wv.y, acc[t]);
+            acc[t] = fmaf(xv[t][2], wv.z, acc[t]);
+            acc[t] = fmaf(xv[t][3], wv.w, acc[t]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+        float v = acc[t];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if (lane == 0) red[wid][t] = v;
+    }
+    __syncthreads();
+    if (tid < T) z[static_cast<int64_t>(tid) * ldz + e] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
 }
 
 __global__ __launch_bounds__(256) void k_fill_i32(int32_t* p, int32_t v, int64_t n) {
@@ -319,6 +383,35 @@ hipError_t launch_split3(const float* W, int64_t n, uint16_t* hi, uint16_t* mid,
     const int64_t blocks = (n + 255) / 256;
     hipLaunchKernelGGL(k_split3, dim3(static_cast<unsigned>(blocks < 8192 ? blocks : 8192)), dim3(256), 0, stream, W,
                        n, hi, mid, lo);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_gemv(const void* x, bool x_f32, const float* W, int T, int d, int E, int ldz, float* z,
+                              hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    if (T > kRouterGemvMaxT || d <= 0 || d % 4 || E <= 0 || ldz < E) return hipErrorInvalidValue;
+#define MOE_GEMV(TM)                                                                                      \
+    do {                                                                                                  \
+        if (x_f32)                                                                                        \
+            hipLaunchKernelGGL((k_router_gemv<float, TM>), dim3(E), dim3(256), 0, stream,                 \
+                               static_cast<const float*>(x), W, T, d, ldz, z);                            \
+        else                                                                                              \
+            hipLaunchKernelGGL((k_router_gemv<bf16_t, TM>), dim3(E), dim3(256), 0, stream,                \
+                               static_cast<const bf16_t*>(x), W, T, d, ldz, z);                           \
+    } while (0)
+    if (T <= 1)
+        MOE_GEMV(1);
+    else if (T <= 2)
+        MOE_GEMV(2);
+    else if (T <= 4)
+        MOE_GEMV(4);
+    else if (T <= 8)
+        MOE_GEMV(8);
+    else if (T <= 16)
+        MOE_GEMV(16);
+    else
+        MOE_GEMV(32);
+#undef MOE_GEMV
     return hipGetLastError();
 }
 

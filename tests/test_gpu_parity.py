@@ -60,10 +60,15 @@ def _full_parity(wl, inp, seed_note="", packed=False):
 
 # ---------------------------------------------------------------- router
 # T = 64 and 65 sit on either side of the switch from 16-row to 128-row
-# logit tiles; 1024 and 4096 split K into different numbers of planes.
+# logit tiles; 1024 and 4096 split K into different numbers of planes; up to
+# 32 tokens the logits are fp32 dot products (32 and 33 on either side).
 @pytest.mark.parametrize("name,T", [("tiny_fp32_t128", None), ("mid_bf16_t300", None),
                                     ("k2_router_t4096", 64), ("k2_router_t4096", 65),
-                                    ("k2_router_t4096", None), ("k3_latent_t4096", 1024)])
+                                    ("k2_router_t4096", None), ("k3_latent_t4096", 1024),
+                                    ("k2_router_t4096", 1), ("k2_router_t4096", 3),
+                                    ("k2_router_t4096", 17), ("k2_router_t4096", 32),
+                                    ("k2_router_t4096", 33), ("k3_latent_t4096", 32),
+                                    ("tiny_fp32_t128", 5)])
 def test_router_parity(name, T):
     wl = get_workload(name)
     log(f"[gpu] router {name} T={T or wl.T}")
@@ -371,7 +376,8 @@ def test_bias_update_from_the_layers_own_counts():
 
 
 @pytest.mark.parametrize("name,T", [("tiny_fp32_t128", None), ("mid_bf16_t300", None),
-                                    ("k3_latent_t4096", None), ("k2_router_t4096", 16384)])
+                                    ("k3_latent_t4096", None), ("k2_router_t4096", 16384),
+                                    ("k3_latent_t4096", 24)])
 def test_bias_quantile_parity(name, T):
     wl = get_workload(name)
     T = T or wl.T
