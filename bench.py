@@ -466,6 +466,65 @@ def measure_bias_steps(moe, torch, seed):
     return out
 
 
+def gpu_clocks(torch):
+    """Current shader (SCLK) and memory (MCLK) clocks of the GPU in MHz: the
+    sysfs DPM tables (the level marked '*') of the card whose PCI bus matches
+    device 0, else amd-smi's clock metrics.  A snapshot between timings, not
+    the clock under load (the MFMA yardstick and the counter tables give
+    that)."""
+    import subprocess
+
+    def dpm(path):
+        try:
+            with open(path) as f:
+                for ln in f:
+                    if ln.rstrip().endswith("*"):
+                        return int("".join(ch for ch in ln.split(":")[1] if ch.isdigit()))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    bus = None
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        if getattr(pr, "pci_bus_id", None) is not None:
+            bus = "%02x:%02x" % (pr.pci_bus_id, getattr(pr, "pci_device_id", 0))
+    except Exception:
+        pass
+    cards = []
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        sclk, mclk = dpm(dev + "/pp_dpm_sclk"), dpm(dev + "/pp_dpm_mclk")
+        if sclk is None and mclk is None:
+            continue
+        cards.append((os.path.basename(os.path.realpath(dev)), sclk, mclk))
+    if cards:
+        pick = [c for c in cards if bus and bus in c[0]] or (cards if len(cards) == 1 else [])
+        if pick:
+            return dict(sclk_mhz=pick[0][1], mclk_mhz=pick[0][2], source="sysfs pp_dpm (" + pick[0][0] + ")")
+    try:
+        out = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True,
+                             timeout=30).stdout
+        data = json.loads(out[out.index("["):] if "[" in out else out)
+        ent = data[0] if isinstance(data, list) else data
+        clk = ent.get("clock", ent)
+
+        def mhz(v):
+            v = v.get("clk", v) if isinstance(v, dict) else v
+            v = v.get("value") if isinstance(v, dict) else v
+            try:
+                return int(float(v))
+            except (TypeError, ValueError):
+                return None
+        gfx = [mhz(v) for k, v in clk.items() if k.startswith("gfx")]
+        mem = [mhz(v) for k, v in clk.items() if k.startswith("mem")]
+        gfx = [g for g in gfx if g is not None]
+        mem = [m for m in mem if m is not None]
+        return dict(sclk_mhz=max(gfx) if gfx else None, mclk_mhz=max(mem) if mem else None,
+                    source="amd-smi metric --clock")
+    except Exception as e:  # no sysfs table and no usable amd-smi: say so
+        return dict(sclk_mhz=None, mclk_mhz=None, source=f"unavailable ({type(e).__name__})")
+
+
 def yardsticks(torch, read_gib=8.0, mfma_ms=20.0):
     """Measured peaks of this GPU in this run (libyardstick.so): the best of
     a plain and a non-temporal streaming read of read_gib GiB over a few grid
@@ -815,6 +874,8 @@ def main():
         print(json.dumps(dict(workload=wl.name, layout=args.layout, steps=args.steps, warmup=args.warmup,
                               sweep=sweep)), flush=True)
         return
+    clocks_before = gpu_clocks(torch)
+    log(f"[bench] clocks before: {clocks_before}")
     log(f"[bench] timing {wl.name}: warmup {args.warmup}, steps {args.steps}")
     main_r = measure_layer(moe, torch, wl, weights, args.steps, args.warmup, args.seed, args.layout)
     log(f"[bench] {wl.name}: {main_r['ms']:.3f} ms/step, stages {main_r['stages']}")
@@ -879,6 +940,8 @@ def main():
         ys = yardsticks(torch)
         log(f"[bench] yardsticks: {ys['hbm_read_gbs']} GB/s ({ys['hbm_read_best']}), "
             f"{ys['mfma_tflops']} TFLOP/s at {ys['mfma_clock_ghz']} GHz")
+    clocks_after = gpu_clocks(torch)
+    log(f"[bench] clocks after: {clocks_after}")
     main_roof, main_kernels = kernel_rooflines(main_wl, main_r, args.layout, ys)
     for name, (awl, r) in also_raw.items():
         roof, kern = kernel_rooflines(awl, r, args.layout, ys)
@@ -914,6 +977,7 @@ def main():
                        weights=weights_note(mw, args.layout), parallelism="single-gpu"),
         "roofline": main_roof, "cpu_baseline": cpu, "kernels": main_kernels,
         "layer": main_r["layer"], "stages_ms": main_r["stages"], "yardsticks": ys,
+        "clocks": dict(before=clocks_before, after=clocks_after),
         "kernel_source": source_hash(), "also": also,
     }
     print(json.dumps(line), flush=True)

@@ -255,12 +255,11 @@ int64_t split_stride(const Plan& p) { return static_cast<int64_t>(p.T) * p.ldz; 
 
 // Router: logits, then the top-K gate.
 moe_status run_router(const Plan& p, const void* x, const float* W_r, const float* b, int32_t* idx, float* w,
-                      int32_t* counts_atomic, void* ws, hipStream_t s) {
+                      int32_t* counts, void* ws, hipStream_t s) {
     moe_status st = run_logits(p, x, W_r, ws, s);
     if (st != MOE_OK) return st;
-    if (counts_atomic) MOE_HIP(launch_fill_i32(counts_atomic, 0, p.E, s));
     MOE_HIP(launch_topk_gate(at<float>(ws, p.o_z), p.nsplit, split_stride(p), p.ldz, b, p.T, p.E, p.K, p.ng, p.tg,
-                             p.scale, idx, w, counts_atomic, s));
+                             p.scale, idx, w, counts, s));
     return MOE_OK;
 }
 

@@ -151,7 +151,8 @@ hipError_t launch_split3(const float* W, int64_t n, uint16_t* hi,
 
 // Sigmoid, biased top-K (limited to the topk_group best of n_group expert
 // groups when n_group > 1), renormalise and scale; z holds nsplit partial
-// logit planes of [T, ldz].  counts (nullable) gets +1 per selection.
+// logit planes of [T, ldz].  counts (nullable, E <= 1024) gets the number of
+// selections of each expert.
 hipError_t launch_topk_gate(const float* z, int nsplit, int64_t split_stride,
                             int ldz, const float* b, int T, int E, int K,
                             int n_group, int topk_group, float scale,

@@ -21,18 +21,38 @@ namespace {
 // is exact in fp32 (its operands agree to within a factor of two), and
 // after two 8-bit captures at most 8 significant bits remain, so lo holds
 // the rest exactly: hi + mid + lo == w for finite normal w.
+__device__ __forceinline__ void split3_one(float w, bf16_t& h, bf16_t& m, bf16_t& l) {
+    h = f32_to_bf16(w);
+    const float r1 = w - bf16_to_f32(h);
+    m = f32_to_bf16(r1);
+    l = f32_to_bf16(r1 - bf16_to_f32(m));
+}
+
+// Four consecutive weights per thread: one 16-byte load, three 8-byte
+// stores (2-byte stores of one weight per thread took twice as long); the
+// last n % 4 weights one by one.
 __global__ __launch_bounds__(256) void k_split3(const float* __restrict__ W, int64_t n, bf16_t* __restrict__ hi,
                                                 bf16_t* __restrict__ mid, bf16_t* __restrict__ lo) {
-    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
-        const float w = W[i];
-        const bf16_t h = f32_to_bf16(w);
-        const float r1 = w - bf16_to_f32(h);
-        const bf16_t m = f32_to_bf16(r1);
-        const float r2 = r1 - bf16_to_f32(m);
-        hi[i] = h;
-        mid[i] = m;
-        lo[i] = f32_to_bf16(r2);
+    const int64_t n4 = n / 4, stride = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n4; i += stride) {
+        const float4 w = reinterpret_cast<const float4*>(W)[i];
+        const float v[4] = {w.x, w.y, w.z, w.w};
+        uint32_t ph[2], pm[2], pl[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            bf16_t h0, m0, l0, h1, m1, l1;
+            split3_one(v[2 * q], h0, m0, l0);
+            split3_one(v[2 * q + 1], h1, m1, l1);
+            ph[q] = h0 | (static_cast<uint32_t>(h1) << 16);
+            pm[q] = m0 | (static_cast<uint32_t>(m1) << 16);
+            pl[q] = l0 | (static_cast<uint32_t>(l1) << 16);
+        }
+        reinterpret_cast<uint2*>(hi)[i] = make_uint2(ph[0], ph[1]);
+        reinterpret_cast<uint2*>(mid)[i] = make_uint2(pm[0], pm[1]);
+        reinterpret_cast<uint2*>(lo)[i] = make_uint2(pl[0], pl[1]);
     }
+    for (int64_t i = 4 * n4 + blockIdx.x * 256ll + threadIdx.x; i < n; i += stride)
+        split3_one(W[i], hi[i], mid[i], lo[i]);
 }
 
 // Router logits of a few tokens straight from the fp32 weight (T <=
@@ -187,6 +207,10 @@ __global__ __launch_bounds__(256) void k_topk_gate(const float* __restrict__ z, 
                                                    int32_t* __restrict__ counts) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // the per-expert counts start at zero here; k_expert_counts, launched
+    // after this kernel, adds them up
+    if (counts && blockIdx.x == 0)
+        for (int e = threadIdx.x; e < E; e += 256) counts[e] = 0;
     if (t >= T) return;
     float v[J], s[J];
 #pragma unroll
@@ -260,8 +284,28 @@ __global__ __launch_bounds__(256) void k_topk_gate(const float* __restrict__ z, 
     if (lane < K) {
         idx[static_cast<int64_t>(t) * K + rank] = my_e;
         w[static_cast<int64_t>(t) * K + rank] = (my_s / den) * scale;
-        if (counts) atomicAdd(counts + my_e, 1);
     }
+}
+
+// Per-expert counts of the n = T K selections in idx: each block counts its
+// share in LDS, then adds its nonzero bins to counts (zeroed by the gate's
+// first block).  Integer adds, so the result does not depend on their
+// order; the global adds of one address number at most the blocks (64),
+// where one add per selection (T K of them, a hot expert's thousands to
+// one address) serialised in L2.
+constexpr int kCountsMaxE = 1024;
+__global__ __launch_bounds__(1024) void k_expert_counts(const int32_t* __restrict__ idx, int64_t n, int E,
+                                                        int32_t* __restrict__ counts) {
+    __shared__ int h[kCountsMaxE];
+    for (int e = threadIdx.x; e < E; e += 1024) h[e] = 0;
+    __syncthreads();
+    for (int64_t i = blockIdx.x * 1024ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 1024) {
+        const unsigned e = static_cast<unsigned>(idx[i]);
+        if (e < static_cast<unsigned>(E)) atomicAdd(&h[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 1024)
+        if (h[e]) atomicAdd(counts + e, h[e]);
 }
 
 // Aux-loss-free bias update after a batch (llm-arch-kb "Kimi K2 MoE": the
@@ -450,6 +494,13 @@ hipError_t launch_topk_gate(const float* z, int nsplit, int64_t split_stride, in
     else
         MOE_TOPK(16);
 #undef MOE_TOPK
+    if (counts) {
+        if (E > kCountsMaxE) return hipErrorInvalidValue;
+        const int64_t n = static_cast<int64_t>(T) * K;
+        const int64_t blocks = std::min<int64_t>(64, (n + 16383) / 16384);
+        hipLaunchKernelGGL(k_expert_counts, dim3(static_cast<unsigned>(blocks)), dim3(1024), 0, stream, idx, n, E,
+                           counts);
+    }
     return hipGetLastError();
 }
 

@@ -94,6 +94,8 @@ def test_router_1024_experts_top16():
     ref = oracle.router(inp["x"], inp["W_r"], inp["b"], wl.K, wl.scale, want_scores=True)
     _, _, st = effective_routing(ref, idx.cpu().numpy(), w.cpu().numpy(), inp["b"].numpy(), wl.K,
                                  wl.scale)
+    # the counts' LDS histogram at its largest expert count
+    np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(idx.cpu().numpy().ravel(), minlength=wl.E))
     record_routing("router E=1024 K=16 T=70", st, wl.T)
 
 
