@@ -118,7 +118,8 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(int E, int bm, int share
             ti.rows = min(bm, cnt - j * bm);
             ti.first = toff;
             ti.count = nt;
-            ti.pad0_ = ti.pad1_ = 0;
+            ti.run_row0 = off;
+            ti.run_rows = cnt;
             tiles[toff + j] = ti;
         }
     }
@@ -133,7 +134,8 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(int E, int bm, int share
         ti.rows = min(bm, shared_rows - j * bm);
         ti.first = ttotal + (j / kSharedRun) * kSharedRun;
         ti.count = min(kSharedRun, nsh - (j / kSharedRun) * kSharedRun);
-        ti.pad0_ = ti.pad1_ = 0;
+        ti.run_row0 = (j / kSharedRun) * kSharedRun * bm;
+        ti.run_rows = min(kSharedRun * bm, shared_rows - ti.run_row0);
         tiles[ttotal + j] = ti;
     }
     if (threadIdx.x == 0) {

@@ -380,38 +380,41 @@ struct Job {
     int gi, expert, row0, rows, n0;
 };
 
+// With a tile table, BM is the table's rows per tile (the planner builds the
+// table for the kernels that walk it), and the job comes from one load of
+// the entry at slot / ntn, whose run fields place every tile of its run;
+// the two tile counts come in one load.
 template <int BM, int BNO>
 __device__ __forceinline__ bool pick_job(const GemmArgs& a, Job& jb) {
-    const int total = (a.tiles ? a.ntiles[0] : (a.M + BM - 1) / BM) * a.ntn;  // active (M, N) tile pairs
-    const int total_r = a.tiles ? a.ntiles[1] * a.ntn : total;                // ... of them routed
+    int total, total_r;  // active (M, N) tile pairs, and the routed ones among them
+    if (a.tiles) {
+        const int2 nt = *reinterpret_cast<const int2*>(a.ntiles);
+        total = nt.x * a.ntn;
+        total_r = nt.y * a.ntn;
+    } else {
+        total = total_r = ((a.M + BM - 1) / BM) * a.ntn;
+    }
     const int lin = xcd_slot_pair(static_cast<int>(blockIdx.x), total_r, total);
     if (lin < 0) return false;
-    int first, cnt;
     if (a.tiles) {
         const TileInfo t0 = a.tiles[lin / a.ntn];
-        first = t0.first;
-        cnt = t0.count;
+        const int u = lin - t0.first * a.ntn, i = u % t0.count;
+        jb.gi = t0.group;
+        jb.expert = t0.expert;
+        jb.row0 = t0.run_row0 + i * BM;
+        jb.rows = min(BM, t0.run_rows - i * BM);
+        jb.n0 = (u / t0.count) * BNO;
     } else {
         const int mtiles = total / a.ntn;
-        first = (lin / a.ntn) & ~7;
-        cnt = min(8, mtiles - first);
-    }
-    const int u = lin - first * a.ntn;
-    const int mt = first + u % cnt;
-    jb.gi = 0;
-    jb.expert = 0;
-    if (a.tiles) {
-        const TileInfo ti = a.tiles[mt];
-        jb.gi = ti.group;
-        jb.expert = ti.expert;
-        jb.row0 = ti.row0;
-        jb.rows = ti.rows;
-    } else {
-        jb.row0 = mt * BM;
+        const int first = (lin / a.ntn) & ~7, cnt = min(8, mtiles - first);
+        const int u = lin - first * a.ntn;
+        jb.gi = 0;
+        jb.expert = 0;
+        jb.row0 = (first + u % cnt) * BM;
         jb.rows = min(BM, a.M - jb.row0);
         if (jb.rows <= 0) return false;
+        jb.n0 = (u / cnt) * BNO;
     }
-    jb.n0 = (u / cnt) * BNO;
     return jb.n0 < (jb.gi ? a.g[1].N : a.g[0].N);
 }
 

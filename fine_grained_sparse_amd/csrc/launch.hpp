@@ -58,10 +58,12 @@ struct GemmGroup {
 // One M tile of a grouped GEMM.  `first` and `count` describe the run of
 // consecutive tiles that share weights (all tiles of one routed expert, or
 // up to 8 tiles of the shared rows); the GEMM walks each run M-tile-fastest
-// so those tiles stream every weight slice together.
+// so those tiles stream every weight slice together.  run_row0 / run_rows
+// are the run's rows (tile i of the run: rows run_row0 + i bm ..), so that a
+// workgroup finds its tile from any entry of the run with one table load.
 struct TileInfo {
     int32_t group, expert, row0, rows;
-    int32_t first, count, pad0_, pad1_;
+    int32_t first, count, run_row0, run_rows;
 };
 
 // XCD-aware slot map of a tile-table launch.  Blocks go to the eight XCDs
