@@ -610,11 +610,14 @@ def _oracle_layer(oracle, wl, hw, W_r, b):
 
 def cpu_baseline(wl, hw, inputs, target_s, seed, full=False, router_only=False):
     """The oracle as it stands (plain fp64 loops, OpenMP over tokens) on the
-    host's cores: the whole layer per token (router over all experts, top-K,
-    K routed + the shared SwiGLU experts, latent maps), or the router alone.
-    full: every token of the batch.  Otherwise a random token sample sized to
-    about target_s seconds; rows are independent, so the per-token rate is
-    the batch's rate (labelled extrapolated)."""
+    host's cores: the whole layer (router over all experts, top-K, K routed
+    + the shared SwiGLU experts, latent maps), or the router alone.
+    full: every token of the batch through the whole layer.  Otherwise the
+    router and the dispatch run over every token, and the expert part
+    (oracle_forward_given_routing under that routing) over a random token
+    sample sized to about target_s seconds; rows are independent there, so
+    the batch's expert time is the sample's per-token time times T.  The
+    layer's time is the sum, labelled extrapolated."""
     import numpy as np
     import oracle
     nth = oracle.default_threads()
@@ -636,12 +639,18 @@ def cpu_baseline(wl, hw, inputs, target_s, seed, full=False, router_only=False):
         sec = time.perf_counter() - t
         return dict(value=round(wl.T / sec, 2), seconds=round(sec, 2), **info,
                     sample=f"all {wl.T} tokens of the batch, whole layer per token ({what})")
+    t = time.perf_counter()
+    rt = oracle.router(x, W_r, b, wl.K, wl.scale, nthreads=nth)
+    router_s = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.dispatch(rt["idx"], wl.E)
+    dispatch_s = time.perf_counter() - t
     rng = np.random.default_rng(seed)
 
     def run(n):
         toks = np.sort(rng.choice(wl.T, size=min(n, wl.T), replace=False))
         t = time.perf_counter()
-        oracle.forward(lay, x[toks].contiguous(), nthreads=nth)
+        oracle.forward_given_routing(lay, x[toks].contiguous(), rt["idx"][toks], rt["w"][toks], nthreads=nth)
         return len(toks), time.perf_counter() - t
 
     n, sec = run(nth)
@@ -649,11 +658,15 @@ def cpu_baseline(wl, hw, inputs, target_s, seed, full=False, router_only=False):
         n2 = int(min(wl.T, max(nth, nth * int(target_s / max(sec, 1e-3)))))
         if n2 > n:
             n, sec = run(n2)
-    rate = n / sec
-    return dict(value=round(rate, 3), seconds=round(sec, 2), extrapolated=True,
-                full_batch_s=round(wl.T / rate, 1), **info,
-                sample=(f"{n} random tokens of the {wl.T}-token batch, whole layer per token "
-                        f"({what}); per-token rate, extrapolated to the batch (rows independent)"))
+    experts_s = sec / n * wl.T
+    layer_s = router_s + dispatch_s + experts_s
+    return dict(value=round(wl.T / layer_s, 3), seconds=round(router_s + dispatch_s + sec, 2),
+                extrapolated=True, full_batch_s=round(layer_s, 1), router_s=round(router_s, 2),
+                dispatch_s=round(dispatch_s, 3), experts_s_extrapolated=round(experts_s, 1), **info,
+                sample=(f"router ({wl.E} experts, top-{wl.K}) and dispatch over all {wl.T} tokens; the "
+                        f"expert part ({wl.K} routed + {wl.n_shared} shared SwiGLU experts"
+                        f"{', latent maps' if wl.d_latent else ''}, fp64) over {n} random tokens under "
+                        f"that routing, its per-token time extrapolated to the batch (rows independent)"))
 
 
 def _load_counter_csv(d):
